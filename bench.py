@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's TSP transformer-layer forward on one MI355X.
+
+A step is one ``tsp_layer_fwd`` call on a fixed synthetic batch: the rank's
+Q/K/V projection for all D weight shards, the zigzag K/V reorder, causal flash
+attention, the output projection with residual, and the gated-MLP weight ring
+(gate/up + SwiGLU, down + residual).  The other ranks' K/V slots of the
+all-gather buffer are filled once before timing (they are communication, not
+this rank's compute).  Inputs are resident in device memory when the timed
+region starts.
+
+Prints one JSON line.  ``value`` is algorithmic TFLOP/s (2MNK per GEMM,
+4*dh per causal query/key pair per head; masked pairs and elementwise work
+not counted).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and tokens/s per one-rank TSP layer fwd; % of bf16 MFMA peak"
+# MI355X published dense peaks: matrix cores 256 CU x 2.4 GHz x 4096 FLOP/clk
+# (bf16 = f16 rate), HBM3E 8 TB/s.
+PEAK_MFMA_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0
+KERNELS = ("qkv", "reorder", "attn", "oproj", "gateup", "down")
+
+
+def kernel_work(d):
+    """Algorithmic work per launch of each kernel: (amount, unit, bound)."""
+    from oracle import tsp_oracle as orc  # work accounting only
+    f = orc.algorithmic_flops(d)
+    c = d.seq // (2 * d.degree)
+    kmax = (2 * d.degree - d.rank) * c
+    reorder_bytes = 2 * 2 * d.n_kv_heads * d.batch * kmax * d.head_dim * 2  # K,V x (read + write)
+    return {
+        "qkv": (f["qkv"], "flop", "mfma"),
+        "reorder": (reorder_bytes, "byte", "hbm"),
+        "attn": (f["attn"], "flop", "mfma"),
+        "oproj": (f["o"], "flop", "mfma"),
+        "gateup": (f["mlp"] * 2 / 3, "flop", "mfma"),
+        "down": (f["mlp"] / 3, "flop", "mfma"),
+    }, f["total"]
+
+
+def cpu_baseline(wl, inp, target_s: float, max_rows: int):
+    """Times the oracle (float64 numpy, host cores) on a sample of the rank's rows:
+    own Q/K/V projection, attention over the full causal prefix, output
+    projection and MLP.  The K/V of all keys is computed before the clock
+    starts (the other ranks' K/V is communication on a real TSP axis)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import tsp_oracle as orc
+
+    d = wl.dims
+    cores = len(os.sched_getaffinity(0))
+    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
+    with threadpool_limits(limits=cores):
+        kmax = (2 * d.degree - d.rank) * c
+        kv = orc.project_kv(inp, d, 0, kmax)
+        w = {n: orc.bf16_bits_to_f64(inp[n]) for n in ("w_q", "w_o", "w_g", "w_u", "w_d")}
+        w_k, w_v = orc.bf16_bits_to_f64(inp["w_k"]), orc.bf16_bits_to_f64(inp["w_v"])
+
+        def run(rows):
+            t0 = time.perf_counter()
+            g = orc.local_to_global(d.seq, d.degree, d.rank)[rows]
+            x = orc.bf16_bits_to_f64(inp["x"][0, g])
+            _ = x @ w_k.T, x @ w_v.T          # own K/V projection of these rows
+            orc.rank_rows_forward(inp, d, 0, rows, kv=kv, weights=w)
+            return time.perf_counter() - t0
+
+        rng = np.random.default_rng(1234)
+
+        def sample(n):  # half from each zigzag chunk, seeded
+            n1 = max(1, n // 2)
+            a = np.sort(rng.choice(c, size=min(n1, c), replace=False))
+            b = np.sort(c + rng.choice(c, size=min(n - n1, c), replace=False))
+            return np.concatenate([a, b])
+
+        probe = sample(16)
+        tp = run(probe)
+        n = int(min(max_rows, T, max(16, 16 * target_s / max(tp, 1e-3))))
+        rows = sample(n)
+        dt = run(rows)
+    fl = orc.algorithmic_flops(d, rows_per_seq=rows)["total"]
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "tokens_per_s": len(rows) / dt, "seconds": dt,
+            "sample": f"{len(rows)} of the rank's {T} rows (seeded, half per zigzag chunk) of "
+                      f"sequence 0, float64 numpy/OpenBLAS on {cores} host threads; K/V of all "
+                      f"{kmax} keys precomputed before timing"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_s8k_d8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one rank of a TSP axis on one GPU; runs on more than one GPU "
+              "are not part of this build (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from folded_tensor_sequence_amd import binding as B
+    from folded_tensor_sequence_amd.harness import RankProblem
+
+    wl = synth.WORKLOADS[args.workload]
+    d = wl.dims
+    torch.cuda.set_device(0)
+    print(f"[bench] building {wl.name}: {wl.about}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(d, wl.sigma, wl.seed)
+    prob = RankProblem.build(d, inp)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        prob.layer()
+    torch.cuda.synchronize()
+
+    # per-kernel durations (one profiled call each, untimed) -> dominant kernel
+    kms = {}
+    for k in KERNELS:
+        B.tsp_profile_kernel(k, 4)
+        for _ in range(3):
+            prob.layer()
+        n, ms = B.tsp_profile_result()
+        kms[k] = ms / max(n, 1)
+    B.tsp_profile_kernel(None)
+    work, total_flop = kernel_work(d)
+    dominant = max(kms, key=kms.get)
+    print(f"[bench] per-kernel ms: {json.dumps({k: round(v, 4) for k, v in kms.items()})}",
+          file=sys.stderr, flush=True)
+
+    # timed region: K steps; the dominant kernel is bracketed by HIP events
+    B.tsp_profile_kernel(dominant, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        prob.layer()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    n_dom, dom_ms = B.tsp_profile_result()
+    B.tsp_profile_kernel(None)
+    ms_per_step = total_ms / args.steps
+    tflops = total_flop / (ms_per_step * 1e-3) / 1e12
+    M = d.batch * d.seq // d.degree
+
+    amount, unit, bound = work[dominant]
+    dom_avg_s = dom_ms / max(n_dom, 1) * 1e-3
+    if bound == "hbm":
+        achieved, peak, runit = amount / dom_avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, runit = amount / dom_avg_s / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s"
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in; bf16/f16 matrix cores, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) activations, N(0,sigma^2) bf16 weights)",
+        "config": {"workload": wl.name, "batch": d.batch, "seq_len": d.seq, "degree": d.degree,
+                   "rank": d.rank, "hidden": d.hidden, "q_heads": d.n_q_heads, "kv_heads": d.n_kv_heads,
+                   "head_dim": d.head_dim, "ffn": d.ffn, "rank_tokens": M},
+        "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
+        "gflop_per_step": round(total_flop / 1e9, 2),
+        "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": runit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(dom_avg_s * 1e3, 5), "launches": n_dom,
+                     "algorithmic_per_launch": amount},
+        "kernels_ms": {k: round(v, 5) for k, v in kms.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        del prob
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, max_rows=d.seq // d.degree)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

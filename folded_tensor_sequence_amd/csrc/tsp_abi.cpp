@@ -1,0 +1,378 @@
+// libtsp C ABI: argument validation, workspace carving and kernel dispatch.
+// Every check runs before the first launch; nothing here allocates device
+// memory or synchronises.
+#include "../../include/tsp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(TSP_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+// Validates dims and fills the derived shape.  Returns TSP_OK or an error code.
+int make_shape(const tsp_dims_t* d, tsp::Shape* s) {
+  if (d == nullptr) return fail(TSP_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1) return fail(TSP_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
+  if (d->degree < 1) return fail(TSP_ERR_INVALID_ARG, "degree must be >= 1 (got %d)", d->degree);
+  if (d->rank < 0 || d->rank >= d->degree)
+    return fail(TSP_ERR_INVALID_ARG, "rank %d not in [0, degree=%d)", d->rank, d->degree);
+  if (d->seq < 2 * d->degree || d->seq % (2 * d->degree) != 0)
+    return fail(TSP_ERR_INVALID_ARG, "seq %d must be a positive multiple of 2*degree=%d", d->seq,
+                2 * d->degree);
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(TSP_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (d->n_q_heads % d->degree != 0 || d->n_kv_heads % d->degree != 0)
+    return fail(TSP_ERR_INVALID_ARG, "n_q_heads %d and n_kv_heads %d must be multiples of degree %d",
+                d->n_q_heads, d->n_kv_heads, d->degree);
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(TSP_ERR_INVALID_ARG, "n_q_heads %d must be a multiple of n_kv_heads %d",
+                d->n_q_heads, d->n_kv_heads);
+  if (d->hidden < 64 || d->hidden % 64 != 0)
+    return fail(TSP_ERR_INVALID_ARG, "hidden %d must be a positive multiple of 64", d->hidden);
+  if (d->ffn < 64 || d->ffn % 64 != 0 || (d->ffn / d->degree) * d->degree != d->ffn ||
+      (d->ffn / d->degree) % 8 != 0)
+    return fail(TSP_ERR_INVALID_ARG,
+                "ffn %d must be a positive multiple of 64 with ffn/degree a multiple of 8", d->ffn);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(TSP_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if ((int64_t)d->seq > kMaxDim || (int64_t)d->batch * d->seq / d->degree > kMaxDim ||
+      d->hidden > 65536 || d->ffn > 1048576 || (int64_t)d->n_q_heads * d->head_dim > 65536)
+    return fail(TSP_ERR_UNSUPPORTED, "shape exceeds the supported index range");
+  tsp::Shape& x = *s;
+  x.B = d->batch;
+  x.S = d->seq;
+  x.D = d->degree;
+  x.r = d->rank;
+  x.h = d->hidden;
+  x.Hq = d->n_q_heads;
+  x.Hkv = d->n_kv_heads;
+  x.dh = d->head_dim;
+  x.F = d->ffn;
+  x.T = x.S / x.D;
+  x.c = x.S / (2 * x.D);
+  x.M = x.B * x.T;
+  x.Hq_s = x.Hq / x.D;
+  x.Hkv_s = x.Hkv / x.D;
+  x.F_s = x.F / x.D;
+  x.kmax = (2 * x.D - x.r) * x.c;
+  x.kmax_pad = (x.kmax + 63) / 64 * 64;
+  x.nqkv_s = (x.Hq_s + 2 * x.Hkv_s) * x.dh;
+  return TSP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int need_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(TSP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TSP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return TSP_OK;
+}
+
+int opt_ptr(const void* p, const char* name) {
+  if (p != nullptr && !aligned16(p)) return fail(TSP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return TSP_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t bytes_q(const tsp::Shape& s) { return (size_t)s.M * s.Hq * s.dh * 2; }
+size_t bytes_kvnat(const tsp::Shape& s) { return (size_t)2 * s.Hkv * s.B * s.kmax_pad * s.dh * 2; }
+size_t bytes_knat(const tsp::Shape& s) { return bytes_kvnat(s) / 2; }
+size_t bytes_o(const tsp::Shape& s) { return (size_t)s.M * s.Hq * s.dh * 2; }
+size_t bytes_h32(const tsp::Shape& s) { return (size_t)s.M * s.h * 4; }
+size_t bytes_h16(const tsp::Shape& s) { return (size_t)s.M * s.h * 2; }
+size_t bytes_act(const tsp::Shape& s) { return (size_t)s.M * s.F * 2; }
+size_t bytes_gathered(const tsp::Shape& s) {
+  return (size_t)s.D * s.D * 2 * s.B * s.T * s.Hkv_s * s.dh * 2;
+}
+
+struct AttnWs {
+  uint16_t *q, *knat, *vnat, *o;
+};
+struct MlpWs {
+  uint16_t *h16, *act;
+};
+
+size_t ws_attn(const tsp::Shape& s) { return up(bytes_q(s)) + up(bytes_kvnat(s)) + up(bytes_o(s)); }
+size_t ws_mlp(const tsp::Shape& s) { return up(bytes_h16(s)) + up(bytes_act(s)); }
+size_t ws_layer(const tsp::Shape& s) { return ws_attn(s) + up(bytes_h32(s)) + ws_mlp(s); }
+
+AttnWs carve_attn(const tsp::Shape& s, char* p) {
+  AttnWs w;
+  w.q = reinterpret_cast<uint16_t*>(p);
+  p += up(bytes_q(s));
+  w.knat = reinterpret_cast<uint16_t*>(p);
+  w.vnat = reinterpret_cast<uint16_t*>(p + bytes_knat(s));
+  p += up(bytes_kvnat(s));
+  w.o = reinterpret_cast<uint16_t*>(p);
+  return w;
+}
+
+MlpWs carve_mlp(const tsp::Shape& s, char* p) {
+  MlpWs w;
+  w.h16 = reinterpret_cast<uint16_t*>(p);
+  p += up(bytes_h16(s));
+  w.act = reinterpret_cast<uint16_t*>(p);
+  return w;
+}
+
+// ---- live per-kernel timing (see tsp_profile_kernel) -----------------------
+struct Profile {
+  int kernel = TSP_K_NONE;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+};
+thread_local Profile g_prof;
+
+void prof_release() {
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.kernel = TSP_K_NONE;
+  g_prof.used = 0;
+}
+
+// Records the opening event when `id` is being profiled; returns the slot or -1.
+int prof_open(int id, hipStream_t st) {
+  if (g_prof.kernel != id || 2 * (g_prof.used + 1) > (int)g_prof.ev.size()) return -1;
+  const int slot = g_prof.used++;
+  (void)hipEventRecord(g_prof.ev[2 * slot], st);
+  return slot;
+}
+void prof_close(int slot, hipStream_t st) {
+  if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], st);
+}
+
+int check_device(const char* where) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, where);
+  return TSP_OK;
+}
+
+#define TSP_TRY(expr)            \
+  do {                           \
+    int _rc = (expr);            \
+    if (_rc != TSP_OK) return _rc; \
+  } while (0)
+
+#define TSP_LAUNCH(expr, where)                   \
+  do {                                            \
+    hipError_t _e = (expr);                       \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// A launch of kernel `id`, bracketed by profiling events when armed.
+#define TSP_KLAUNCH(id, st, expr, where)          \
+  do {                                            \
+    const int _slot = prof_open(id, st);          \
+    hipError_t _e = (expr);                       \
+    prof_close(_slot, st);                        \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+int run_attention(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* w_qkv,
+                  const uint16_t* w_o, uint16_t* kv_gathered, float* out, uint16_t* out16,
+                  const AttnWs& w, hipStream_t st) {
+  TSP_KLAUNCH(TSP_K_QKV, st, tsp::launch_qkv_gemm(s, s.r, x_local, w_qkv, w.q, kv_gathered, st),
+              "qkv projection");
+  TSP_KLAUNCH(TSP_K_REORDER, st, tsp::launch_kv_reorder(s, kv_gathered, w.knat, w.vnat, st), "kv reorder");
+  TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, w.knat, w.vnat, w.o, st), "flash attention");
+  TSP_KLAUNCH(TSP_K_OPROJ, st, tsp::launch_oproj_gemm(s, w.o, w_o, x_local, out, out16, st),
+              "output projection");
+  return TSP_OK;
+}
+
+int run_mlp(const tsp::Shape& s, const uint16_t* h16, const float* resid, const uint16_t* w_gate,
+            const uint16_t* w_up, const uint16_t* w_down, float* y, const MlpWs& w, hipStream_t st) {
+  TSP_KLAUNCH(TSP_K_GATEUP, st, tsp::launch_gateup_gemm(s, h16, w_gate, w_up, w.act, st), "mlp gate/up");
+  TSP_KLAUNCH(TSP_K_DOWN, st, tsp::launch_down_gemm(s, w.act, w_down, resid, y, st), "mlp down ring");
+  return TSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tsp_last_error(void) { return g_last_error.c_str(); }
+
+int tsp_profile_kernel(int32_t kernel_id, int32_t max_launches) {
+  if (kernel_id < TSP_K_NONE || kernel_id >= TSP_K_COUNT)
+    return fail(TSP_ERR_INVALID_ARG, "unknown kernel id %d", kernel_id);
+  prof_release();
+  if (kernel_id == TSP_K_NONE) return TSP_OK;
+  if (max_launches < 1 || max_launches > 100000)
+    return fail(TSP_ERR_INVALID_ARG, "max_launches %d not in [1, 100000]", max_launches);
+  TSP_TRY(check_device("tsp_profile_kernel"));
+  g_prof.ev.resize(2 * (size_t)max_launches, nullptr);
+  for (hipEvent_t& e : g_prof.ev) {
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      prof_release();
+      return hip_fail(err, "tsp_profile_kernel");
+    }
+  }
+  g_prof.kernel = kernel_id;
+  return TSP_OK;
+}
+
+int tsp_profile_result(int32_t* launches, float* total_ms) {
+  if (launches == nullptr || total_ms == nullptr)
+    return fail(TSP_ERR_INVALID_ARG, "launches and total_ms must not be NULL");
+  float sum = 0.0f;
+  for (int i = 0; i < g_prof.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "tsp_profile_result");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "tsp_profile_result");
+    sum += ms;
+  }
+  *launches = g_prof.used;
+  *total_ms = sum;
+  g_prof.used = 0;
+  return TSP_OK;
+}
+
+size_t tsp_workspace_bytes(const tsp_dims_t* dims, int32_t fn) {
+  tsp::Shape s;
+  if (make_shape(dims, &s) != TSP_OK) return 0;
+  switch (fn) {
+    case TSP_FN_ATTN: return ws_attn(s);
+    case TSP_FN_MLP: return ws_mlp(s);
+    case TSP_FN_LAYER: return ws_layer(s);
+    case TSP_FN_KV_NATURAL: return bytes_kvnat(s);
+    case TSP_FN_KV_GATHERED: return bytes_gathered(s);
+    default: fail(TSP_ERR_INVALID_ARG, "unknown workspace selector %d", fn); return 0;
+  }
+}
+
+int tsp_zigzag_index(const tsp_dims_t* dims, int32_t* local_to_global, int32_t* global_to_slot,
+                     hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  if (local_to_global == nullptr) return fail(TSP_ERR_INVALID_ARG, "local_to_global is NULL");
+  TSP_TRY(check_device("tsp_zigzag_index"));
+  TSP_LAUNCH(tsp::launch_zigzag_index(s, local_to_global, global_to_slot, stream), "zigzag index");
+  return TSP_OK;
+}
+
+int tsp_qkv_proj(const tsp_dims_t* dims, int32_t src_rank, const uint16_t* x_shard,
+                 const uint16_t* w_qkv, uint16_t* q_out, uint16_t* kv_gathered, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  if (src_rank < 0 || src_rank >= s.D)
+    return fail(TSP_ERR_INVALID_ARG, "src_rank %d not in [0, %d)", src_rank, s.D);
+  TSP_TRY(need_ptr(x_shard, "x_shard"));
+  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
+  TSP_TRY(opt_ptr(q_out, "q_out"));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(check_device("tsp_qkv_proj"));
+  TSP_KLAUNCH(TSP_K_QKV, stream,
+              tsp::launch_qkv_gemm(s, src_rank, x_shard, w_qkv, q_out, kv_gathered, stream),
+              "qkv projection");
+  return TSP_OK;
+}
+
+int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered, uint16_t* kv_natural,
+                   hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(need_ptr(kv_natural, "kv_natural"));
+  TSP_TRY(check_device("tsp_kv_reorder"));
+  uint16_t* vnat = kv_natural + bytes_knat(s) / 2;
+  TSP_KLAUNCH(TSP_K_REORDER, stream, tsp::launch_kv_reorder(s, kv_gathered, kv_natural, vnat, stream),
+              "kv reorder");
+  return TSP_OK;
+}
+
+int tsp_attn_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                 const uint16_t* w_o, uint16_t* kv_gathered, float* out, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(x_local, "x_local"));
+  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
+  TSP_TRY(need_ptr(w_o, "w_o"));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(need_ptr(out, "out"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_attn(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_attn(s));
+  TSP_TRY(check_device("tsp_attn_fwd"));
+  const AttnWs w = carve_attn(s, static_cast<char*>(ws));
+  return run_attention(s, x_local, w_qkv, w_o, kv_gathered, out, nullptr, w, stream);
+}
+
+int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const float* x, const uint16_t* w_gate,
+                     const uint16_t* w_up, const uint16_t* w_down, float* y, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(x, "x"));
+  TSP_TRY(need_ptr(w_gate, "w_gate"));
+  TSP_TRY(need_ptr(w_up, "w_up"));
+  TSP_TRY(need_ptr(w_down, "w_down"));
+  TSP_TRY(need_ptr(y, "y"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_mlp(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_mlp(s));
+  TSP_TRY(check_device("tsp_mlp_ring_fwd"));
+  const MlpWs w = carve_mlp(s, static_cast<char*>(ws));
+  TSP_LAUNCH(tsp::launch_f32_to_f16(x, w.h16, (int64_t)s.M * s.h, stream), "mlp input rounding");
+  return run_mlp(s, w.h16, x, w_gate, w_up, w_down, y, w, stream);
+}
+
+int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                  const uint16_t* w_o, const uint16_t* w_gate, const uint16_t* w_up,
+                  const uint16_t* w_down, uint16_t* kv_gathered, float* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(x_local, "x_local"));
+  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
+  TSP_TRY(need_ptr(w_o, "w_o"));
+  TSP_TRY(need_ptr(w_gate, "w_gate"));
+  TSP_TRY(need_ptr(w_up, "w_up"));
+  TSP_TRY(need_ptr(w_down, "w_down"));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(need_ptr(y, "y"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_layer(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_layer(s));
+  TSP_TRY(check_device("tsp_layer_fwd"));
+  char* p = static_cast<char*>(ws);
+  const AttnWs aw = carve_attn(s, p);
+  p += ws_attn(s);
+  float* h32 = reinterpret_cast<float*>(p);
+  p += up(bytes_h32(s));
+  const MlpWs mw = carve_mlp(s, p);
+  TSP_TRY(run_attention(s, x_local, w_qkv, w_o, kv_gathered, h32, mw.h16, aw, stream));
+  return run_mlp(s, mw.h16, h32, w_gate, w_up, w_down, y, mw, stream);
+}
+
+}  // extern "C"

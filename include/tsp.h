@@ -1,0 +1,209 @@
+/* tsp.h -- C ABI of libtsp: one rank's share of a Tensor-and-Sequence-Parallel
+ * (TSP) transformer-layer forward on one AMD Instinct MI355X (gfx950).
+ *
+ * What TSP computes (Zyphra TSP article on ai-trends.today, "Zyphra Introduces
+ * Tensor and Sequence Parallelism (TSP)...", section "How to Fold a Book"):
+ * one device axis of size D carries both tensor and sequence parallelism, so
+ * rank r keeps 1/D of every weight matrix and 1/D of the tokens.  Attention
+ * iterates over packed weight shards {W_Q, W_K, W_V, W_O}: every rank
+ * projects its own tokens with shard j, K and V are all-gathered, reordered
+ * with the zigzag partition and fed to causal attention; the output
+ * projection of shard j is a row split whose partials are summed locally.
+ * The gated MLP runs as a ring over gate/up/down weight shards; each rank
+ * accumulates its partial outputs locally and the sequence never moves.
+ *
+ * This library computes the per-rank work with all D weight shards already
+ * resident in device memory (no collectives).  The layer is read as
+ *     h = x + Attn(x),   y = h + MLP(h),
+ *     MLP(h) = (silu(h Wg^T) * (h Wu^T)) Wd^T,  silu(z) = z / (1 + e^-z),
+ * causal attention with scale 1/sqrt(head_dim) and keys k <= query q, no
+ * normalisation, rotary embedding, bias or dropout.
+ *
+ * Zigzag partition: the sequence of S positions is cut into 2D chunks of
+ * c = S/(2D); rank r holds chunk r then chunk 2D-1-r (local row order), i.e.
+ * local row t has global position r*c + t for t < c and (2D-1-r)*c + (t-c)
+ * otherwise.  GQA: q-head i reads kv-head floor(i*Hkv/Hq).  Shard j is head
+ * group j: q-heads [j*Hq/D, (j+1)*Hq/D), kv-heads [j*Hkv/D, (j+1)*Hkv/D), and
+ * MLP rows/columns [j*F/D, (j+1)*F/D).  The MLP ring at step s uses shard
+ * (r - s) mod D.
+ *
+ * General rules for every entry point
+ *   - Tensor pointers are DEVICE memory owned by the caller, 16-byte aligned.
+ *     16-bit tensors are passed as uint16_t bit patterns: "bf16" = bfloat16,
+ *     "f16" = IEEE half.  All index arithmetic is 64-bit.
+ *   - Every call is asynchronous on `stream` (NULL = the default stream); it
+ *     never synchronises and never allocates device memory.
+ *   - Arguments are validated before anything is launched.  The return value
+ *     is TSP_OK (0) or a negative tsp_status; tsp_last_error() then returns a
+ *     thread-local message.  A failed launch returns TSP_ERR_HIP.
+ *   - Inputs are read-only; outputs are overwritten in full.
+ *   - Overlapping calls on different streams must not share outputs or
+ *     workspace.
+ */
+#ifndef TSP_H_
+#define TSP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layer shape as seen from one rank.
+ *   batch      B >= 1 independent sequences, each zigzag-split the same way
+ *   seq        S, total positions per sequence;   S % (2*degree) == 0
+ *   degree     D >= 1, size of the TSP axis
+ *   rank       r in [0, D)
+ *   hidden     h, h % 64 == 0
+ *   n_q_heads  Hq, n_kv_heads Hkv:  Hq % D == 0, Hkv % D == 0, Hq % Hkv == 0
+ *   head_dim   dh in {64, 128}
+ *   ffn        F, F % 64 == 0 and (F/D) % 8 == 0
+ * Derived: T = S/D local rows per sequence, c = S/(2D), M = B*T, F_s = F/D,
+ *   kmax = (2D - r)*c (one past the largest position rank r attends to),
+ *   kmax_pad = kmax rounded up to a multiple of 64.
+ */
+typedef struct {
+  int32_t batch, seq, degree, rank, hidden, n_q_heads, n_kv_heads, head_dim, ffn;
+} tsp_dims_t;
+
+typedef enum {
+  TSP_OK = 0,
+  TSP_ERR_INVALID_ARG = -1, /* shape rule broken, NULL or misaligned pointer */
+  TSP_ERR_UNSUPPORTED = -2, /* valid TSP shape this build does not handle */
+  TSP_ERR_WORKSPACE = -3,   /* ws too small (see tsp_workspace_bytes) */
+  TSP_ERR_HIP = -4          /* HIP runtime error (no device, launch failure) */
+} tsp_status;
+
+/* Selectors for tsp_workspace_bytes. */
+typedef enum {
+  TSP_FN_ATTN = 1,       /* tsp_attn_fwd workspace */
+  TSP_FN_MLP = 2,        /* tsp_mlp_ring_fwd workspace */
+  TSP_FN_LAYER = 3,      /* tsp_layer_fwd workspace */
+  TSP_FN_KV_NATURAL = 4, /* size of the kv_natural output of tsp_kv_reorder */
+  TSP_FN_KV_GATHERED = 5 /* size of the kv_gathered buffer */
+} tsp_fn;
+
+/* Zigzag maps of the partition described above (TSP article, "How to Fold a
+ * Book": K/V are reordered with a zigzag partition that balances causal work
+ * across ranks; r007.github.io "Распределенное обучение", section
+ * "Параллелизм по контексту: Ring Attention против Ulysses", item 1).
+ *   local_to_global  int32 [T]: global position of rank dims->rank's row t.
+ *   global_to_slot   int32 [S] or NULL: for each global position g, the slot
+ *                    rank*T + t that holds it in a rank-major all-gather.
+ * Both maps are exact integers. */
+int tsp_zigzag_index(const tsp_dims_t* dims, int32_t* local_to_global,
+                     int32_t* global_to_slot, hipStream_t stream);
+
+/* Packed per-shard Q/K/V projection of one rank's tokens (TSP article, "How
+ * to Fold a Book": each rank applies the broadcast W_Q/W_K/W_V of shard j to
+ * its own tokens).  Computes X_src * W_qkv,j^T for every shard j with bf16
+ * matrix cores and float32 accumulation, rounding results to f16.
+ *   src_rank     rank whose tokens x_shard holds (its zigzag rows)
+ *   x_shard      bf16 [B][T][h], local zigzag row order of src_rank
+ *   w_qkv        bf16 [D][(Hq/D + 2*Hkv/D)*dh][h]: shard j's rows are its
+ *                Hq/D q-heads, then its Hkv/D k-heads, then its v-heads,
+ *                dh rows each, in nn.Linear [out][in] order
+ *   q_out        f16 [B][Hq][T][dh] or NULL (then Q is not stored)
+ *   kv_gathered  f16 [D_shard][D_src][2][B][T][Hkv/D*dh]: the all-gather
+ *                destination; this call writes only the src_rank slots
+ *                (index 0 of the [2] axis is K, 1 is V).
+ * The library uses this for its own rank inside tsp_attn_fwd/tsp_layer_fwd;
+ * a caller simulating the other ranks' all-gather contributions calls it
+ * once per other rank. */
+int tsp_qkv_proj(const tsp_dims_t* dims, int32_t src_rank, const uint16_t* x_shard,
+                 const uint16_t* w_qkv, uint16_t* q_out, uint16_t* kv_gathered,
+                 hipStream_t stream);
+
+/* Zigzag reorder of the gathered K/V into natural sequence order (TSP
+ * article, "How to Fold a Book").  Bit-exact 16-bit copy of every key
+ * position g < kmax; the positions [kmax, kmax_pad) are zero-filled.
+ *   kv_gathered  f16, layout of tsp_qkv_proj, all D_src slots filled
+ *   kv_natural   f16, TSP_FN_KV_NATURAL bytes:
+ *                K part  [Hkv][B][kmax_pad][dh]   (key-major rows)
+ *                V part  [Hkv][B][dh][kmax_pad]   (transposed: dh-major)
+ *                the V part starts right after the K part; the kv-head
+ *                index is the global one, j*Hkv/D + (head within shard j). */
+int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered,
+                   uint16_t* kv_natural, hipStream_t stream);
+
+/* Attention half of the layer on rank dims->rank:
+ *     out = x + sum_j O_j W_O,j^T,
+ * O_j = causal attention of the rank's zigzag queries (q-heads of shard j)
+ * over the natural-order K/V of shard j (TSP article, "How to Fold a Book";
+ * the head split with row-split output projection is exact:
+ * bowenzhou.top "张量并行", section "机制：行切与列切").
+ *   x_local      bf16 [B][T][h]
+ *   w_qkv        bf16, layout of tsp_qkv_proj;  w_o bf16 [D][h][Hq/D*dh]
+ *                (shard j = W_o columns of its q-heads)
+ *   kv_gathered  in: the other ranks' slots; out: this rank's slots
+ *   out          float32 [B][T][h]
+ *   ws           device workspace of >= tsp_workspace_bytes(dims, TSP_FN_ATTN)
+ * Precision: Q/K/V, softmax probabilities and O are f16 with float32
+ * accumulation and float32 online softmax; W_o is read as bf16 and rounded
+ * to f16 for the matrix cores. */
+int tsp_attn_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                 const uint16_t* w_o, uint16_t* kv_gathered, float* out, void* ws,
+                 size_t ws_bytes, hipStream_t stream);
+
+/* Gated-MLP weight ring on rank dims->rank (TSP article, "How to Fold a
+ * Book": gate/up/down shards travel around a ring, partial outputs are
+ * accumulated locally, no all-reduce; the column/row split sums exactly,
+ * bowenzhou.top "张量并行", section "机制：行切与列切"):
+ *     y = x + sum_{s=0}^{D-1} (silu(x Wg_j^T) * (x Wu_j^T)) Wd_j^T,  j = (r - s) mod D
+ *   x        float32 [B][T][h] (rounded to f16 for the matrix cores)
+ *   w_gate, w_up  bf16 [D][F/D][h] (= [F][h]);  w_down bf16 [D][h][F/D]
+ *   y        float32 [B][T][h]; may alias x
+ *   ws       >= tsp_workspace_bytes(dims, TSP_FN_MLP) bytes */
+int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const float* x, const uint16_t* w_gate,
+                     const uint16_t* w_up, const uint16_t* w_down, float* y, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Whole layer on rank dims->rank: h = x + Attn(x), y = h + MLP(h), with the
+ * argument layouts of tsp_attn_fwd and tsp_mlp_ring_fwd.  h stays float32;
+ * its f16 copy feeds the MLP matrix cores.
+ *   y   float32 [B][T][h]
+ *   ws  >= tsp_workspace_bytes(dims, TSP_FN_LAYER) bytes */
+int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                  const uint16_t* w_o, const uint16_t* w_gate, const uint16_t* w_up,
+                  const uint16_t* w_down, uint16_t* kv_gathered, float* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of workspace (or of a buffer) named by fn for these dims; 0 if the
+ * dims are invalid (tsp_last_error says why). */
+size_t tsp_workspace_bytes(const tsp_dims_t* dims, int32_t fn);
+
+/* Kernels of the layer, for tsp_profile_kernel. */
+typedef enum {
+  TSP_K_NONE = 0,
+  TSP_K_QKV = 1,     /* packed Q/K/V projection GEMM */
+  TSP_K_REORDER = 2, /* zigzag K/V reorder */
+  TSP_K_ATTN = 3,    /* causal flash attention */
+  TSP_K_OPROJ = 4,   /* output projection GEMM (+ residual) */
+  TSP_K_GATEUP = 5,  /* MLP gate/up GEMM with the SwiGLU epilogue */
+  TSP_K_DOWN = 6,    /* MLP down-projection ring GEMM (+ residual) */
+  TSP_K_COUNT = 7
+} tsp_kernel_id;
+
+/* Live timing of one kernel: after tsp_profile_kernel(id, n) the next n
+ * launches of kernel `id` made by this thread (through any entry point) are
+ * bracketed by a pair of HIP events recorded on the launch stream.  The
+ * events are created here, once, not inside the timed calls.  id = TSP_K_NONE
+ * stops and releases them.  Not for use while a HIP graph is being captured. */
+int tsp_profile_kernel(int32_t kernel_id, int32_t max_launches);
+
+/* Waits for the recorded events of the current profile and returns the number
+ * of bracketed launches and their summed duration in milliseconds; the
+ * profile stays armed for the same kernel with its counters reset. */
+int tsp_profile_result(int32_t* launches, float* total_ms);
+
+/* Thread-local text describing the last non-zero return on this thread. */
+const char* tsp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSP_H_ */

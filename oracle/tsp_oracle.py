@@ -64,6 +64,8 @@ __all__ = [
     "layer_rank_rows",
     "project_kv",
     "rank_rows_forward",
+    "qkv_rows",
+    "mlp_block",
     "tsp_schedule",
     "algorithmic_flops",
 ]
@@ -216,6 +218,21 @@ def rank_rows_forward(inputs: dict, dims, b: int, rows: np.ndarray, kv=None,
     hres = x + attn
     mlp = swiglu_mlp(hres, weights["w_g"], weights["w_u"], weights["w_d"])
     return {"o": o, "attn": attn, "h": hres, "mlp": mlp, "y": hres + mlp, "x": x}
+
+
+def qkv_rows(inputs: dict, dims, b: int, rows, rank=None) -> dict:
+    """Q, K, V projections X W^T of local rows ``rows`` of sequence b on rank
+    ``rank`` (default dims.rank), float64, unsharded head order."""
+    r = dims.rank if rank is None else rank
+    g = local_to_global(dims.seq, dims.degree, r)[np.asarray(rows, dtype=np.int64)]
+    x = bf16_bits_to_f64(inputs["x"][b, g])
+    return {n: x @ bf16_bits_to_f64(inputs["w_" + n]).T for n in ("q", "k", "v")}
+
+
+def mlp_block(inputs: dict, x: np.ndarray) -> np.ndarray:
+    """x + SwiGLU-MLP(x) for float64 rows x [n][h] (the MLP half of the layer)."""
+    w_g, w_u, w_d = (bf16_bits_to_f64(inputs[n]) for n in ("w_g", "w_u", "w_d"))
+    return x + swiglu_mlp(x, w_g, w_u, w_d)
 
 
 def layer_rank_rows(inputs: dict, dims, rows=None) -> dict:
