@@ -165,7 +165,7 @@ def test_mlp_ring_fwd(name):
     T = d.seq // d.degree
     # MLP input: this rank's bf16 rows of X, handed over as float32
     l2g = orc.local_to_global(d.seq, d.degree, d.rank)
-    x = orc.bf16_bits_to_f64(inp["x"][:, l2g]).astype(np.float32)
+    x = np.ascontiguousarray(orc.bf16_bits_to_f64(inp["x"][:, l2g]), dtype=np.float32)
     xt = torch.from_numpy(x).cuda()
     y = torch.empty_like(xt)
     ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP), dtype=torch.uint8, device="cuda")
