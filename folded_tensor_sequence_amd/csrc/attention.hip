@@ -9,10 +9,15 @@
 // контексту: Ring Attention против Ulysses": the online-softmax accumulator),
 // so the S x S score matrix is never stored.
 //
-// Work item = (sequence b, q-head, block of 128 local rows inside one zigzag
-// chunk); 4 waves x 32 query rows.  Items of the later chunk (longer key
-// prefix) come first in the grid so the dispatcher hands out the long ones
-// first.  Per 64-key tile:
+// Work: a block is 128 consecutive local rows of one zigzag chunk for one
+// (sequence, q-head); 4 waves x 32 query rows.  The rank's later chunk sees a
+// key prefix up to 2D-1 times longer than its earlier one, so a block whose
+// key range exceeds kt_max tiles of 64 keys is cut into pieces along the keys
+// (each piece keeps its own max / sum / unnormalised output, merged afterwards
+// in piece order, so results are deterministic).  Units are ordered heaviest
+// block first.
+//
+// Per 64-key tile:
 //   S^T = K Q^T   (32x32x16 MFMA, K from LDS as the first operand, the wave's
 //                  Q rows kept in registers as the second) -> each lane holds
 //                  one query (column) and 32 of the tile's 64 keys; the lane
@@ -23,6 +28,9 @@
 //   V is stored transposed (head-dim major) so those 8 keys are one 16-byte
 //   LDS read.
 //   O^T += V^T P  (32x32x16 MFMA, probabilities rounded to f16).
+// K and V tiles are copied global -> LDS with 16-byte direct loads into an
+// NST-deep ring; the barrier between tiles carries no memory fence, so the
+// loads of later tiles stay in flight across it.
 #include <math.h>
 
 #include "common.h"
@@ -35,10 +43,19 @@ struct AttnArgs {
   const uint16_t* knat;  // f16 [Hkv][B][kmax_pad][dh]
   const uint16_t* vnat;  // f16 [Hkv][B][dh][kmax_pad]
   uint16_t* o;           // f16 [B][T][Hq*dh]
+  float* part_o;         // [pieces][B*Hq][128][dh] unnormalised outputs of split blocks
+  float* part_ml;        // [pieces][B*Hq][2][128] (scaled max, sum)
   Shape s;
   float scale_log2;      // log2(e) / sqrt(dh)
   int32_t nrb;           // 128-row blocks per chunk
+  int32_t kt_max;        // key tiles per piece at most
 };
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void attn_load_lds16(const uint16_t* g, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+}
 
 // Row permutation inside each 32-key group: swaps 4-row blocks 1<->2, 5<->6.
 __device__ __forceinline__ int key_perm(int i) {
@@ -46,44 +63,90 @@ __device__ __forceinline__ int key_perm(int i) {
   return ((b4 ^ (b4 >> 1)) & 1) ? (i ^ 12) : i;
 }
 
+// 16-byte LDS accesses are served 16 lanes at a time over 64 four-byte banks.
+// K rows are DH*2 bytes: with 256-byte rows every row starts at bank 0, so
+// slot c of row r sits at c ^ (r & 15); with 128-byte rows (and the 128-byte
+// rows of the transposed V tile) rows alternate bank halves, so the XOR key is
+// (r >> 1) & 7.  Either way the 16 rows of one operand read hit 16 distinct
+// bank groups.
 template <int DH>
-__global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
+__device__ __forceinline__ int kswz(int row) {
+  return DH == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+
+// Block geometry shared by the attention and merge kernels.  Block index
+// bi in [0, 2 nrb): the later chunk's blocks first, last rows first.
+struct BlockGeo {
+  int row_begin, row_end;  // local rows of the chunk
+  int gstart;              // global position of the chunk's first row
+  int t0;                  // first local row of the block
+  int nkt;                 // key tiles the block needs
+  int ns;                  // pieces
+};
+
+__device__ __forceinline__ BlockGeo block_geo(const Shape& s, int nrb, int kt_max, int bi) {
+  BlockGeo g;
+  const int late = bi < nrb ? 1 : 0;
+  const int rb = nrb - 1 - (late ? bi : bi - nrb);
+  g.row_begin = late * s.c;
+  g.row_end = g.row_begin + s.c;
+  g.gstart = (late ? (2 * s.D - 1 - s.r) : s.r) * s.c;
+  g.t0 = g.row_begin + rb * 128;
+  const int last = g.t0 + 127 < g.row_end ? g.t0 + 127 : g.row_end - 1;
+  g.nkt = (g.gstart + (last - g.row_begin) + 64) / 64;
+  g.ns = (g.nkt + kt_max - 1) / kt_max;
+  return g;
+}
+
+template <int DH, int NST>
+__global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnArgs a) {
   constexpr int BN = 64;
   constexpr int KROW = DH * 2;
   constexpr int K_BYTES = BN * KROW;
   constexpr int V_BYTES = DH * BN * 2;
   constexpr int STAGE = K_BYTES + V_BYTES;
-  constexpr int KCH = DH / 8;
-  constexpr int K_LD = BN * KCH / 256;
-  constexpr int V_LD = DH * 8 / 256;
+  constexpr int KRPI = 1024 / KROW;          // K rows per direct-load instruction
+  constexpr int K_INS = BN / KRPI;           // instructions per K tile
+  constexpr int V_INS = DH / 8;              // 8 transposed-V rows of 128 bytes each
+  constexpr int QT = K_INS + V_INS;
+  static_assert(QT % 4 == 0, "loads split evenly over 4 waves");
+  constexpr int QW = QT / 4;                 // per wave
   constexpr int NDB = DH / 32;
   constexpr int NKS = DH / 16;
-  __shared__ __align__(16) unsigned char smem[2 * STAGE];
+  __shared__ __align__(16) unsigned char smem[NST * STAGE];
 
   const Shape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lgrp = lane >> 5;
 
-  // ---- work item -------------------------------------------------------
-  const int per = s.B * s.Hq;
-  const int pos = blockIdx.x / per, bh = blockIdx.x - pos * per;
+  // ---- work unit -> (block, piece, sequence, q-head) --------------------
+  const int per_bh = s.B * s.Hq;
+  int u = blockIdx.x, bi = 0, piece_base = 0;
+  BlockGeo g = block_geo(s, a.nrb, a.kt_max, 0);
+  for (;;) {
+    const int n = g.ns * per_bh;
+    if (u < n || bi + 1 >= 2 * a.nrb) break;
+    u -= n;
+    if (g.ns > 1) piece_base += g.ns;
+    ++bi;
+    g = block_geo(s, a.nrb, a.kt_max, bi);
+  }
+  const int piece = u / per_bh, bh = u - piece * per_bh;
   const int b = bh / s.Hq, qh = bh - b * s.Hq;
-  const int late = pos < a.nrb ? 1 : 0;
-  const int rb = a.nrb - 1 - (late ? pos : pos - a.nrb);
-  const int row_begin = late * s.c, row_end = row_begin + s.c;
-  const int gstart = (late ? (2 * s.D - 1 - s.r) : s.r) * s.c;
-  const int t0 = row_begin + rb * 128;
-  const int wt0 = t0 + wave * 32;
-  const bool wave_active = wt0 < row_end;
+  const int tper = (g.nkt + g.ns - 1) / g.ns;
+  const int kt_begin = piece * tper;
+  const int kt_end = kt_begin + tper < g.nkt ? kt_begin + tper : g.nkt;
+
+  const int wt0 = g.t0 + wave * 32;
+  const bool wave_active = wt0 < g.row_end;
   int t_lane = wt0 + lrow;
-  const bool lane_valid = t_lane < row_end;
-  t_lane = lane_valid ? t_lane : row_end - 1;
-  const int qpos = gstart + (t_lane - row_begin);
-  const int wg_last = (t0 + 127 < row_end ? t0 + 127 : row_end - 1);
-  const int nkt = (gstart + (wg_last - row_begin) + BN) / BN;
-  const int w_last = (wt0 + 31 < row_end ? wt0 + 31 : row_end - 1);
-  const int wave_maxpos = gstart + (w_last - row_begin);
-  const int wave_minpos = gstart + (wt0 - row_begin);
+  const bool lane_valid = t_lane < g.row_end;
+  t_lane = lane_valid ? t_lane : g.row_end - 1;
+  const int qpos = g.gstart + (t_lane - g.row_begin);
+  const int w_last = (wt0 + 31 < g.row_end ? wt0 + 31 : g.row_end - 1);
+  const int wave_maxpos = g.gstart + (w_last - g.row_begin);
+  const int wave_minpos = g.gstart + (wt0 - g.row_begin);
 
   const int G = qh / (s.Hq / s.Hkv);
   const uint16_t* kbase = a.knat + ((int64_t)G * s.B + b) * s.kmax_pad * DH;
@@ -97,35 +160,44 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + lgrp * 8);
   }
 
-  // ---- K/V tile staging -------------------------------------------------
-  u32x4 rk[K_LD], rv[V_LD];
-  auto gload = [&](int kt) {
-    const int key0 = kt * BN;
+  // ---- direct-load assignment: wave instruction q = wave + 4 i ------------
+  const uint16_t* lsrc[QW];
 #pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int ci = tid + 256 * i, kr = ci / KCH, kc = ci - kr * KCH;
-      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(key0 + kr) * DH + kc * 8);
+  for (int i = 0; i < QW; ++i) {
+    const int q = wave + 4 * i;
+    if (q < K_INS) {
+      const int row = KRPI * q + lane / (KROW / 16);
+      const int slot = lane % (KROW / 16);
+      const int key = (row & ~31) | key_perm(row & 31);
+      lsrc[i] = kbase + (int64_t)key * DH + ((slot ^ kswz<DH>(row)) * 8);
+    } else {
+      const int d = 8 * (q - K_INS) + lane / 8;
+      lsrc[i] = vbase + (int64_t)d * s.kmax_pad + ((lane % 8) ^ vswz(d)) * 8;
     }
+  }
+  auto issue = [&](int kt, int stage) {
+    unsigned char* sb = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < V_LD; ++i) {
-      const int ci = tid + 256 * i, d = ci >> 3, vc = ci & 7;
-      rv[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)d * s.kmax_pad + key0 + vc * 8);
+    for (int i = 0; i < QW; ++i) {
+      const int q = wave + 4 * i;
+      // K rows step by DH elements per key, V rows by one element per key
+      const int64_t off = q < K_INS ? (int64_t)kt * BN * DH : (int64_t)kt * BN;
+      attn_load_lds16(lsrc[i] + off, sb + q * 1024);
     }
   };
-  auto lstore = [&](int stage) {
-    unsigned char* sk = smem + stage * STAGE;
-    unsigned char* sv = sk + K_BYTES;
-#pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int ci = tid + 256 * i, kr = ci / KCH, kc = ci - kr * KCH;
-      const int row = (kr & ~31) | key_perm(kr & 31);
-      *reinterpret_cast<u32x4*>(sk + row * KROW + ((kc ^ (row & 7)) << 4)) = rk[i];
+  auto wait_tile = [&](int newer) {  // loads of later tiles may stay in flight
+    if constexpr (NST >= 3) {
+      if (newer >= 1) {
+        __builtin_amdgcn_s_waitcnt((QW & 15) | ((QW >> 4) << 14) | (7 << 4) | (0 << 8));
+        return;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < V_LD; ++i) {
-      const int ci = tid + 256 * i, d = ci >> 3, vc = ci & 7;
-      *reinterpret_cast<u32x4*>(sv + d * 128 + ((vc ^ (d & 7)) << 4)) = rv[i];
-    }
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+  };
+  auto barrier = [&]() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
   f32x16 oacc[NDB];
@@ -136,14 +208,25 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
   const float sc = a.scale_log2;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) gload(kt + 1);
+  {
+    int issued = 0;
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i)
+      if (kt_begin + i < kt_end) {
+        issue(kt_begin + i, i);
+        ++issued;
+      }
+    wait_tile(issued - 1);
+    barrier();
+  }
+  int stage = 0;
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    int fill = stage + NST - 1;
+    fill = fill >= NST ? fill - NST : fill;
+    if (kt + NST - 1 < kt_end) issue(kt + NST - 1, fill);
     const int key0 = kt * BN;
     if (wave_active && key0 <= wave_maxpos) {
-      const unsigned char* sk = smem + (kt & 1) * STAGE;
+      const unsigned char* sk = smem + stage * STAGE;
       const unsigned char* sv = sk + K_BYTES;
       f32x16 sacc[2];
 #pragma unroll
@@ -152,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) sacc[x][e] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const int pch = ((2 * ks + lgrp) ^ (lrow & 7)) << 4;
+        const int pch = ((2 * ks + lgrp) ^ kswz<DH>(lrow)) << 4;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lrow) * KROW + pch);
@@ -176,7 +259,6 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx * sc);
-      const float alpha = exp2f(m_run - m_new);
       float rs = 0.0f;
       u32x4 pf[2][2];
 #pragma unroll
@@ -185,17 +267,25 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const float p0 = exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_new));
-            const float p1 = exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_new));
-            rs += p0 + p1;
-            pf[kb][st][w] = pack_f16x2(p0, p1);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_new));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_new));
+            const uint32_t pk = pack_f16x2(p0, p1);
+            pf[kb][st][w] = pk;
+            // the row sum is taken over the f16 probabilities that P V uses
+            rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, pk),
+                                        (__attribute__((ext_vector_type(2))) _Float16){1.0f16, 1.0f16}, rs, false);
           }
-      l_run = l_run * alpha + rs;
+      // rescale only when some row's maximum moved (alpha == 1 otherwise)
+      if (__any(m_new != m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int x = 0; x < NDB; ++x)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
+      }
+      l_run += rs;
       m_run = m_new;
-#pragma unroll
-      for (int x = 0; x < NDB; ++x)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int row = db * 32 + lrow;
@@ -204,18 +294,21 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             const int ch = 4 * kb + 2 * st + lgrp;
-            const u32x4 vf = *reinterpret_cast<const u32x4*>(sv + row * 128 + ((ch ^ (row & 7)) << 4));
+            const u32x4 vf = *reinterpret_cast<const u32x4*>(sv + row * 128 + ((ch ^ vswz(row)) << 4));
             oacc[db] = mfma_f16(vf, pf[kb][st], oacc[db]);
           }
       }
     }
-    if (kt + 1 < nkt) lstore((kt + 1) & 1);
-    __syncthreads();
+    const int last_issued = (kt + NST - 1 < kt_end) ? kt + NST - 1 : kt_end - 1;
+    wait_tile(last_issued - (kt + 1));
+    barrier();
+    stage = stage + 1 == NST ? 0 : stage + 1;
   }
 
-  // ---- normalise and store ------------------------------------------------
+  // ---- store: final f16 output, or the piece's partial state ------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (wave_active && lane_valid) {
+  if (!wave_active || !lane_valid) return;
+  if (g.ns == 1) {
     const float inv = 1.0f / l_tot;
     uint16_t* orow = a.o + ((int64_t)b * s.T + t_lane) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH;
 #pragma unroll
@@ -227,24 +320,149 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnArgs a) {
                  pack_f16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + d) = pk;
       }
+  } else {
+    const int64_t pidx = (int64_t)(piece_base + piece) * per_bh + bh;
+    const int r = t_lane - g.t0;
+    float* po = a.part_o + (pidx * 128 + r) * DH;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * lgrp;
+        f32x4 v{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(po + d) = v;
+      }
+    if (lgrp == 0) {
+      a.part_ml[(pidx * 2 + 0) * 128 + r] = m_run;
+      a.part_ml[(pidx * 2 + 1) * 128 + r] = l_tot;
+    }
   }
 }
 
+// Combines the pieces of every split block, in piece order:
+// O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p, m = max_p m_p.
+// One thread per (row, 4 head-dim columns).
+template <int DH>
+__global__ void attn_merge_kernel(AttnArgs a) {
+  const Shape& s = a.s;
+  const int per_bh = s.B * s.Hq;
+  const int cols = DH / 4;
+  int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // locate the split block this item belongs to
+  int piece_base = 0;
+  for (int bi = 0; bi < 2 * a.nrb; ++bi) {
+    const BlockGeo g = block_geo(s, a.nrb, a.kt_max, bi);
+    if (g.ns == 1) continue;
+    const int64_t n = (int64_t)per_bh * 128 * cols;
+    if (item >= n) {
+      item -= n;
+      piece_base += g.ns;
+      continue;
+    }
+    const int c4 = (int)(item % cols);
+    const int r = (int)((item / cols) % 128);
+    const int bh = (int)(item / (cols * 128));
+    const int t = g.t0 + r;
+    if (t >= g.row_end) return;
+    float mmax = -INFINITY;
+    for (int p = 0; p < g.ns; ++p) {
+      const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
+      mmax = fmaxf(mmax, a.part_ml[(pidx * 2 + 0) * 128 + r]);
+    }
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int p = 0; p < g.ns; ++p) {
+      const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
+      const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * 128 + r] - mmax);
+      l += w * a.part_ml[(pidx * 2 + 1) * 128 + r];
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (pidx * 128 + r) * DH + 4 * c4);
+      acc[0] += w * v[0];
+      acc[1] += w * v[1];
+      acc[2] += w * v[2];
+      acc[3] += w * v[3];
+    }
+    const float inv = 1.0f / l;
+    const int b = bh / s.Hq, qh = bh - b * s.Hq;
+    uint16_t* orow = a.o + ((int64_t)b * s.T + t) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH + 4 * c4;
+    u32x2 pk{pack_f16x2(acc[0] * inv, acc[1] * inv), pack_f16x2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(orow) = pk;
+    return;
+  }
+}
+
+// ---- host-side plan (shared with workspace sizing) -----------------------
+static int host_nkt(const Shape& s, int nrb, int bi) {
+  const int late = bi < nrb ? 1 : 0;
+  const int rb = nrb - 1 - (late ? bi : bi - nrb);
+  const int row_begin = late * s.c, row_end = row_begin + s.c;
+  const int gstart = (late ? (2 * s.D - 1 - s.r) : s.r) * s.c;
+  const int t0 = row_begin + rb * 128;
+  const int last = t0 + 127 < row_end ? t0 + 127 : row_end - 1;
+  return (gstart + (last - row_begin) + 64) / 64;
+}
+
+AttnPlan attn_plan(const Shape& s) {
+  AttnPlan p;
+  p.nrb = (s.c + 127) / 128;
+  const int64_t blocks = (int64_t)2 * p.nrb * s.B * s.Hq;
+  int64_t tiles = 0;
+  for (int bi = 0; bi < 2 * p.nrb; ++bi) tiles += host_nkt(s, p.nrb, bi);
+  tiles *= (int64_t)s.B * s.Hq;
+  // split only when there are too few blocks to fill 256 CUs twice over
+  if (blocks >= 1024) {
+    p.kt_max = 1 << 30;
+  } else {
+    int64_t kt = (tiles + 511) / 512;
+    p.kt_max = (int)(kt < 16 ? 16 : kt);
+  }
+  p.units = 0;
+  p.pieces = 0;
+  for (int bi = 0; bi < 2 * p.nrb; ++bi) {
+    const int nkt = host_nkt(s, p.nrb, bi);
+    const int ns = (nkt + p.kt_max - 1) / p.kt_max;
+    p.units += (int64_t)ns * s.B * s.Hq;
+    if (ns > 1) p.pieces += ns;
+  }
+  p.split_rows = 0;
+  for (int bi = 0; bi < 2 * p.nrb; ++bi) {
+    const int nkt = host_nkt(s, p.nrb, bi);
+    if ((nkt + p.kt_max - 1) / p.kt_max > 1) p.split_rows += 128;
+  }
+  return p;
+}
+
+size_t attn_partial_bytes(const Shape& s) {
+  const AttnPlan p = attn_plan(s);
+  return (size_t)p.pieces * s.B * s.Hq * 128 * (s.dh + 2) * sizeof(float);
+}
+
 hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* knat,
-                             const uint16_t* vnat, uint16_t* o, hipStream_t st) {
+                             const uint16_t* vnat, uint16_t* o, float* partial, hipStream_t st) {
+  const AttnPlan p = attn_plan(s);
   AttnArgs a;
   a.q = q;
   a.knat = knat;
   a.vnat = vnat;
   a.o = o;
+  a.part_o = partial;
+  a.part_ml = partial + (size_t)p.pieces * s.B * s.Hq * 128 * s.dh;
   a.s = s;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.dh));
-  a.nrb = (s.c + 127) / 128;
-  dim3 grid((unsigned)(2 * a.nrb * s.B * s.Hq));
+  a.nrb = p.nrb;
+  a.kt_max = p.kt_max;
+  dim3 grid((unsigned)p.units);
   if (s.dh == 128)
-    hipLaunchKernelGGL(flash_attn_kernel<128>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((flash_attn_kernel<128, 2>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(flash_attn_kernel<64>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((flash_attn_kernel<64, 2>), grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.pieces == 0) return e;
+  const int64_t items = (int64_t)p.split_rows * s.B * s.Hq * (s.dh / 4);
+  const unsigned blocks = (unsigned)((items + 255) / 256);
+  if (s.dh == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -9,20 +9,22 @@
 // partial outputs are summed locally; the row split of the second matrix sums
 // exactly, bowenzhou.top "张量并行", section "机制：行切与列切").
 //
-// Design: 256 threads = 4 waves in a 2x2 grid; a BM x BN tile (x NB weight
-// matrices for the fused gate/up product) with BK = 64; global -> registers ->
-// LDS double buffer with one barrier per K step; XOR-swizzled 128-byte LDS
-// rows so both the 16-byte stores and the matrix-core operand reads are free
-// of bank conflicts; 32x32x16 MFMA with the weight tile as the first operand
-// so each lane ends up owning 4 consecutive output columns of one row.
-// Blocks are remapped so that the tiles that share a weight block run on the
-// same XCD (blocks are dealt round-robin to the 8 XCDs) and hit its L2.
+// Design: a workgroup of 4 or 8 waves computes a BM x BN tile (x NB weight
+// matrices for the fused gate/up product) with 32x32x16 MFMAs, the weight
+// tile as the first operand so each lane ends up owning 4 consecutive output
+// columns of one row.  Blocks are renumbered so the tiles that share a weight
+// block run on the same XCD (blocks are dealt round-robin to the 8 XCDs) and
+// hit its L2.  Details of the pipeline are at the kernel below.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace tsp {
 
-enum { EPI_QKV = 0, EPI_RESID_BF16X = 1, EPI_RESID_F32 = 2, EPI_SWIGLU = 3 };
+enum { EPI_QKV = 0, EPI_RESID_BF16X = 1, EPI_RESID_F32 = 2, EPI_SWIGLU = 3, EPI_PARTIAL = 4 };
 
 struct GemmArgs {
   const uint16_t* A;
@@ -39,6 +41,9 @@ struct GemmArgs {
   uint16_t* kv;
   Shape s;
   int32_t src_rank;
+  // split-K: nsplit > 1 writes float32 partial sums to partial[split][M][N]
+  int32_t nsplit;
+  float* partial;
 };
 
 __device__ __forceinline__ float silu_f32(float z) {
@@ -91,6 +96,9 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
     o[2] = r[2] + v[2];
     o[3] = r[3] + v[3];
     *reinterpret_cast<f32x4*>(a.out + off) = o;
+  } else if constexpr (EPI == EPI_PARTIAL) {
+    // v2 carries the split index in its first element's bits (see caller)
+    (void)v2;
   } else {  // EPI_SWIGLU: v = gate, v2 = up
     const int64_t off = (int64_t)m * a.N + n;
     u32x2 pk{pack_f16x2(silu_f32(v[0]) * v2[0], silu_f32(v[1]) * v2[1]),
@@ -99,80 +107,202 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
   }
 }
 
-template <int BM, int BN, int NB, bool F16, bool CONVB, int EPI, int OCC>
-__global__ __launch_bounds__(256, OCC) void gemm_kernel(GemmArgs a) {
-  constexpr int BK = 64;
-  constexpr int WM = BM / 2, WN = BN / 2;
+__device__ __forceinline__ void seg_offsets(const GemmArgs& a, int k, int64_t& aoff, int64_t& boff) {
+  const int sg = k / a.seg_len;
+  const int kk = k - sg * a.seg_len;
+  int j = sg;
+  if (a.ring_rank >= 0) {
+    j = a.ring_rank - sg;
+    j = j < 0 ? j + a.nseg : j;
+  }
+  aoff = (int64_t)j * a.a_seg_step + kk;
+  boff = (int64_t)j * a.b_seg_step + kk;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void load_lds16(const uint16_t* g, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_MFMA = 0x008, SG_DS_RD = 0x100;
+
+// --------------------------------------------------------------------------
+// Kernel: NST-deep LDS ring with every operand copied global -> LDS by direct
+// 16-byte loads (global_load_lds_dwordx4: lane i of a wave writes bytes
+// [16i, 16i+16) of a 1 KB run), so the loads for tile kt+NST-1 are in flight
+// while tile kt is multiplied.  The barrier between K tiles carries no memory
+// fence (see lds_barrier).  Weights that must become f16 are converted right
+// after their operand read (VALU work that overlaps the other waves' MFMAs).
+// LDS rows are BK*2 bytes; 16-byte slot c of row r sits at c ^ swz(r) so the
+// 16 rows of one operand read cover the 16 bank groups of the 64-bank LDS.
+// Operand reads of the next 16-wide K step are interleaved with this step's
+// MFMAs (sched_group_barrier), and the last step's MFMAs run after the
+// barrier, overlapping the first operand reads of the next tile.
+// Optional split-K (nsplit > 1): unit = (tile, K range), float32 partial tiles
+// summed in a fixed order by gemm_reduce_kernel (deterministic).
+// --------------------------------------------------------------------------
+template <int BK>
+__device__ __forceinline__ int gswz(int row) {
+  return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+// Waits until at most N vector-memory operations of this wave are pending and
+// all its LDS operations are done (expcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// makes the compiler wait for every outstanding load, including the tiles
+// prefetched for later K steps.  Callers wait for exactly what the next step
+// needs (wait_vmcnt) first; the signal fences keep the compiler from moving
+// LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Q/K/V scatter of one 32-row x 32-column accumulator block: the column
+// block lies inside one head of one shard, so its destination is worked out
+// once per block (wave-uniform) and only the row varies per lane.
+__device__ __forceinline__ void epi_qkv_block(const GemmArgs& a, int m, int nb0, int lgrp, const f32x16& acc) {
+  const Shape& s = a.s;
+  if (nb0 >= a.N) return;
+  const int j = nb0 / s.nqkv_s;
+  int w = nb0 - j * s.nqkv_s;
+  const int qd = s.Hq_s * s.dh, kvd = s.Hkv_s * s.dh;
+  if (m >= a.M) return;
+  const int b = m / s.T, t = m - b * s.T;
+  uint16_t* dst;
+  if (w < qd) {
+    if (a.q == nullptr) return;
+    const int head = j * s.Hq_s + w / s.dh, d0 = w % s.dh;
+    dst = a.q + ((((int64_t)b * s.Hq + head) * s.T + t) * s.dh + d0);
+  } else {
+    w -= qd;
+    const int sel = w >= kvd ? 1 : 0;
+    w -= sel * kvd;
+    dst = a.kv + (((((int64_t)j * s.D + a.src_rank) * 2 + sel) * s.B + b) * s.T + t) * kvd + w;
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    u32x2 pk{pack_f16x2(acc[4 * q4], acc[4 * q4 + 1]), pack_f16x2(acc[4 * q4 + 2], acc[4 * q4 + 3])};
+    *reinterpret_cast<u32x2*>(dst + 8 * q4 + 4 * lgrp) = pk;
+  }
+}
+
+template <int BM, int BN, int NB, int WGM, int NW, int BK, int NST, bool SEGFAST, bool F16, bool CONVB, int EPI,
+          int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
+  constexpr int WGN = NW / WGM;
+  constexpr int ROWB = BK * 2, SLOTS = BK / 8, RPI = 1024 / ROWB;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NBL = WN / 32;
-  constexpr int A_LD = BM / 32, B_LD = NB * BN / 32;
-  constexpr int ROWB = BK * 2;
+  constexpr int BROWS = NB * BN;
   constexpr int A_BYTES = BM * ROWB;
-  constexpr int STAGE = (BM + NB * BN) * ROWB;
-  __shared__ __align__(16) unsigned char smem[2 * STAGE];
+  constexpr int STAGE = (BM + BROWS) * ROWB;
+  constexpr int QA = BM / RPI;                   // direct-load instructions of the A tile
+  constexpr int QT = (BM + BROWS) / RPI;         // ... of the whole stage
+  constexpr int QI = (QT + NW - 1) / NW;         // per wave, at most
+  constexpr int C_HI = QI, C_LO = QT / NW;       // per-wave counts (waves < QT % NW have C_HI)
+  constexpr int KS = BK / 16;
+  constexpr int NFRAG = MB + NB * NBL;
+  constexpr int NMFMA = MB * NB * NBL;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(NST >= 2 && NST <= 5, "stages");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(BM % RPI == 0 && BROWS % RPI == 0, "load split");
+  static_assert((NST - 2) * C_HI < 64, "vmcnt range");
+  __shared__ __align__(16) unsigned char smem[NST * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const bool hi_count = (QT % NW == 0) || (wave < QT % NW);
 
-  // tile index: XCD-grouped so the blocks of one XCD cover consecutive tiles
   const int mtiles = (a.M + BM - 1) / BM;
   const int ntiles = mtiles * ((a.N + BN - 1) / BN);
-  int logical;
+  const int units = ntiles * a.nsplit;
+  int u;
   {
     const int bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
-    const int q = ntiles >> 3, rem = ntiles & 7;
-    logical = xcd * q + (xcd < rem ? xcd : rem) + idx;
+    const int q = units >> 3, rem = units & 7;
+    u = xcd * q + (xcd < rem ? xcd : rem) + idx;
   }
-  const int mt = logical % mtiles, nt = logical / mtiles;
+  const int tile = u % ntiles, split = u / ntiles;
+  const int mt = tile % mtiles, nt = tile / mtiles;
   const int m0 = mt * BM, n0 = nt * BN;
+  const int nk_all = a.K / BK;
+  const int per = (nk_all + a.nsplit - 1) / a.nsplit;
+  const int kt0 = split * per;
+  const int kt1 = (kt0 + per < nk_all) ? kt0 + per : nk_all;
 
-  // global load assignment: row r_in (+32 i), 16-byte chunk cc of the 128-byte K slice
-  const int r_in = tid >> 3, cc = tid & 7;
-  const uint16_t* aptr[A_LD];
-  const uint16_t* bptr[B_LD];
+  // direct loads: instruction q writes LDS rows RPI q ..; lane i lands in row
+  // RPI q + i / SLOTS at physical slot i % SLOTS (logical slot ^ swizzle)
+  const uint16_t* src[QI];
+  int chunk[QI];
+  bool isb[QI];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    int m = m0 + r_in + 32 * i;
-    m = m < a.M ? m : a.M - 1;
-    aptr[i] = a.A + (int64_t)m * a.lda;
-  }
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int row = r_in + 32 * i;
-    const int which = row / BN;
-    int n = n0 + (row - which * BN);
-    n = n < a.N ? n : a.N - 1;
-    const uint16_t* base = (NB == 2 && which == 1) ? a.B1 : a.B0;
-    bptr[i] = base + (int64_t)n * a.ldb;
-  }
-  const int st_off = r_in * ROWB + ((cc ^ (r_in & 7)) << 4);
-
-  u32x4 ra[A_LD], rb[B_LD];
-  auto gload = [&](int kt) {
-    const int k = kt * BK + cc * 8;
-    const int sg = k / a.seg_len;
-    const int kk = k - sg * a.seg_len;
-    int j = sg;
-    if (a.ring_rank >= 0) {
-      j = a.ring_rank - sg;
-      j = j < 0 ? j + a.nseg : j;
+  for (int i = 0; i < QI; ++i) {
+    const int q = wave + NW * i;
+    const int row = RPI * q + lane / SLOTS;
+    chunk[i] = (lane % SLOTS) ^ gswz<BK>(row);
+    isb[i] = q >= QA;
+    if (q < QA) {
+      int m = m0 + row;
+      m = m < a.M ? m : a.M - 1;
+      src[i] = a.A + (int64_t)m * a.lda;
+    } else {
+      const int brow = row - BM;
+      const int which = brow / BN;
+      int n = n0 + brow - which * BN;
+      n = n < a.N ? n : a.N - 1;
+      src[i] = ((NB == 2 && which == 1) ? a.B1 : a.B0) + (int64_t)n * a.ldb;
     }
-    const int64_t aoff = (int64_t)j * a.a_seg_step + kk;
-    const int64_t boff = (int64_t)j * a.b_seg_step + kk;
+    if constexpr (SEGFAST) src[i] += chunk[i] * 8;
+  }
+  // K cursor of the next tile to load (segment s, offset kk inside it)
+  int cur_s = 0, cur_kk = 0;
+  if constexpr (SEGFAST) {
+    const int k = kt0 * BK;
+    cur_s = k / a.seg_len;
+    cur_kk = k - cur_s * a.seg_len;
+  }
+  auto issue_loads = [&](int kt, int stage) {
+    unsigned char* sbase = smem + stage * STAGE;
+    int64_t aoff_u = 0, boff_u = 0;
+    if constexpr (SEGFAST) {
+      int j = cur_s;
+      if (a.ring_rank >= 0) {
+        j = a.ring_rank - cur_s;
+        j = j < 0 ? j + a.nseg : j;
+      }
+      aoff_u = (int64_t)j * a.a_seg_step + cur_kk;
+      boff_u = (int64_t)j * a.b_seg_step + cur_kk;
+      cur_kk += BK;
+      if (cur_kk >= a.seg_len) {
+        cur_kk -= a.seg_len;
+        ++cur_s;
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(aptr[i] + aoff);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + boff);
-  };
-  auto lstore = [&](int stage) {
-    unsigned char* sa = smem + stage * STAGE;
-    unsigned char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(sa + st_off + i * 32 * ROWB) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      u32x4 v = rb[i];
-      if constexpr (CONVB) v = bf16x8_to_f16x8(v);
-      *reinterpret_cast<u32x4*>(sb + st_off + i * 32 * ROWB) = v;
+    for (int i = 0; i < QI; ++i) {
+      const int q = wave + NW * i;
+      if (q < QT) {
+        int64_t off;
+        if constexpr (SEGFAST) {
+          off = isb[i] ? boff_u : aoff_u;
+        } else {
+          int64_t ao, bo;
+          seg_offsets(a, kt * BK + chunk[i] * 8, ao, bo);
+          off = isb[i] ? bo : ao;
+        }
+        load_lds16(src[i] + off, sbase + q * 1024);
+      }
     }
   };
 
@@ -186,92 +316,261 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[x][y][z][e] = 0.0f;
 
-  const int lrow = lane & 31, lgrp = lane >> 5, lsw = lane & 7;
-  const int nk = a.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const unsigned char* sa = smem + cur * STAGE;
+  const int lrow = lane & 31, lgrp = lane >> 5, lsw = gswz<BK>(lane & 31);
+  u32x4 af[2][MB], bf[2][NB][NBL];
+  auto read_frags = [&](int stage, int ks, int buf) {
+    const unsigned char* sa = smem + stage * STAGE;
     const unsigned char* sb = sa + A_BYTES;
+    const int pch = ((2 * ks + lgrp) ^ lsw) << 4;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int pch = ((2 * ks + lgrp) ^ lsw) << 4;
-      u32x4 af[MB], bf[NB][NBL];
+    for (int z = 0; z < MB; ++z)
+      af[buf][z] = *reinterpret_cast<const u32x4*>(sa + (wm * WM + z * 32 + lrow) * ROWB + pch);
 #pragma unroll
-      for (int z = 0; z < MB; ++z)
-        af[z] = *reinterpret_cast<const u32x4*>(sa + (wm * WM + z * 32 + lrow) * ROWB + pch);
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int y = 0; y < NBL; ++y)
+        bf[buf][x][y] = *reinterpret_cast<const u32x4*>(sb + (x * BN + wn * WN + y * 32 + lrow) * ROWB + pch);
+  };
+  auto mfmas = [&](int buf) {
+    if constexpr (CONVB) {
 #pragma unroll
       for (int x = 0; x < NB; ++x)
 #pragma unroll
-        for (int y = 0; y < NBL; ++y)
-          bf[x][y] = *reinterpret_cast<const u32x4*>(sb + (x * BN + wn * WN + y * 32 + lrow) * ROWB + pch);
-#pragma unroll
-      for (int x = 0; x < NB; ++x)
-#pragma unroll
-        for (int y = 0; y < NBL; ++y)
-#pragma unroll
-          for (int z = 0; z < MB; ++z) {
-            if constexpr (F16)
-              acc[x][y][z] = mfma_f16(bf[x][y], af[z], acc[x][y][z]);
-            else
-              acc[x][y][z] = mfma_bf16(bf[x][y], af[z], acc[x][y][z]);
-          }
+        for (int y = 0; y < NBL; ++y) bf[buf][x][y] = bf16x8_to_f16x8(bf[buf][x][y]);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int y = 0; y < NBL; ++y)
+#pragma unroll
+        for (int z = 0; z < MB; ++z) {
+          if constexpr (F16)
+            acc[x][y][z] = mfma_f16(bf[buf][x][y], af[buf][z], acc[x][y][z]);
+          else
+            acc[x][y][z] = mfma_bf16(bf[buf][x][y], af[buf][z], acc[x][y][z]);
+        }
+  };
+  auto schedule_step = [&]() {
+    constexpr int NPAIR = NFRAG < NMFMA ? NFRAG : NMFMA;
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    }
+    if constexpr (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NMFMA - NPAIR, 0);
+    if constexpr (NFRAG > NPAIR) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, NFRAG - NPAIR, 0);
+  };
+  // wait until this wave's loads of the tile issued `newer` tiles before the
+  // most recent one have landed (loads complete in issue order)
+  auto wait_tile = [&](int newer) {
+    if constexpr (NST >= 5) {
+      if (newer >= 3) {
+        if (hi_count) wait_vmcnt<3 * C_HI>(); else wait_vmcnt<3 * C_LO>();
+        return;
+      }
+    }
+    if constexpr (NST >= 4) {
+      if (newer >= 2) {
+        if (hi_count) wait_vmcnt<2 * C_HI>(); else wait_vmcnt<2 * C_LO>();
+        return;
+      }
+    }
+    if constexpr (NST >= 3) {
+      if (newer >= 1) {
+        if (hi_count) wait_vmcnt<C_HI>(); else wait_vmcnt<C_LO>();
+        return;
+      }
+    }
+    wait_vmcnt<0>();
+  };
+
+  if (kt0 < kt1) {
+    int issued = 0;
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i)
+      if (kt0 + i < kt1) {
+        issue_loads(kt0 + i, i);
+        ++issued;
+      }
+    wait_tile(issued - 1);
+    lds_barrier();
+    read_frags(0, 0, 0);
+  }
+  int stage = 0;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    int fill = stage + NST - 1;
+    fill = fill >= NST ? fill - NST : fill;
+    if (kt + NST - 1 < kt1) issue_loads(kt + NST - 1, fill);
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      read_frags(stage, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+      schedule_step();
+    }
+    const int last_issued = (kt + NST - 1 < kt1) ? kt + NST - 1 : kt1 - 1;
+    wait_tile(last_issued - (kt + 1));
+    lds_barrier();
+    const int nstage = stage + 1 == NST ? 0 : stage + 1;
+    if (kt + 1 < kt1) read_frags(nstage, 0, 0);
+    mfmas((KS - 1) & 1);
+    stage = nstage;
   }
 
-  // epilogue: lane owns row m = ... + lrow and columns n..n+3 per register quad
 #pragma unroll
   for (int y = 0; y < NBL; ++y)
 #pragma unroll
     for (int z = 0; z < MB; ++z) {
       const int m = m0 + wm * WM + z * 32 + lrow;
+      const int nb0 = n0 + wn * WN + y * 32;
+      if constexpr (EPI == EPI_QKV) {
+        epi_qkv_block(a, m, nb0, lgrp, acc[0][y][z]);
+      } else {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int n = n0 + wn * WN + y * 32 + 8 * q4 + 4 * lgrp;
-        float v[4], v2[4];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int n = nb0 + 8 * q4 + 4 * lgrp;
+          float v[4], v2[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = acc[0][y][z][4 * q4 + e];
-          v2[e] = acc[NB - 1][y][z][4 * q4 + e];
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[0][y][z][4 * q4 + e];
+            v2[e] = acc[NB - 1][y][z][4 * q4 + e];
+          }
+          if constexpr (EPI == EPI_PARTIAL) {
+            if (m < a.M && n < a.N) {
+              f32x4 o{v[0], v[1], v[2], v[3]};
+              *reinterpret_cast<f32x4*>(a.partial + ((int64_t)split * a.M + m) * a.N + n) = o;
+            }
+          } else {
+            epilogue4<EPI>(a, m, n, v, v2);
+          }
         }
-        epilogue4<EPI>(a, m, n, v, v2);
       }
     }
+}
+
+// Sums the split-K partials in split order and applies the residual epilogue:
+// out = resid + sum_p partial[p]  (resid bf16 when EPI == EPI_RESID_BF16X,
+// float32 when EPI_RESID_F32), plus the f16 copy when out16 != nullptr.
+template <int EPI>
+__global__ void gemm_reduce_kernel(GemmArgs a) {
+  const int64_t n4 = (int64_t)a.M * a.N / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const int64_t off = i * 4;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(a.partial + off);
+    for (int p = 1; p < a.nsplit; ++p) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(a.partial + (int64_t)p * a.M * a.N + off);
+      acc[0] += t[0];
+      acc[1] += t[1];
+      acc[2] += t[2];
+      acc[3] += t[3];
+    }
+    const int m = (int)(off / a.N), n = (int)(off - (int64_t)m * a.N);
+    float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+    epilogue4<EPI>(a, m, n, v, v);
+  }
 }
 
 // --------------------------------------------------------------------------
 // Host-side tile choice and launch
 // --------------------------------------------------------------------------
-template <int BM, int BN, int NB, bool F16, bool CONVB, int EPI, int OCC>
-static hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
+template <int BM, int BN, int NB, int WGM, int NW, int BK, int NST, bool SEGFAST, bool F16, bool CONVB, int EPI,
+          int OCC>
+static hipError_t launch_tile_seg(GemmArgs a, int nsplit, hipStream_t st) {
   const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, NB, F16, CONVB, EPI, OCC>), dim3(mt * nt), dim3(256), 0, st, a);
+  if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BF16X) {
+    if (nsplit > 1 && a.partial != nullptr) {
+      a.nsplit = nsplit;
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, NB, WGM, NW, BK, NST, SEGFAST, F16, CONVB, EPI_PARTIAL, OCC>),
+                         dim3(mt * nt * nsplit), dim3(64 * NW), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      int64_t blocks = ((int64_t)a.M * a.N / 4 + 255) / 256;
+      if (blocks > 2048) blocks = 2048;
+      hipLaunchKernelGGL((gemm_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  a.nsplit = 1;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, NB, WGM, NW, BK, NST, SEGFAST, F16, CONVB, EPI, OCC>), dim3(mt * nt),
+                     dim3(64 * NW), 0, st, a);
   return hipGetLastError();
+}
+
+// Segments that are whole multiples of BK never split a K tile, so the
+// segment cursor can be kept per tile instead of per lane.
+template <int BM, int BN, int NB, int WGM, int NW, int BK, int NST, bool F16, bool CONVB, int EPI, int OCC>
+static hipError_t launch_tile(GemmArgs a, int nsplit, hipStream_t st) {
+  if (a.seg_len % BK == 0)
+    return launch_tile_seg<BM, BN, NB, WGM, NW, BK, NST, true, F16, CONVB, EPI, OCC>(a, nsplit, st);
+  return launch_tile_seg<BM, BN, NB, WGM, NW, BK, NST, false, F16, CONVB, EPI, OCC>(a, nsplit, st);
 }
 
 static int tiles_of(int M, int N, int bm, int bn) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-// Rough cost of a tile choice: waves of 256 CUs x tile work / relative
-// per-CU efficiency of that tile shape.
-static double tile_cost(int M, int N, int bm, int bn, int nb, double eff) {
-  const int t = tiles_of(M, N, bm, bn);
-  const int waves = (t + 255) / 256;
-  return waves * (double)bm * bn * nb / eff;
+// Tuning override (no effect unless set): TSP_GEMM_<NAME>=<config>[:<nsplit>].
+static int env_choice(const char* name, int* nsplit) {
+  char key[64];
+  snprintf(key, sizeof(key), "TSP_GEMM_%s", name);
+  const char* v = getenv(key);
+  if (v == nullptr || *v == 0) return -1;
+  int cfg = atoi(v);
+  const char* c = strchr(v, ':');
+  if (c != nullptr && nsplit != nullptr) *nsplit = atoi(c + 1);
+  return cfg;
+}
+
+// Single-weight GEMM configurations (tile M x N, waves, K step, LDS stages):
+//   0: 256x256, 8 waves (2x4), BK 32, 5 stages
+//   1: 256x192, 8 waves (4x2), BK 32, 5 stages
+//   2: 256x128, 8 waves (2x4), BK 64, 3 stages
+//   3: 128x128, 4 waves (2x2), BK 64, 4 stages
+template <bool F16, bool CONVB, int EPI>
+static hipError_t launch_cfg(const GemmArgs& a, int cfg, int nsplit, hipStream_t st) {
+  switch (cfg) {
+    case 0: return launch_tile<256, 256, 1, 2, 8, 32, 5, F16, CONVB, EPI, 1>(a, nsplit, st);
+    case 1: return launch_tile<256, 192, 1, 4, 8, 32, 5, F16, CONVB, EPI, 1>(a, nsplit, st);
+    case 2: return launch_tile<256, 128, 1, 2, 8, 64, 3, F16, CONVB, EPI, 1>(a, nsplit, st);
+    default: return launch_tile<128, 128, 1, 2, 4, 64, 4, F16, CONVB, EPI, 1>(a, nsplit, st);
+  }
+}
+
+static const int kCfgBM[4] = {256, 256, 256, 128};
+static const int kCfgBN[4] = {256, 192, 128, 128};
+
+// Choice for the M x h projections (output and down): big tiles when they
+// fill the chip; otherwise split K so that tiles x splits ~ 256 work units.
+// Long K (the down projection) keeps 256x256 tiles and splits more; short K
+// (the output projection) uses 256x128 tiles and splits less.
+static void choose_resid(const GemmArgs& a, int max_split, int* cfg, int* nsplit) {
+  *nsplit = 1;
+  if (tiles_of(a.M, a.N, 256, 256) >= 192 || max_split <= 1) {
+    *cfg = tiles_of(a.M, a.N, 256, 256) >= 192 ? 0 : 3;
+    return;
+  }
+  *cfg = a.K >= 8192 ? 0 : 2;
+  const int t = tiles_of(a.M, a.N, kCfgBM[*cfg], kCfgBN[*cfg]);
+  int p = (256 + t - 1) / t;
+  *nsplit = p > max_split ? max_split : p;
 }
 
 template <bool F16, bool CONVB, int EPI>
-static hipError_t launch_single(const GemmArgs& a, hipStream_t st) {
-  const double big = tile_cost(a.M, a.N, 256, 256, 1, 1.0);
-  const double small = tile_cost(a.M, a.N, 128, 128, 1, 0.8);
-  if (big <= small) return launch_tile<256, 256, 1, F16, CONVB, EPI, 1>(a, st);
-  return launch_tile<128, 128, 1, F16, CONVB, EPI, 2>(a, st);
+static hipError_t launch_single(const GemmArgs& a, const char* name, int max_split, hipStream_t st) {
+  int nsplit = 1, cfg;
+  if (EPI == EPI_QKV) {
+    cfg = a.N % 192 == 0 ? 1 : 0;
+  } else {
+    choose_resid(a, max_split, &cfg, &nsplit);
+  }
+  int env_split = nsplit;
+  const int env_cfg = env_choice(name, &env_split);
+  if (env_cfg >= 0) {
+    cfg = env_cfg;
+    nsplit = env_split;
+  }
+  if (nsplit < 1 || nsplit > max_split || a.partial == nullptr) nsplit = 1;
+  return launch_cfg<F16, CONVB, EPI>(a, cfg, nsplit, st);
 }
 
 static GemmArgs base_args(const Shape& s) {
@@ -279,6 +578,7 @@ static GemmArgs base_args(const Shape& s) {
   a.s = s;
   a.ring_rank = -1;
   a.nseg = 1;
+  a.nsplit = 1;
   return a;
 }
 
@@ -296,11 +596,12 @@ hipError_t launch_qkv_gemm(const Shape& s, int src_rank, const uint16_t* x, cons
   a.q = q;
   a.kv = kv_gathered;
   a.src_rank = src_rank;
-  return launch_single<false, false, EPI_QKV>(a, st);
+  return launch_single<false, false, EPI_QKV>(a, "QKV", 1, st);
 }
 
 hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* w_o,
-                             const uint16_t* x_resid, float* out, uint16_t* out16, hipStream_t st) {
+                             const uint16_t* x_resid, float* out, uint16_t* out16, float* partial,
+                             hipStream_t st) {
   GemmArgs a = base_args(s);
   const int seg = s.Hq_s * s.dh;
   a.A = o;
@@ -317,7 +618,8 @@ hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* 
   a.out = out;
   a.out16 = out16;
   a.resid = x_resid;
-  return launch_single<true, true, EPI_RESID_BF16X>(a, st);
+  a.partial = partial;
+  return launch_single<true, true, EPI_RESID_BF16X>(a, "OPROJ", gemm_split_plan(s), st);
 }
 
 hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_t* w_g,
@@ -333,14 +635,16 @@ hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_
   a.K = s.h;
   a.seg_len = s.h;
   a.out16 = act;
-  const double c1 = tile_cost(a.M, a.N, 256, 128, 2, 1.0);
-  const double c2 = tile_cost(a.M, a.N, 128, 128, 2, 0.85);
-  if (c1 <= c2) return launch_tile<256, 128, 2, true, true, EPI_SWIGLU, 1>(a, st);
-  return launch_tile<128, 128, 2, true, true, EPI_SWIGLU, 1>(a, st);
+  // Dual-weight (gate and up) configurations:
+  //   0: 128x128 (x2), 4 waves, BK 64, 3 stages;  1: 256x128 (x2), 8 waves, BK 32, 4 stages
+  int cfg = env_choice("GATEUP", nullptr);
+  if (cfg < 0) cfg = 0;
+  if (cfg == 1) return launch_tile<256, 128, 2, 2, 8, 32, 4, true, true, EPI_SWIGLU, 1>(a, 1, st);
+  return launch_tile<128, 128, 2, 2, 4, 64, 3, true, true, EPI_SWIGLU, 1>(a, 1, st);
 }
 
 hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t* w_d,
-                            const float* resid, float* y, hipStream_t st) {
+                            const float* resid, float* y, float* partial, hipStream_t st) {
   GemmArgs a = base_args(s);
   a.A = act;
   a.lda = s.F;
@@ -356,7 +660,8 @@ hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t*
   a.ring_rank = s.r;
   a.out = y;
   a.resid = resid;
-  return launch_single<true, true, EPI_RESID_F32>(a, st);
+  a.partial = partial;
+  return launch_single<true, true, EPI_RESID_F32>(a, "DOWN", gemm_split_plan(s), st);
 }
 
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n4) {

@@ -17,10 +17,25 @@ hipError_t launch_kv_reorder(const Shape& s, const uint16_t* gathered, uint16_t*
 hipError_t launch_qkv_gemm(const Shape& s, int src_rank, const uint16_t* x, const uint16_t* w_qkv,
                            uint16_t* q, uint16_t* kv_gathered, hipStream_t st);
 
+// Largest split-K factor of the output and down projections; `partial` (float
+// [kMaxSplit][M][h]) may be nullptr, which disables split-K.
+constexpr int kMaxSplit = 4;
+
+// Split-K factor planned for the output and down projections (both produce
+// an M x h result): 1 when 256x256 tiles already cover the 256 CUs, else up to
+// kMaxSplit.  The workspace holds split * M * h floats when it is > 1.
+inline int gemm_split_plan(const Shape& s) {
+  const int tiles = ((s.M + 255) / 256) * ((s.h + 255) / 256);
+  if (tiles >= 128) return 1;
+  int p = (256 + tiles - 1) / tiles;
+  return p > kMaxSplit ? kMaxSplit : p;
+}
+
 // out = x(bf16) + O * W_o^T over the D shards' K-segments; also an f16 copy
 // of out when out16 != nullptr.
 hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* w_o,
-                             const uint16_t* x_resid, float* out, uint16_t* out16, hipStream_t st);
+                             const uint16_t* x_resid, float* out, uint16_t* out16, float* partial,
+                             hipStream_t st);
 
 // act = silu(h16 Wg^T) * (h16 Wu^T) (f16 matrix cores, weights bf16->f16).
 hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_t* w_g,
@@ -28,13 +43,25 @@ hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_
 
 // y = resid + sum over ring steps of act_j W_d,j^T.
 hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t* w_d,
-                            const float* resid, float* y, hipStream_t st);
+                            const float* resid, float* y, float* partial, hipStream_t st);
 
 // f32 -> f16 rounding copy (MLP input when it arrives as float32).
 hipError_t launch_f32_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t st);
 
-// Causal flash attention over the natural-order K/V.
+// Causal flash attention over the natural-order K/V.  Blocks of 128 query rows
+// whose key range is long are cut into pieces along the keys (plan below);
+// `partial` holds the pieces' state (attn_partial_bytes) and may be nullptr
+// only when the plan has no pieces.
+struct AttnPlan {
+  int nrb;          // 128-row blocks per zigzag chunk
+  int kt_max;       // key tiles (64 keys) per piece at most
+  int64_t units;    // work groups of the attention kernel
+  int pieces;       // pieces of split blocks, summed over the block list
+  int split_rows;   // 128 x (number of split blocks)
+};
+AttnPlan attn_plan(const Shape& s);
+size_t attn_partial_bytes(const Shape& s);
 hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* knat,
-                             const uint16_t* vnat, uint16_t* o, hipStream_t st);
+                             const uint16_t* vnat, uint16_t* o, float* partial, hipStream_t st);
 
 }  // namespace tsp

@@ -110,34 +110,58 @@ size_t bytes_gathered(const tsp::Shape& s) {
   return (size_t)s.D * s.D * 2 * s.B * s.T * s.Hkv_s * s.dh * 2;
 }
 
+// Scratch for partial results: the split-K partial sums of the output and
+// down projections, or the attention pieces; never live at the same time.
+size_t bytes_partial(const tsp::Shape& s) {
+  const int p = tsp::gemm_split_plan(s);
+  const size_t gemm = p > 1 ? (size_t)p * s.M * s.h * 4 : 0;
+  const size_t attn = tsp::attn_partial_bytes(s);
+  return gemm > attn ? gemm : attn;
+}
+
 struct AttnWs {
   uint16_t *q, *knat, *vnat, *o;
+  float* partial;
 };
 struct MlpWs {
   uint16_t *h16, *act;
+  float* partial;
 };
 
-size_t ws_attn(const tsp::Shape& s) { return up(bytes_q(s)) + up(bytes_kvnat(s)) + up(bytes_o(s)); }
-size_t ws_mlp(const tsp::Shape& s) { return up(bytes_h16(s)) + up(bytes_act(s)); }
-size_t ws_layer(const tsp::Shape& s) { return ws_attn(s) + up(bytes_h32(s)) + ws_mlp(s); }
-
-AttnWs carve_attn(const tsp::Shape& s, char* p) {
-  AttnWs w;
-  w.q = reinterpret_cast<uint16_t*>(p);
-  p += up(bytes_q(s));
-  w.knat = reinterpret_cast<uint16_t*>(p);
-  w.vnat = reinterpret_cast<uint16_t*>(p + bytes_knat(s));
-  p += up(bytes_kvnat(s));
-  w.o = reinterpret_cast<uint16_t*>(p);
-  return w;
+// Workspace layouts (256-byte aligned pieces):
+//   attention  [q | K,V natural | o | split-K partials]
+//   MLP        [h16 | act | split-K partials]
+//   layer      [q | K,V natural | o | h32 | h16 | act | split-K partials]
+size_t ws_attn(const tsp::Shape& s) {
+  return up(bytes_q(s)) + up(bytes_kvnat(s)) + up(bytes_o(s)) + up(bytes_partial(s));
+}
+size_t ws_mlp(const tsp::Shape& s) { return up(bytes_h16(s)) + up(bytes_act(s)) + up(bytes_partial(s)); }
+size_t ws_layer(const tsp::Shape& s) {
+  return up(bytes_q(s)) + up(bytes_kvnat(s)) + up(bytes_o(s)) + up(bytes_h32(s)) + up(bytes_h16(s)) +
+         up(bytes_act(s)) + up(bytes_partial(s));
 }
 
-MlpWs carve_mlp(const tsp::Shape& s, char* p) {
-  MlpWs w;
-  w.h16 = reinterpret_cast<uint16_t*>(p);
+char* carve_attn(const tsp::Shape& s, char* p, AttnWs* w) {
+  w->q = reinterpret_cast<uint16_t*>(p);
+  p += up(bytes_q(s));
+  w->knat = reinterpret_cast<uint16_t*>(p);
+  w->vnat = reinterpret_cast<uint16_t*>(p + bytes_knat(s));
+  p += up(bytes_kvnat(s));
+  w->o = reinterpret_cast<uint16_t*>(p);
+  p += up(bytes_o(s));
+  return p;
+}
+
+char* carve_mlp(const tsp::Shape& s, char* p, MlpWs* w) {
+  w->h16 = reinterpret_cast<uint16_t*>(p);
   p += up(bytes_h16(s));
-  w.act = reinterpret_cast<uint16_t*>(p);
-  return w;
+  w->act = reinterpret_cast<uint16_t*>(p);
+  p += up(bytes_act(s));
+  return p;
+}
+
+float* partial_or_null(const tsp::Shape& s, char* p) {
+  return bytes_partial(s) > 0 ? reinterpret_cast<float*>(p) : nullptr;
 }
 
 // ---- live per-kernel timing (see tsp_profile_kernel) -----------------------
@@ -200,8 +224,9 @@ int run_attention(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* 
   TSP_KLAUNCH(TSP_K_QKV, st, tsp::launch_qkv_gemm(s, s.r, x_local, w_qkv, w.q, kv_gathered, st),
               "qkv projection");
   TSP_KLAUNCH(TSP_K_REORDER, st, tsp::launch_kv_reorder(s, kv_gathered, w.knat, w.vnat, st), "kv reorder");
-  TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, w.knat, w.vnat, w.o, st), "flash attention");
-  TSP_KLAUNCH(TSP_K_OPROJ, st, tsp::launch_oproj_gemm(s, w.o, w_o, x_local, out, out16, st),
+  TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, w.knat, w.vnat, w.o, w.partial, st),
+              "flash attention");
+  TSP_KLAUNCH(TSP_K_OPROJ, st, tsp::launch_oproj_gemm(s, w.o, w_o, x_local, out, out16, w.partial, st),
               "output projection");
   return TSP_OK;
 }
@@ -209,7 +234,8 @@ int run_attention(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* 
 int run_mlp(const tsp::Shape& s, const uint16_t* h16, const float* resid, const uint16_t* w_gate,
             const uint16_t* w_up, const uint16_t* w_down, float* y, const MlpWs& w, hipStream_t st) {
   TSP_KLAUNCH(TSP_K_GATEUP, st, tsp::launch_gateup_gemm(s, h16, w_gate, w_up, w.act, st), "mlp gate/up");
-  TSP_KLAUNCH(TSP_K_DOWN, st, tsp::launch_down_gemm(s, w.act, w_down, resid, y, st), "mlp down ring");
+  TSP_KLAUNCH(TSP_K_DOWN, st, tsp::launch_down_gemm(s, w.act, w_down, resid, y, w.partial, st),
+              "mlp down ring");
   return TSP_OK;
 }
 
@@ -324,7 +350,8 @@ int tsp_attn_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t
   if (ws_bytes < ws_attn(s))
     return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_attn(s));
   TSP_TRY(check_device("tsp_attn_fwd"));
-  const AttnWs w = carve_attn(s, static_cast<char*>(ws));
+  AttnWs w;
+  w.partial = partial_or_null(s, carve_attn(s, static_cast<char*>(ws), &w));
   return run_attention(s, x_local, w_qkv, w_o, kv_gathered, out, nullptr, w, stream);
 }
 
@@ -342,7 +369,8 @@ int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const float* x, const uint16_t* w_g
   if (ws_bytes < ws_mlp(s))
     return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_mlp(s));
   TSP_TRY(check_device("tsp_mlp_ring_fwd"));
-  const MlpWs w = carve_mlp(s, static_cast<char*>(ws));
+  MlpWs w;
+  w.partial = partial_or_null(s, carve_mlp(s, static_cast<char*>(ws), &w));
   TSP_LAUNCH(tsp::launch_f32_to_f16(x, w.h16, (int64_t)s.M * s.h, stream), "mlp input rounding");
   return run_mlp(s, w.h16, x, w_gate, w_up, w_down, y, w, stream);
 }
@@ -365,12 +393,13 @@ int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_
   if (ws_bytes < ws_layer(s))
     return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_layer(s));
   TSP_TRY(check_device("tsp_layer_fwd"));
-  char* p = static_cast<char*>(ws);
-  const AttnWs aw = carve_attn(s, p);
-  p += ws_attn(s);
+  AttnWs aw;
+  MlpWs mw;
+  char* p = carve_attn(s, static_cast<char*>(ws), &aw);
   float* h32 = reinterpret_cast<float*>(p);
   p += up(bytes_h32(s));
-  const MlpWs mw = carve_mlp(s, p);
+  p = carve_mlp(s, p, &mw);
+  aw.partial = mw.partial = partial_or_null(s, p);
   TSP_TRY(run_attention(s, x_local, w_qkv, w_o, kv_gathered, h32, mw.h16, aw, stream));
   return run_mlp(s, mw.h16, h32, w_gate, w_up, w_down, y, mw, stream);
 }

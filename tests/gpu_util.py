@@ -14,7 +14,8 @@ REL_FROB = 5e-3
 # Small shapes: each spans several tiles with ragged tails; together they cover
 # GQA ratios 1/2/4/8, head_dim 64/128, B = 2, D = 1, one-row chunks (c = 1),
 # chunk lengths that are not multiples of the attention row block (c = 96,
-# 24), and MLP shards whose width is not a multiple of 64 (F/D = 176, 96).
+# 24), MLP shards whose width is not a multiple of 64 (F/D = 176, 96), and
+# attention blocks long enough to be split along the keys.
 SWEEP = {
     "mha_d2_r1": (1, 256, 2, 1, 256, 4, 4, 64, 768),
     "gqa4_dh128_d4_r2": (1, 512, 4, 2, 256, 16, 4, 128, 512),
@@ -25,6 +26,10 @@ SWEEP = {
     "c24_generic_reorder": (1, 96, 2, 0, 128, 4, 2, 64, 192),
     "wide_tiles_dh128": (1, 1024, 2, 0, 512, 8, 8, 128, 1536),
     "gqa2_b2_dh128_c80": (2, 320, 2, 1, 256, 8, 4, 128, 640),
+    # few 128-row blocks with long key ranges: attention splits blocks into
+    # key pieces and merges them
+    "split_keys_dh128": (1, 4096, 2, 0, 128, 2, 2, 128, 256),
+    "split_keys_gqa_b2": (2, 2048, 2, 1, 128, 4, 2, 64, 256),
 }
 
 
