@@ -19,6 +19,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -196,6 +198,42 @@ __device__ __forceinline__ void epi_qkv_block(const GemmArgs& a, int m, int nb0,
   }
 }
 
+// Epilogue of one wave's MB x NBL grid of 32x32 accumulator blocks (x NB
+// weight matrices), rows from m_base, columns from n_base.
+template <int MB, int NBL, int NB, int EPI>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[NB][NBL][MB], int m_base,
+                                           int n_base, int lrow, int lgrp, int split) {
+#pragma unroll
+  for (int y = 0; y < NBL; ++y)
+#pragma unroll
+    for (int z = 0; z < MB; ++z) {
+      const int m = m_base + z * 32 + lrow;
+      const int nb0 = n_base + y * 32;
+      if constexpr (EPI == EPI_QKV) {
+        epi_qkv_block(a, m, nb0, lgrp, acc[0][y][z]);
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int n = nb0 + 8 * q4 + 4 * lgrp;
+          float v[4], v2[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[0][y][z][4 * q4 + e];
+            v2[e] = acc[NB - 1][y][z][4 * q4 + e];
+          }
+          if constexpr (EPI == EPI_PARTIAL) {
+            if (m < a.M && n < a.N) {
+              f32x4 o{v[0], v[1], v[2], v[3]};
+              *reinterpret_cast<f32x4*>(a.partial + ((int64_t)split * a.M + m) * a.N + n) = o;
+            }
+          } else {
+            epilogue4<EPI>(a, m, n, v, v2);
+          }
+        }
+      }
+    }
+}
+
 template <int BM, int BN, int NB, int WGM, int NW, int BK, int NST, bool SEGFAST, bool F16, bool CONVB, int EPI,
           int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
@@ -220,7 +258,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
   static_assert((NST - 2) * C_HI < 64, "vmcnt range");
   __shared__ __align__(16) unsigned char smem[NST * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index made scalar so everything derived from it (load roles, LDS
+  // offsets, segment selects) stays in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WGM, wn = wave / WGM;
   const bool hi_count = (QT % NW == 0) || (wave < QT % NW);
 
@@ -243,6 +283,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
 
   // direct loads: instruction q writes LDS rows RPI q ..; lane i lands in row
   // RPI q + i / SLOTS at physical slot i % SLOTS (logical slot ^ swizzle)
+  // When NW divides both instruction counts, whether load i is an A or a B
+  // load and whether it exists at all are compile-time facts.
+  constexpr bool STATIC_ROLES = (QA % NW == 0) && (QT % NW == 0);
   const uint16_t* src[QI];
   int chunk[QI];
   bool isb[QI];
@@ -251,8 +294,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
     const int q = wave + NW * i;
     const int row = RPI * q + lane / SLOTS;
     chunk[i] = (lane % SLOTS) ^ gswz<BK>(row);
-    isb[i] = q >= QA;
-    if (q < QA) {
+    isb[i] = STATIC_ROLES ? (NW * i >= QA) : (q >= QA);
+    if (!isb[i]) {
       int m = m0 + row;
       m = m < a.M ? m : a.M - 1;
       src[i] = a.A + (int64_t)m * a.lda;
@@ -292,7 +335,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
       const int q = wave + NW * i;
-      if (q < QT) {
+      if (STATIC_ROLES || q < QT) {
         int64_t off;
         if constexpr (SEGFAST) {
           off = isb[i] ? boff_u : aoff_u;
@@ -354,15 +397,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
     constexpr int NPAIR = NFRAG < NMFMA ? NFRAG : NMFMA;
 #pragma unroll
     for (int i = 0; i < NPAIR; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
     }
     if constexpr (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NMFMA - NPAIR, 0);
     if constexpr (NFRAG > NPAIR) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, NFRAG - NPAIR, 0);
   };
-  // wait until this wave's loads of the tile issued `newer` tiles before the
-  // most recent one have landed (loads complete in issue order)
+  // Waits until this wave's loads of all but the newest `newer` issued tiles
+  // have landed (loads complete in issue order) and its LDS reads are done.
+  // The LDS wait is a separate instruction on every path so the compiler
+  // knows no LDS read is pending after it, whatever branch the vmcnt wait took.
   auto wait_tile = [&](int newer) {
+    wait_vmcnt<63>();
     if constexpr (NST >= 5) {
       if (newer >= 3) {
         if (hi_count) wait_vmcnt<3 * C_HI>(); else wait_vmcnt<3 * C_LO>();
@@ -383,6 +429,39 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
     }
     wait_vmcnt<0>();
   };
+  // Steady-state wait: the newest NST - 2 tiles may stay in flight.
+  auto wait_steady = [&]() {
+    if constexpr (QT % NW == 0) {
+      wait_vmcnt<(NST - 2) * C_HI>();
+    } else {
+      wait_vmcnt<63>();
+      if (hi_count) wait_vmcnt<(NST - 2) * C_HI>(); else wait_vmcnt<(NST - 2) * C_LO>();
+    }
+  };
+  // The rest of a K tile after its first 16-wide step: the remaining steps
+  // (operand reads of step ks + 1 overlapping the MFMAs of step ks), the wait
+  // for the next tile, the barrier, and the last step's MFMAs overlapping the
+  // next tile's first operand reads (which, on the last tile, read a stage
+  // that is never used: kept unconditional so the reads and the MFMAs share a
+  // basic block and the compiler does not wait for the reads).
+  int stage = 0;
+  auto finish_tile = [&](bool steady) {
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      read_frags(stage, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+      schedule_step();
+    }
+    // keep every MFMA of the step above the wait and the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    if (steady) wait_steady(); else wait_vmcnt<0>();
+    lds_barrier();
+    const int nstage = stage + 1 == NST ? 0 : stage + 1;
+    read_frags(nstage, 0, 0);
+    mfmas((KS - 1) & 1);
+    schedule_step();
+    stage = nstage;
+  };
 
   if (kt0 < kt1) {
     int issued = 0;
@@ -396,55 +475,289 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
     lds_barrier();
     read_frags(0, 0, 0);
   }
-  int stage = 0;
-  for (int kt = kt0; kt < kt1; ++kt) {
+  int kt = kt0;
+  // steady state: every iteration issues the tile NST - 1 ahead
+  for (; kt + NST - 1 < kt1; ++kt) {
     int fill = stage + NST - 1;
     fill = fill >= NST ? fill - NST : fill;
-    if (kt + NST - 1 < kt1) issue_loads(kt + NST - 1, fill);
-#pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      read_frags(stage, ks + 1, (ks + 1) & 1);
-      mfmas(ks & 1);
-      schedule_step();
-    }
-    const int last_issued = (kt + NST - 1 < kt1) ? kt + NST - 1 : kt1 - 1;
-    wait_tile(last_issued - (kt + 1));
-    lds_barrier();
-    const int nstage = stage + 1 == NST ? 0 : stage + 1;
-    if (kt + 1 < kt1) read_frags(nstage, 0, 0);
-    mfmas((KS - 1) & 1);
-    stage = nstage;
+    issue_loads(kt + NST - 1, fill);
+    finish_tile(true);
   }
+  // drain: nothing left to issue
+  for (; kt < kt1; ++kt) finish_tile(false);
 
+  store_tile<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lrow, lgrp, split);
+}
+
+// --------------------------------------------------------------------------
+// Register-staged kernel (NW waves, accumulators in AGPRs).  K steps of 64
+// so that each row of a tile is one whole 128-byte line, read by 8 lanes with
+// 16-byte loads.  Global loads run PF K tiles ahead into PF register sets; a
+// landed tile is written into the free one of two LDS stages (the weights
+// converted bf16 -> f16 on the way when CONVB, once per tile rather than once
+// per operand read).  Thread t stages the 16-byte slot t % 8 of rows
+// t / 8 + (NW * 8) i of the tile, so all its loads share one K offset.
+// Offsets are 32-bit byte offsets from a wave-uniform base (the launcher
+// checks the operands fit in 4 GiB).
+// --------------------------------------------------------------------------
+constexpr int SG_DS_WR = 0x200, SG_VMEM_RD = 0x020;
+
+// Schedule of the K step that also stages a tile: MFMA i is followed by one
+// operand read of the next step and by an even share of the tile's LDS
+// writes (and of the loads that refill the freed registers).
+template <int I, int NMFMA, int NFRAG, int CPT, bool LOADS>
+__device__ __forceinline__ void sched_stage_one() {
+  constexpr int PER = (CPT + NMFMA - 1) / NMFMA;
+  constexpr int done = I * PER;
+  constexpr int w = done >= CPT ? 0 : (CPT - done < PER ? CPT - done : PER);
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+  if constexpr (I < NFRAG) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+  if constexpr (w > 0) {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_WR, w, 0);
+    if constexpr (LOADS) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, w, 0);
+  }
+  if constexpr (I == NMFMA - 1 && NFRAG > NMFMA) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, NFRAG - NMFMA, 0);
+}
+template <int NMFMA, int NFRAG, int CPT, bool LOADS, int... I>
+__device__ __forceinline__ void sched_stage_step(std::integer_sequence<int, I...>) {
+  (sched_stage_one<I, NMFMA, NFRAG, CPT, LOADS>(), ...);
+}
+
+template <int J, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>{});
+    static_for<J + 1, N>(f);
+  }
+}
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
+  // LDS rows of 64 K-values padded from 128 to 144 bytes: the 16 rows one
+  // operand read touches then start in 16 different bank groups, and the
+  // K step and stage enter the read address as immediates
+  constexpr int BK = 64, ROWB = 144;
+  constexpr int WGN = NW / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MB = WM / 32, NBL = WN / 32;
+  constexpr int R = BM + NB * BN;       // LDS rows per stage
+  constexpr int STAGE = R * ROWB;
+  constexpr int RS = 8 * NW;            // rows covered by one chunk round
+  constexpr int CPT = R / RS;           // staged 16-byte chunks per thread per tile
+  constexpr int CA = BM / RS;           // ... of which rows of A
+  constexpr int KS = BK / 16;
+  constexpr int NFRAG = MB + NB * NBL, NMFMA = MB * NB * NBL;
+  static_assert(NW % WGM == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(BM % RS == 0 && BN % RS == 0, "chunk rounds must not straddle operands");
+  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+  __shared__ __align__(16) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+
+  const int mtiles = (a.M + BM - 1) / BM;
+  const int ntiles = mtiles * ((a.N + BN - 1) / BN);
+  const int units = ntiles * a.nsplit;
+  int u;
+  {
+    const int bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
+    const int q = units >> 3, rem = units & 7;
+    u = xcd * q + (xcd < rem ? xcd : rem) + idx;
+  }
+  const int tile = u % ntiles, split = u / ntiles;
+  const int mt = tile % mtiles, nt_ = tile / mtiles;
+  const int m0 = mt * BM, n0 = nt_ * BN;
+  const int nk_all = a.K / BK;
+  const int per = (nk_all + a.nsplit - 1) / a.nsplit;
+  const int kt0 = split * per;
+  const int kt1 = (kt0 + per < nk_all) ? kt0 + per : nk_all;
+  const int ntile = kt1 > kt0 ? kt1 - kt0 : 0;
+
+  // staging roles
+  const int crow = tid >> 3, cslot = tid & 7;
+  // byte offset of the chunk's row (+ its slot when the K cursor is uniform;
+  // a per-lane cursor already includes the slot), K offset excluded
+  const int slot_k = SEGFAST ? cslot * 8 : 0;
+  uint32_t goff[CPT];
 #pragma unroll
-  for (int y = 0; y < NBL; ++y)
-#pragma unroll
-    for (int z = 0; z < MB; ++z) {
-      const int m = m0 + wm * WM + z * 32 + lrow;
-      const int nb0 = n0 + wn * WN + y * 32;
-      if constexpr (EPI == EPI_QKV) {
-        epi_qkv_block(a, m, nb0, lgrp, acc[0][y][z]);
-      } else {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int n = nb0 + 8 * q4 + 4 * lgrp;
-          float v[4], v2[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = acc[0][y][z][4 * q4 + e];
-            v2[e] = acc[NB - 1][y][z][4 * q4 + e];
-          }
-          if constexpr (EPI == EPI_PARTIAL) {
-            if (m < a.M && n < a.N) {
-              f32x4 o{v[0], v[1], v[2], v[3]};
-              *reinterpret_cast<f32x4*>(a.partial + ((int64_t)split * a.M + m) * a.N + n) = o;
-            }
-          } else {
-            epilogue4<EPI>(a, m, n, v, v2);
-          }
-        }
+  for (int i = 0; i < CPT; ++i) {
+    const int row = crow + RS * i;
+    if (i < CA) {
+      int m = m0 + row;
+      m = m < a.M ? m : a.M - 1;
+      goff[i] = (uint32_t)(((int64_t)m * a.lda + slot_k) * 2);
+    } else {
+      const int brow = row - BM;
+      const int which = (RS * i - BM) / BN;  // compile-time per i
+      int n = n0 + brow - which * BN;
+      n = n < a.N ? n : a.N - 1;
+      goff[i] = (uint32_t)(((int64_t)n * a.ldb + slot_k) * 2);
+    }
+  }
+  const uint32_t lds_w = crow * ROWB + cslot * 16;
+
+  // K cursor of the next tile to load: uniform when segments are whole
+  // multiples of 64, else per lane (its slot may cross a segment boundary
+  // at a different tile than other slots).  Loads past the last tile reload
+  // the last one (kept in ak/bk), so every iteration has the same shape.
+  int cur_s, cur_kk, nload = 0;
+  {
+    const int k = kt0 * BK + (SEGFAST ? 0 : cslot * 8);
+    cur_s = k / a.seg_len;
+    cur_kk = k - cur_s * a.seg_len;
+  }
+  uint32_t ak = 0, bk = 0;
+  u32x4 stg[2][CPT];
+  // offsets of the next tile to load (advances the K cursor)
+  auto next_offsets = [&]() __attribute__((always_inline)) {
+    if (nload < ntile) {
+      int j = cur_s;
+      if (a.ring_rank >= 0) {
+        j = a.ring_rank - cur_s;
+        j = j < 0 ? j + a.nseg : j;
+      }
+      ak = (uint32_t)(((int64_t)j * a.a_seg_step + cur_kk) * 2);
+      bk = (uint32_t)(((int64_t)j * a.b_seg_step + cur_kk) * 2);
+      cur_kk += BK;
+      if (cur_kk >= a.seg_len) {
+        cur_kk -= a.seg_len;
+        ++cur_s;
       }
     }
+    ++nload;
+  };
+  auto load_chunk = [&](u32x4& dst, int i) __attribute__((always_inline)) {
+    const unsigned char* base;
+    uint32_t off = goff[i];
+    if (i < CA) {
+      base = reinterpret_cast<const unsigned char*>(a.A);
+      off += ak;
+    } else {
+      const int which = (RS * i - BM) / BN;
+      base = reinterpret_cast<const unsigned char*>((NB == 2 && which == 1) ? a.B1 : a.B0);
+      off += bk;
+    }
+    dst = *reinterpret_cast<const u32x4*>(base + off);
+  };
+  auto write_chunk = [&](const u32x4& src, int i, int stage) __attribute__((always_inline)) {
+    u32x4 v = src;
+    if constexpr (CONVB) {
+      if (i >= CA) v = bf16x8_to_f16x8(v);
+    }
+    *reinterpret_cast<u32x4*>(smem + stage * STAGE + lds_w + i * RS * ROWB) = v;
+  };
+  auto load_tile = [&](u32x4 (&dst)[CPT]) __attribute__((always_inline)) {
+    next_offsets();
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) load_chunk(dst[i], i);
+  };
+
+  f32x16 acc[NB][NBL][MB];
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int y = 0; y < NBL; ++y)
+#pragma unroll
+      for (int z = 0; z < MB; ++z)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[x][y][z][e] = 0.0f;
+
+  const int lrow = lane & 31, lgrp = lane >> 5;
+  u32x4 af[2][MB], bf[2][NB][NBL];
+  auto read_frags = [&](int stage, int ks, int buf) __attribute__((always_inline)) {
+    const unsigned char* sa = smem + stage * STAGE;
+    const unsigned char* sb = sa + BM * ROWB;
+    const int pch = (2 * ks + lgrp) << 4;
+#pragma unroll
+    for (int z = 0; z < MB; ++z)
+      af[buf][z] = *reinterpret_cast<const u32x4*>(sa + (wm * WM + z * 32 + lrow) * ROWB + pch);
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int y = 0; y < NBL; ++y)
+        bf[buf][x][y] = *reinterpret_cast<const u32x4*>(sb + (x * BN + wn * WN + y * 32 + lrow) * ROWB + pch);
+  };
+  auto mfmas = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int y = 0; y < NBL; ++y)
+#pragma unroll
+        for (int z = 0; z < MB; ++z) {
+          if constexpr (F16)
+            acc[x][y][z] = mfma_f16(bf[buf][x][y], af[buf][z], acc[x][y][z]);
+          else
+            acc[x][y][z] = mfma_bf16(bf[buf][x][y], af[buf][z], acc[x][y][z]);
+        }
+  };
+  // one MFMA, then one operand read of the next step, and so on
+  auto schedule_step = [&]() __attribute__((always_inline)) {
+    constexpr int NPAIR = NFRAG < NMFMA ? NFRAG : NMFMA;
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+    }
+    if constexpr (NMFMA > NPAIR) __builtin_amdgcn_sched_group_barrier(SG_MFMA, NMFMA - NPAIR, 0);
+    if constexpr (NFRAG > NPAIR) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, NFRAG - NPAIR, 0);
+  };
+  // LDS wait + workgroup barrier (no memory fence: see lds_barrier)
+  auto sync = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<63>();
+    lds_barrier();
+  };
+
+  // One K tile in LDS stage P.  MODE 0: also write register set 1 - P (the
+  // next tile) into the other stage, chunk by chunk over the K steps, and
+  // refill each chunk's registers with the tile two further on; MODE 1:
+  // last tile.
+  constexpr int CH = (CPT + KS - 2) / (KS - 1);  // chunks staged per K step
+  auto iteration = [&](auto P_, auto MODE_) __attribute__((always_inline)) {
+    constexpr int P = decltype(P_)::value, MODE = decltype(MODE_)::value;
+    if constexpr (MODE == 0) next_offsets();
+    static_for<0, KS - 1>([&](auto KS_) __attribute__((always_inline)) {
+      constexpr int ks = decltype(KS_)::value;
+      read_frags(P, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+      if constexpr (MODE == 0) {
+        constexpr int NC = CPT - ks * CH < CH ? CPT - ks * CH : CH;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          write_chunk(stg[1 - P][ks * CH + c], ks * CH + c, 1 - P);
+          load_chunk(stg[1 - P][ks * CH + c], ks * CH + c);
+        }
+        sched_stage_step<NMFMA, NFRAG, NC, true>(std::make_integer_sequence<int, NMFMA>{});
+      } else {
+        schedule_step();
+      }
+    });
+    if constexpr (MODE == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      sync();
+      read_frags(1 - P, 0, 0);
+    }
+    mfmas((KS - 1) & 1);
+    if constexpr (MODE == 0) schedule_step();
+  };
+
+  if (ntile > 0) {
+    load_tile(stg[0]);
+    load_tile(stg[1]);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) write_chunk(stg[0][i], i, 0);
+    load_tile(stg[0]);
+    sync();
+    read_frags(0, 0, 0);
+    int t = 0;
+    for (; t + 1 < ntile; t += 2) {
+      iteration(IC<0>{}, IC<0>{});
+      iteration(IC<1>{}, IC<0>{});
+    }
+    if (t < ntile) iteration(IC<0>{}, IC<1>{});
+  }
+  store_tile<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lrow, lgrp, split);
 }
 
 // Sums the split-K partials in split order and applies the residual epilogue:
@@ -505,8 +818,43 @@ static hipError_t launch_tile(GemmArgs a, int nsplit, hipStream_t st) {
   return launch_tile_seg<BM, BN, NB, WGM, NW, BK, NST, false, F16, CONVB, EPI, OCC>(a, nsplit, st);
 }
 
-static int tiles_of(int M, int N, int bm, int bn) {
-  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+// The staged kernel addresses its operands with 32-bit byte offsets.
+static bool staged_fits(const GemmArgs& a) {
+  const int64_t seg_extra = a.seg_len;
+  const int64_t a_end = ((int64_t)(a.M - 1) * a.lda + (int64_t)(a.nseg - 1) * a.a_seg_step + seg_extra) * 2;
+  const int64_t b_end = ((int64_t)(a.N - 1) * a.ldb + (int64_t)(a.nseg - 1) * a.b_seg_step + seg_extra) * 2;
+  return a_end < ((int64_t)1 << 32) - 64 && b_end < ((int64_t)1 << 32) - 64 && a.K % 64 == 0;
+}
+
+template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI>
+static hipError_t launch_staged_seg(GemmArgs a, int nsplit, hipStream_t st) {
+  const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+  if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BF16X) {
+    if (nsplit > 1 && a.partial != nullptr) {
+      a.nsplit = nsplit;
+      hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI_PARTIAL>),
+                         dim3(mt * nt * nsplit), dim3(64 * NW), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      int64_t blocks = ((int64_t)a.M * a.N / 4 + 255) / 256;
+      if (blocks > 2048) blocks = 2048;
+      hipLaunchKernelGGL((gemm_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  a.nsplit = 1;
+  hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI>), dim3(mt * nt),
+                     dim3(64 * NW), 0, st, a);
+  return hipGetLastError();
+}
+
+// Returns hipErrorNotSupported (nothing launched) when the operands are too
+// large for 32-bit offsets; callers then use the direct-load kernel.
+template <int BM, int BN, int NB, int WGM, int NW, bool F16, bool CONVB, int EPI>
+static hipError_t launch_staged(const GemmArgs& a, int nsplit, hipStream_t st) {
+  if (!staged_fits(a)) return hipErrorNotSupported;
+  if (a.seg_len % 64 == 0) return launch_staged_seg<BM, BN, NB, WGM, NW, true, F16, CONVB, EPI>(a, nsplit, st);
+  return launch_staged_seg<BM, BN, NB, WGM, NW, false, F16, CONVB, EPI>(a, nsplit, st);
 }
 
 // Tuning override (no effect unless set): TSP_GEMM_<NAME>=<config>[:<nsplit>].
@@ -521,48 +869,31 @@ static int env_choice(const char* name, int* nsplit) {
   return cfg;
 }
 
-// Single-weight GEMM configurations (tile M x N, waves, K step, LDS stages):
-//   0: 256x256, 8 waves (2x4), BK 32, 5 stages
-//   1: 256x192, 8 waves (4x2), BK 32, 5 stages
-//   2: 256x128, 8 waves (2x4), BK 64, 3 stages
-//   3: 128x128, 4 waves (2x2), BK 64, 4 stages
+// Single-weight GEMM configurations:
+//   0: staged, 256x192 tile, 8 waves (4x2)   -- Q/K/V projection
+//   1: staged, 256x128 tile, 4 waves (2x2)   -- output and down projections
+//   2: staged, 256x192 tile, 4 waves (2x2)
+//   3: direct-load ring, 256x256 tile, 8 waves, K step 32, 5 stages
+// The staged kernel needs 32-bit operand offsets; beyond that the direct-load
+// ring kernel (64-bit addressing) runs instead.
 template <bool F16, bool CONVB, int EPI>
 static hipError_t launch_cfg(const GemmArgs& a, int cfg, int nsplit, hipStream_t st) {
+  hipError_t e = hipErrorNotSupported;
   switch (cfg) {
-    case 0: return launch_tile<256, 256, 1, 2, 8, 32, 5, F16, CONVB, EPI, 1>(a, nsplit, st);
-    case 1: return launch_tile<256, 192, 1, 4, 8, 32, 5, F16, CONVB, EPI, 1>(a, nsplit, st);
-    case 2: return launch_tile<256, 128, 1, 2, 8, 64, 3, F16, CONVB, EPI, 1>(a, nsplit, st);
-    default: return launch_tile<128, 128, 1, 2, 4, 64, 4, F16, CONVB, EPI, 1>(a, nsplit, st);
+    case 0: e = launch_staged<256, 192, 1, 4, 8, F16, CONVB, EPI>(a, nsplit, st); break;
+    case 1: e = launch_staged<256, 128, 1, 2, 4, F16, CONVB, EPI>(a, nsplit, st); break;
+    case 2: e = launch_staged<256, 192, 1, 2, 4, F16, CONVB, EPI>(a, nsplit, st); break;
+    default: break;
   }
-}
-
-static const int kCfgBM[4] = {256, 256, 256, 128};
-static const int kCfgBN[4] = {256, 192, 128, 128};
-
-// Choice for the M x h projections (output and down): big tiles when they
-// fill the chip; otherwise split K so that tiles x splits ~ 256 work units.
-// Long K (the down projection) keeps 256x256 tiles and splits more; short K
-// (the output projection) uses 256x128 tiles and splits less.
-static void choose_resid(const GemmArgs& a, int max_split, int* cfg, int* nsplit) {
-  *nsplit = 1;
-  if (tiles_of(a.M, a.N, 256, 256) >= 192 || max_split <= 1) {
-    *cfg = tiles_of(a.M, a.N, 256, 256) >= 192 ? 0 : 3;
-    return;
-  }
-  *cfg = a.K >= 8192 ? 0 : 2;
-  const int t = tiles_of(a.M, a.N, kCfgBM[*cfg], kCfgBN[*cfg]);
-  int p = (256 + t - 1) / t;
-  *nsplit = p > max_split ? max_split : p;
+  if (e != hipErrorNotSupported) return e;
+  return launch_tile<256, 256, 1, 2, 8, 32, 5, F16, CONVB, EPI, 1>(a, nsplit, st);
 }
 
 template <bool F16, bool CONVB, int EPI>
 static hipError_t launch_single(const GemmArgs& a, const char* name, int max_split, hipStream_t st) {
-  int nsplit = 1, cfg;
-  if (EPI == EPI_QKV) {
-    cfg = a.N % 192 == 0 ? 1 : 0;
-  } else {
-    choose_resid(a, max_split, &cfg, &nsplit);
-  }
+  // Q/K/V: 256x192 tiles; output/down (M x h): 256x128 tiles, split along K
+  // as planned by gemm_split_plan so that tiles x splits covers the CUs
+  int cfg = EPI == EPI_QKV ? 0 : 1, nsplit = EPI == EPI_QKV ? 1 : max_split;
   int env_split = nsplit;
   const int env_cfg = env_choice(name, &env_split);
   if (env_cfg >= 0) {
@@ -636,10 +967,14 @@ hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_
   a.seg_len = s.h;
   a.out16 = act;
   // Dual-weight (gate and up) configurations:
-  //   0: 128x128 (x2), 4 waves, BK 64, 3 stages;  1: 256x128 (x2), 8 waves, BK 32, 4 stages
+  //   0: staged, 128x192 (x2) tile, 8 waves (4x2);  1: staged, 128x192 (x2), 4 waves (2x2)
+  //   2: direct-load ring, 128x128 (x2), 4 waves, K step 64, 3 stages
   int cfg = env_choice("GATEUP", nullptr);
   if (cfg < 0) cfg = 0;
-  if (cfg == 1) return launch_tile<256, 128, 2, 2, 8, 32, 4, true, true, EPI_SWIGLU, 1>(a, 1, st);
+  hipError_t e = hipErrorNotSupported;
+  if (cfg == 0) e = launch_staged<128, 192, 2, 4, 8, true, true, EPI_SWIGLU>(a, 1, st);
+  if (cfg == 1) e = launch_staged<128, 192, 2, 2, 4, true, true, EPI_SWIGLU>(a, 1, st);
+  if (e != hipErrorNotSupported) return e;
   return launch_tile<128, 128, 2, 2, 4, 64, 3, true, true, EPI_SWIGLU, 1>(a, 1, st);
 }
 

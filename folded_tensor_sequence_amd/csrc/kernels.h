@@ -22,11 +22,12 @@ hipError_t launch_qkv_gemm(const Shape& s, int src_rank, const uint16_t* x, cons
 constexpr int kMaxSplit = 4;
 
 // Split-K factor planned for the output and down projections (both produce
-// an M x h result): 1 when 256x256 tiles already cover the 256 CUs, else up to
-// kMaxSplit.  The workspace holds split * M * h floats when it is > 1.
+// an M x h result with 256x128 tiles): 1 when the tiles already cover the 256
+// CUs (224 or more), else up to kMaxSplit so that tiles x splits ~ 256.  The
+// workspace holds split * M * h floats when it is > 1.
 inline int gemm_split_plan(const Shape& s) {
-  const int tiles = ((s.M + 255) / 256) * ((s.h + 255) / 256);
-  if (tiles >= 128) return 1;
+  const int tiles = ((s.M + 255) / 256) * ((s.h + 127) / 128);
+  if (tiles >= 224) return 1;
   int p = (256 + tiles - 1) / tiles;
   return p > kMaxSplit ? kMaxSplit : p;
 }
