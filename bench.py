@@ -2,9 +2,11 @@
 """Benchmark of one rank's TSP transformer-layer forward on one MI355X.
 
 A step is one ``tsp_layer_fwd`` call on a fixed synthetic batch: the rank's
-Q/K/V projection for all D weight shards, the zigzag K/V reorder, causal flash
-attention, the output projection with residual, and the gated-MLP weight ring
-(gate/up + SwiGLU, down + residual).  The other ranks' K/V slots of the
+Q/K/V projection for all D weight shards, causal flash attention over the
+all-gathered K/V (read in zigzag order through the position -> slot map), the
+output projection with residual, and the gated-MLP weight ring (gate/up +
+SwiGLU, down + residual).  The standalone zigzag K/V reorder kernel
+(``tsp_kv_reorder``) is timed separately and reported as ``reorder_standalone``.  The other ranks' K/V slots of the
 all-gather buffer are filled once before timing (they are communication, not
 this rank's compute).  Inputs are resident in device memory when the timed
 region starts.
@@ -29,7 +31,7 @@ METRIC = "TFLOP/s and tokens/s per one-rank TSP layer fwd; % of bf16 MFMA peak"
 # (bf16 = f16 rate), HBM3E 8 TB/s.
 PEAK_MFMA_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 PEAK_HBM_GBS = 8000.0
-KERNELS = ("qkv", "reorder", "attn", "oproj", "gateup", "down")
+KERNELS = ("qkv", "attn", "oproj", "gateup", "down")
 
 
 def kernel_work(d):
@@ -192,6 +194,23 @@ def main():
                      "algorithmic_per_launch": amount},
         "kernels_ms": {k: round(v, 5) for k, v in kms.items()},
     }
+    # standalone zigzag K/V reorder (not part of the layer step): HBM-bound copy
+    nat = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_KV_NATURAL) // 2, dtype=torch.int16, device="cuda")
+    for _ in range(3):
+        B.tsp_kv_reorder(d, prob.kv_gathered, nat)
+    B.tsp_profile_kernel("reorder", args.steps)
+    for _ in range(args.steps):
+        B.tsp_kv_reorder(d, prob.kv_gathered, nat)
+    n_re, re_ms = B.tsp_profile_result()
+    B.tsp_profile_kernel(None)
+    torch.cuda.synchronize()
+    re_s = re_ms / max(n_re, 1) * 1e-3
+    re_bytes = work["reorder"][0]
+    out["reorder_standalone"] = {"avg_launch_ms": round(re_s * 1e3, 5), "launches": n_re,
+                                 "bytes_per_launch": re_bytes, "achieved": round(re_bytes / re_s / 1e9, 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(re_bytes / re_s / 1e9 / PEAK_HBM_GBS, 4)}
+    del nat
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         del prob

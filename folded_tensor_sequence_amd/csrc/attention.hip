@@ -25,12 +25,17 @@
 //                  cross-half exchange.
 //   K rows are stored in LDS in a permuted order so that, for every 16-key
 //   step of the P V product, a lane's 8 probabilities are 8 consecutive keys;
-//   V is stored transposed (head-dim major) so those 8 keys are one 16-byte
-//   LDS read.
+//   V is stored key-major, as it arrives, and read with the transposing LDS
+//   load (ds_read_b64_tr_b16: 16 lanes that each point at 4 head-dim values
+//   of one key row receive, per lane, 4 consecutive keys of one head-dim
+//   column), two of which give a lane its 8 keys.
 //   O^T += V^T P  (32x32x16 MFMA, probabilities rounded to f16).
 // K and V tiles are copied global -> LDS with 16-byte direct loads into an
-// NST-deep ring; the barrier between tiles carries no memory fence, so the
-// loads of later tiles stay in flight across it.
+// NST-deep ring, straight from the all-gathered K/V slots: the zigzag map
+// (position p -> chunk p / c -> source rank and local row) is applied to the
+// row addresses, so no reordered copy of K/V is made.  The barrier between
+// tiles carries no memory fence, so the loads of later tiles stay in flight
+// across it.
 #include <math.h>
 
 #include "common.h"
@@ -40,8 +45,7 @@ namespace tsp {
 
 struct AttnArgs {
   const uint16_t* q;     // f16 [B][Hq][T][dh]
-  const uint16_t* knat;  // f16 [Hkv][B][kmax_pad][dh]
-  const uint16_t* vnat;  // f16 [Hkv][B][dh][kmax_pad]
+  const uint16_t* kv;    // f16 all-gathered K/V [D shard][D src][K|V][B][T][Hkv/D * dh]
   uint16_t* o;           // f16 [B][T][Hq*dh]
   float* part_o;         // [pieces][B*Hq][128][dh] unnormalised outputs of split blocks
   float* part_ml;        // [pieces][B*Hq][2][128] (scaled max, sum)
@@ -73,7 +77,27 @@ template <int DH>
 __device__ __forceinline__ int kswz(int row) {
   return DH == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+// Key-major V rows are DH*2 bytes = DH/32 64-byte chunks.  A transposing PV
+// read touches one 64-byte chunk of 4 consecutive key rows per 32 lanes; the
+// chunk index is XORed with the row so those 4 rows sit in 4 different
+// 64-byte bank windows.
+template <int DH>
+__device__ __forceinline__ int vswz(int row) {
+  return DH == 128 ? (row & 3) : ((row >> 1) & 1);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Row of the all-gathered K/V buffer holding global position p (zigzag map:
+// chunk q = p / c lives on rank q (q < D) or 2D-1-q, at local row
+// p mod c (+ c for the later chunk)).
+__device__ __forceinline__ int64_t gathered_row(const Shape& s, int j, int sel, int b, int p) {
+  const int qc = p / s.c;
+  const int g = qc < s.D ? qc : 2 * s.D - 1 - qc;
+  const int t = (qc < s.D ? 0 : s.c) + (p - qc * s.c);
+  return ((((int64_t)j * s.D + g) * 2 + sel) * s.B + b) * s.T + t;
+}
 
 // Block geometry shared by the attention and merge kernels.  Block index
 // bi in [0, 2 nrb): the later chunk's blocks first, last rows first.
@@ -99,16 +123,18 @@ __device__ __forceinline__ BlockGeo block_geo(const Shape& s, int nrb, int kt_ma
   return g;
 }
 
-template <int DH, int NST>
+// CH64: chunks are whole multiples of 64 keys, so a key tile never straddles
+// two chunks and its gathered rows are consecutive (one address per tile).
+template <int DH, int NST, bool CH64>
 __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnArgs a) {
   constexpr int BN = 64;
   constexpr int KROW = DH * 2;
   constexpr int K_BYTES = BN * KROW;
-  constexpr int V_BYTES = DH * BN * 2;
+  constexpr int V_BYTES = BN * KROW;
   constexpr int STAGE = K_BYTES + V_BYTES;
-  constexpr int KRPI = 1024 / KROW;          // K rows per direct-load instruction
+  constexpr int KRPI = 1024 / KROW;          // K (and V) rows per direct-load instruction
   constexpr int K_INS = BN / KRPI;           // instructions per K tile
-  constexpr int V_INS = DH / 8;              // 8 transposed-V rows of 128 bytes each
+  constexpr int V_INS = BN / KRPI;           // ... per V tile
   constexpr int QT = K_INS + V_INS;
   static_assert(QT % 4 == 0, "loads split evenly over 4 waves");
   constexpr int QW = QT / 4;                 // per wave
@@ -119,6 +145,17 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   const Shape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lgrp = lane >> 5;
+  // transposing V reads: lane (group gq = lane / 16, s = lane % 16) points at
+  // key row 8 (gq / 2) + s / 4 (+ the step's key base) and head-dim columns
+  // db * 32 + 16 (gq % 2) + 4 (s % 4) .. + 3
+  int vlane[NDB];
+  {
+    const int gq = lane >> 4, sl = lane & 15;
+    const int vrow = 8 * (gq >> 1) + (sl >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      vlane[db] = vrow * KROW + ((db ^ vswz<DH>(vrow)) << 6) + 32 * (gq & 1) + 8 * (sl & 3);
+  }
 
   // ---- work unit -> (block, piece, sequence, q-head) --------------------
   const int per_bh = s.B * s.Hq;
@@ -149,8 +186,10 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   const int wave_minpos = g.gstart + (wt0 - g.row_begin);
 
   const int G = qh / (s.Hq / s.Hkv);
-  const uint16_t* kbase = a.knat + ((int64_t)G * s.B + b) * s.kmax_pad * DH;
-  const uint16_t* vbase = a.vnat + ((int64_t)G * s.B + b) * DH * (int64_t)s.kmax_pad;
+  const int jsh = G / s.Hkv_s, hk = G - jsh * s.Hkv_s;
+  const int kvd = s.Hkv_s * DH;
+  const int64_t head_off = (int64_t)hk * DH;
+  const int64_t v_step = (int64_t)s.B * s.T * kvd;  // K slot -> V slot of the same rows
 
   // ---- Q fragments (second operand of S^T = K Q^T) ---------------------
   u32x4 qf[NKS];
@@ -161,28 +200,43 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   }
 
   // ---- direct-load assignment: wave instruction q = wave + 4 i ------------
-  const uint16_t* lsrc[QW];
+  // K rows go to LDS in permuted order with XOR-swizzled 16-byte slots; V
+  // rows in natural order with XOR-swizzled 64-byte chunks.
+  int lkey[QW], lcol[QW];
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
     const int q = wave + 4 * i;
+    const int slot = lane % (KROW / 16);
     if (q < K_INS) {
       const int row = KRPI * q + lane / (KROW / 16);
-      const int slot = lane % (KROW / 16);
-      const int key = (row & ~31) | key_perm(row & 31);
-      lsrc[i] = kbase + (int64_t)key * DH + ((slot ^ kswz<DH>(row)) * 8);
+      lkey[i] = (row & ~31) | key_perm(row & 31);
+      lcol[i] = (slot ^ kswz<DH>(row)) * 8;
     } else {
-      const int d = 8 * (q - K_INS) + lane / 8;
-      lsrc[i] = vbase + (int64_t)d * s.kmax_pad + ((lane % 8) ^ vswz(d)) * 8;
+      const int row = KRPI * (q - K_INS) + lane / (KROW / 16);
+      lkey[i] = row;
+      lcol[i] = (4 * ((slot >> 2) ^ vswz<DH>(row)) + (slot & 3)) * 8;
     }
   }
   auto issue = [&](int kt, int stage) {
     unsigned char* sb = smem + stage * STAGE;
+    const int key0 = kt * BN;
+    if constexpr (CH64) {
+      const int64_t kb0 = gathered_row(s, jsh, 0, b, key0) * kvd + head_off;
 #pragma unroll
-    for (int i = 0; i < QW; ++i) {
-      const int q = wave + 4 * i;
-      // K rows step by DH elements per key, V rows by one element per key
-      const int64_t off = q < K_INS ? (int64_t)kt * BN * DH : (int64_t)kt * BN;
-      attn_load_lds16(lsrc[i] + off, sb + q * 1024);
+      for (int i = 0; i < QW; ++i) {
+        const int q = wave + 4 * i;
+        const int64_t off = kb0 + (q < K_INS ? 0 : v_step) + (int64_t)lkey[i] * kvd + lcol[i];
+        attn_load_lds16(a.kv + off, sb + q * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        const int q = wave + 4 * i;
+        int p = key0 + lkey[i];
+        p = p < s.S ? p : s.S - 1;  // keys past the sequence end are masked
+        const int64_t off = gathered_row(s, jsh, q < K_INS ? 0 : 1, b, p) * kvd + head_off + lcol[i];
+        attn_load_lds16(a.kv + off, sb + q * 1024);
+      }
     }
   };
   auto wait_tile = [&](int newer) {  // loads of later tiles may stay in flight
@@ -288,13 +342,16 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
       m_run = m_new;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int row = db * 32 + lrow;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const int ch = 4 * kb + 2 * st + lgrp;
-            const u32x4 vf = *reinterpret_cast<const u32x4*>(sv + row * 128 + ((ch ^ vswz(row)) << 4));
+            // keys 32 kb + 16 st + 8 (lane / 32) + 4 r + (0..3), head-dim column db * 32 + lane % 32
+            const unsigned char* vp = sv + vlane[db] + (32 * kb + 16 * st) * KROW;
+            const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp);
+            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KROW));
+            const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
+            const u32x4 vf{h0[0], h0[1], h1[0], h1[1]};
             oacc[db] = mfma_f16(vf, pf[kb][st], oacc[db]);
           }
       }
@@ -436,13 +493,12 @@ size_t attn_partial_bytes(const Shape& s) {
   return (size_t)p.pieces * s.B * s.Hq * 128 * (s.dh + 2) * sizeof(float);
 }
 
-hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* knat,
-                             const uint16_t* vnat, uint16_t* o, float* partial, hipStream_t st) {
+hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, uint16_t* o,
+                             float* partial, hipStream_t st) {
   const AttnPlan p = attn_plan(s);
   AttnArgs a;
   a.q = q;
-  a.knat = knat;
-  a.vnat = vnat;
+  a.kv = kv_gathered;
   a.o = o;
   a.part_o = partial;
   a.part_ml = partial + (size_t)p.pieces * s.B * s.Hq * 128 * s.dh;
@@ -451,10 +507,18 @@ hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* 
   a.nrb = p.nrb;
   a.kt_max = p.kt_max;
   dim3 grid((unsigned)p.units);
-  if (s.dh == 128)
-    hipLaunchKernelGGL((flash_attn_kernel<128, 2>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((flash_attn_kernel<64, 2>), grid, dim3(256), 0, st, a);
+  const bool ch64 = s.c % 64 == 0;
+  if (s.dh == 128) {
+    if (ch64)
+      hipLaunchKernelGGL((flash_attn_kernel<128, 2, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((flash_attn_kernel<128, 2, false>), grid, dim3(256), 0, st, a);
+  } else {
+    if (ch64)
+      hipLaunchKernelGGL((flash_attn_kernel<64, 2, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((flash_attn_kernel<64, 2, false>), grid, dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.pieces == 0) return e;
   const int64_t items = (int64_t)p.split_rows * s.B * s.Hq * (s.dh / 4);

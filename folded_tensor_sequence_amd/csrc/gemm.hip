@@ -871,9 +871,11 @@ static int env_choice(const char* name, int* nsplit) {
 
 // Single-weight GEMM configurations:
 //   0: staged, 256x192 tile, 8 waves (4x2)   -- Q/K/V projection
-//   1: staged, 256x128 tile, 4 waves (2x2)   -- output and down projections
+//   1: staged, 256x128 tile, 4 waves (2x2)
 //   2: staged, 256x192 tile, 4 waves (2x2)
 //   3: direct-load ring, 256x256 tile, 8 waves, K step 32, 5 stages
+//   4: staged, 128x128 tile, 4 waves (2x2);  5: staged, 128x128 tile, 8 waves (2x4)
+//   6: staged, 256x128 tile, 8 waves (4x2)   -- output and down projections
 // The staged kernel needs 32-bit operand offsets; beyond that the direct-load
 // ring kernel (64-bit addressing) runs instead.
 template <bool F16, bool CONVB, int EPI>
@@ -883,6 +885,9 @@ static hipError_t launch_cfg(const GemmArgs& a, int cfg, int nsplit, hipStream_t
     case 0: e = launch_staged<256, 192, 1, 4, 8, F16, CONVB, EPI>(a, nsplit, st); break;
     case 1: e = launch_staged<256, 128, 1, 2, 4, F16, CONVB, EPI>(a, nsplit, st); break;
     case 2: e = launch_staged<256, 192, 1, 2, 4, F16, CONVB, EPI>(a, nsplit, st); break;
+    case 4: e = launch_staged<128, 128, 1, 2, 4, F16, CONVB, EPI>(a, nsplit, st); break;
+    case 5: e = launch_staged<128, 128, 1, 2, 8, F16, CONVB, EPI>(a, nsplit, st); break;
+    case 6: e = launch_staged<256, 128, 1, 4, 8, F16, CONVB, EPI>(a, nsplit, st); break;
     default: break;
   }
   if (e != hipErrorNotSupported) return e;
@@ -893,7 +898,7 @@ template <bool F16, bool CONVB, int EPI>
 static hipError_t launch_single(const GemmArgs& a, const char* name, int max_split, hipStream_t st) {
   // Q/K/V: 256x192 tiles; output/down (M x h): 256x128 tiles, split along K
   // as planned by gemm_split_plan so that tiles x splits covers the CUs
-  int cfg = EPI == EPI_QKV ? 0 : 1, nsplit = EPI == EPI_QKV ? 1 : max_split;
+  int cfg = EPI == EPI_QKV ? 0 : 6, nsplit = EPI == EPI_QKV ? 1 : max_split;
   int env_split = nsplit;
   const int env_cfg = env_choice(name, &env_split);
   if (env_cfg >= 0) {

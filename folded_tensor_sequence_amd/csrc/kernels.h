@@ -49,10 +49,11 @@ hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t*
 // f32 -> f16 rounding copy (MLP input when it arrives as float32).
 hipError_t launch_f32_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t st);
 
-// Causal flash attention over the natural-order K/V.  Blocks of 128 query rows
-// whose key range is long are cut into pieces along the keys (plan below);
-// `partial` holds the pieces' state (attn_partial_bytes) and may be nullptr
-// only when the plan has no pieces.
+// Causal flash attention of the rank's queries over the all-gathered K/V
+// (read in zigzag order through the position -> slot map, no reordered copy).
+// Blocks of 128 query rows whose key range is long are cut into pieces along
+// the keys (plan below); `partial` holds the pieces' state
+// (attn_partial_bytes) and may be nullptr only when the plan has no pieces.
 struct AttnPlan {
   int nrb;          // 128-row blocks per zigzag chunk
   int kt_max;       // key tiles (64 keys) per piece at most
@@ -62,7 +63,7 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(const Shape& s);
 size_t attn_partial_bytes(const Shape& s);
-hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* knat,
-                             const uint16_t* vnat, uint16_t* o, float* partial, hipStream_t st);
+hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, uint16_t* o,
+                             float* partial, hipStream_t st);
 
 }  // namespace tsp

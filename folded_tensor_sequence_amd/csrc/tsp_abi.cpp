@@ -120,7 +120,7 @@ size_t bytes_partial(const tsp::Shape& s) {
 }
 
 struct AttnWs {
-  uint16_t *q, *knat, *vnat, *o;
+  uint16_t *q, *o;
   float* partial;
 };
 struct MlpWs {
@@ -129,24 +129,20 @@ struct MlpWs {
 };
 
 // Workspace layouts (256-byte aligned pieces):
-//   attention  [q | K,V natural | o | split-K partials]
+//   attention  [q | o | split-K partials]
 //   MLP        [h16 | act | split-K partials]
-//   layer      [q | K,V natural | o | h32 | h16 | act | split-K partials]
-size_t ws_attn(const tsp::Shape& s) {
-  return up(bytes_q(s)) + up(bytes_kvnat(s)) + up(bytes_o(s)) + up(bytes_partial(s));
-}
+//   layer      [q | o | h32 | h16 | act | split-K partials]
+// (attention reads K/V straight from the all-gathered buffer)
+size_t ws_attn(const tsp::Shape& s) { return up(bytes_q(s)) + up(bytes_o(s)) + up(bytes_partial(s)); }
 size_t ws_mlp(const tsp::Shape& s) { return up(bytes_h16(s)) + up(bytes_act(s)) + up(bytes_partial(s)); }
 size_t ws_layer(const tsp::Shape& s) {
-  return up(bytes_q(s)) + up(bytes_kvnat(s)) + up(bytes_o(s)) + up(bytes_h32(s)) + up(bytes_h16(s)) +
-         up(bytes_act(s)) + up(bytes_partial(s));
+  return up(bytes_q(s)) + up(bytes_o(s)) + up(bytes_h32(s)) + up(bytes_h16(s)) + up(bytes_act(s)) +
+         up(bytes_partial(s));
 }
 
 char* carve_attn(const tsp::Shape& s, char* p, AttnWs* w) {
   w->q = reinterpret_cast<uint16_t*>(p);
   p += up(bytes_q(s));
-  w->knat = reinterpret_cast<uint16_t*>(p);
-  w->vnat = reinterpret_cast<uint16_t*>(p + bytes_knat(s));
-  p += up(bytes_kvnat(s));
   w->o = reinterpret_cast<uint16_t*>(p);
   p += up(bytes_o(s));
   return p;
@@ -223,8 +219,7 @@ int run_attention(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* 
                   const AttnWs& w, hipStream_t st) {
   TSP_KLAUNCH(TSP_K_QKV, st, tsp::launch_qkv_gemm(s, s.r, x_local, w_qkv, w.q, kv_gathered, st),
               "qkv projection");
-  TSP_KLAUNCH(TSP_K_REORDER, st, tsp::launch_kv_reorder(s, kv_gathered, w.knat, w.vnat, st), "kv reorder");
-  TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, w.knat, w.vnat, w.o, w.partial, st),
+  TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, st),
               "flash attention");
   TSP_KLAUNCH(TSP_K_OPROJ, st, tsp::launch_oproj_gemm(s, w.o, w_o, x_local, out, out16, w.partial, st),
               "output projection");

@@ -132,7 +132,9 @@ int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered,
 /* Attention half of the layer on rank dims->rank:
  *     out = x + sum_j O_j W_O,j^T,
  * O_j = causal attention of the rank's zigzag queries (q-heads of shard j)
- * over the natural-order K/V of shard j (TSP article, "How to Fold a Book";
+ * over the K/V of shard j in natural sequence order (TSP article, "How to
+ * Fold a Book"; the attention kernel applies the zigzag position -> slot map
+ * while it loads K/V tiles from kv_gathered, so no reordered copy is made;
  * the head split with row-split output projection is exact:
  * bowenzhou.top "张量并行", section "机制：行切与列切").
  *   x_local      bf16 [B][T][h]

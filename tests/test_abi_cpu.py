@@ -164,7 +164,8 @@ def test_workspace_sizes_match_layout(lib, name):
     assert ws(B.TSP_FN_KV_GATHERED) == \
         d.degree * d.degree * 2 * d.batch * T * (d.n_kv_heads // d.degree) * d.head_dim * 2
     attn, mlp, layer = ws(B.TSP_FN_ATTN), ws(B.TSP_FN_MLP), ws(B.TSP_FN_LAYER)
-    fixed_attn = up(q) + up(kvn) + up(q)
+    # attention reads K/V from the gathered buffer: its workspace is q and o
+    fixed_attn = up(q) + up(q)
     fixed_mlp = up(M * d.hidden * 2) + up(M * d.ffn * 2)
     assert attn >= fixed_attn and mlp >= fixed_mlp
     scratch = attn - fixed_attn
