@@ -86,6 +86,17 @@ __device__ __forceinline__ int vswz(int row) {
   return DH == 128 ? (row & 3) : ((row >> 1) & 1);
 }
 
+// max / sum over a lane and its partner lane ^ 32: v_permlane32_swap on two
+// copies of x leaves {x_l, x_(l^32)} in the two results of every lane
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -311,8 +322,10 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair_max(mx);
       const float m_new = fmaxf(m_run, mx * sc);
+      // a row with no unmasked key yet keeps m = -inf; its probabilities are 0
+      const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
       float rs = 0.0f;
       u32x4 pf[2][2];
 #pragma unroll
@@ -321,8 +334,8 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_new));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_new));
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_sub));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_sub));
             const uint32_t pk = pack_f16x2(p0, p1);
             pf[kb][st][w] = pk;
             // the row sum is taken over the f16 probabilities that P V uses
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
           }
       // rescale only when some row's maximum moved (alpha == 1 otherwise)
       if (__any(m_new != m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int x = 0; x < NDB; ++x)
@@ -363,7 +376,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   }
 
   // ---- store: final f16 output, or the piece's partial state ------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (!wave_active || !lane_valid) return;
   if (g.ns == 1) {
     const float inv = 1.0f / l_tot;
