@@ -34,10 +34,28 @@ PEAK_HBM_GBS = 8000.0
 KERNELS = ("qkv", "attn", "oproj", "gateup", "down")
 
 
+def layer_flops(d):
+    """Algorithmic FLOPs of one rank's layer forward, per part.
+
+    GEMMs count 2*M*N*K.  Attention counts 4*dh per (query, key) pair per
+    query head over the causal pairs of the rank's rows: a rank holding
+    zigzag chunks r and 2D-1-r (c tokens each) sees, per sequence,
+    sum over its rows of (position + 1) = c^2 (2D-1) + c (c+1) pairs, the
+    same count on every rank (the load balance the zigzag split exists for).
+    """
+    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
+    m = d.batch * T
+    pairs = d.batch * (c * c * (2 * d.degree - 1) + c * (c + 1))
+    qkv = 2.0 * m * (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim * d.hidden
+    o = 2.0 * m * d.n_q_heads * d.head_dim * d.hidden
+    attn = 4.0 * d.head_dim * d.n_q_heads * pairs
+    mlp = 2.0 * m * 3 * d.ffn * d.hidden
+    return {"qkv": qkv, "o": o, "attn": attn, "mlp": mlp, "total": qkv + o + attn + mlp}
+
+
 def kernel_work(d):
     """Algorithmic work per launch of each kernel: (amount, unit, bound)."""
-    from oracle import tsp_oracle as orc  # work accounting only
-    f = orc.algorithmic_flops(d)
+    f = layer_flops(d)
     c = d.seq // (2 * d.degree)
     kmax = (2 * d.degree - d.rank) * c
     reorder_bytes = 2 * 2 * d.n_kv_heads * d.batch * kmax * d.head_dim * 2  # K,V x (read + write)
@@ -49,6 +67,32 @@ def kernel_work(d):
         "gateup": (f["mlp"] * 2 / 3, "flop", "mfma"),
         "down": (f["mlp"] / 3, "flop", "mfma"),
     }, f["total"]
+
+
+def source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` as last measured with the FETCH_SIZE
+    and WRITE_SIZE counters (scaled by the copy calibration), from the record
+    under profiles/; None when there is no record for this workload and kernel
+    or the kernel's sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel") != kernel or rec.get("workload") != workload:
+        return None
+    if source_digest(rec["sources"]) != rec["sources_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def cpu_baseline(wl, inp, target_s: float, max_rows: int):
@@ -107,6 +151,10 @@ def main():
     ap.add_argument("--workload", default="llama7b_s8k_d8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the benchmark, run a plain elementwise copy of 1 GiB (float32 "
+                         "negation: 1 GiB read, 1 GiB written) three times, as the known-size "
+                         "reference for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one rank of a TSP axis on one GPU; runs on more than one GPU "
@@ -211,6 +259,14 @@ def main():
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(re_bytes / re_s / 1e9 / PEAK_HBM_GBS, 4)}
     del nat
+    out["roofline"]["traffic"] = recorded_traffic(wl.name, dominant)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         del prob

@@ -1,0 +1,39 @@
+"""Host-side checks of the benchmark's work accounting (no GPU)."""
+import pytest
+
+import bench
+import synth
+from oracle import tsp_oracle as orc
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_closed_form_flops_match_the_oracle_count(name):
+    # bench.py counts causal pairs with a closed form; the oracle sums over the
+    # rank's actual zigzag positions
+    d = synth.WORKLOADS[name].dims
+    mine, ref = bench.layer_flops(d), orc.algorithmic_flops(d)
+    for k in ref:
+        assert mine[k] == ref[k], k
+
+
+def test_pair_count_is_rank_independent():
+    import dataclasses
+    base = synth.WORKLOADS["llama7b_s8k_d8"].dims
+    counts = {bench.layer_flops(dataclasses.replace(base, rank=r))["attn"] for r in range(base.degree)}
+    refs = {orc.algorithmic_flops(dataclasses.replace(base, rank=r))["attn"] for r in range(base.degree)}
+    assert len(counts) == 1 and counts == refs
+
+
+def test_recorded_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
+    import json
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1")
+    (tmp_path / "profiles").mkdir()
+    rec = {"kernel": "gateup", "workload": "w", "sources": ["k.hip"], "traffic_bytes_per_launch": 123}
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    rec["sources_sha256"] = bench.source_digest(["k.hip"])
+    (tmp_path / "profiles" / "traffic_gateup_w.json").write_text(json.dumps(rec))
+    assert bench.recorded_traffic("w", "gateup") == 123
+    assert bench.recorded_traffic("w", "qkv") is None          # no record for that kernel
+    src.write_text("kernel v2")
+    assert bench.recorded_traffic("w", "gateup") is None       # counters predate the change
