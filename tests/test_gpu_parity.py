@@ -219,7 +219,7 @@ def test_layer_fwd_full_size_sampled(name):
     torch.cuda.empty_cache()
     for b in range(d.batch):
         ref = orc.rank_rows_forward(inp, d, b, rows)
-        # the max-abs bar is met except where noted in the design notes (70B-like
-        # layer, first tokens); rel-Frobenius always
-        max_abs = 4e-2 if name == "wide70b_s32k_d8" else 2e-2
+        # the max-abs bar is met except on the 70B-like layer, whose f16 storage
+        # floor alone is 2.50e-2 (tests/test_rounding_floor.py); rel-Frobenius always
+        max_abs = 3e-2 if name == "wide70b_s32k_d8" else 2e-2
         assert_close(yg[b, rows], ref["y"], max_abs=max_abs, what=f"y b={b} rows={rows.tolist()}")

@@ -1,0 +1,71 @@
+"""The f16 storage-rounding model (``oracle/rounding_model.py``): pinned to the
+oracle and to IEEE binary16, then used to show where each workload's error
+floor lies against the tolerance (max-abs 2e-2, rel-Frobenius 5e-3).  CPU only."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import rounding_model as rm
+from oracle import tsp_oracle as orc
+from gpu_util import sample_rows
+
+
+def test_f16_rounding_known_values():
+    # binary16 has a 10-bit fraction: spacing 2^-10 in [1, 2), ties to even
+    ulp = 2.0 ** -10
+    vals = np.array([1 + ulp / 2, 1 + 3 * ulp / 2, 1 + ulp / 2 + 2 ** -30, 65504.0, 2.0 ** -24, 2.0 ** -26, -3.0])
+    want = np.array([1.0, 1 + 2 * ulp, 1 + ulp, 65504.0, 2.0 ** -24, 0.0, -3.0])
+    assert np.array_equal(rm.f16(vals), want)
+
+
+def test_without_rounding_points_it_is_the_oracle():
+    wl = synth.WORKLOADS["tiny_d2"]
+    d = wl.dims
+    inp = synth.make_inputs(d, wl.sigma, wl.seed)
+    rows = np.arange(d.seq // d.degree)
+    ref = orc.rank_rows_forward(inp, d, 0, rows)["y"]
+    got = rm.rank_rows_rounded(inp, d, 0, rows, points=())
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        rm.rank_rows_rounded(inp, d, 0, rows, points=("bf16",))
+
+
+def test_each_rounding_point_changes_the_result():
+    # every point is wired in: enabling it alone moves y, by an amount of the
+    # order of f16 spacing times the activations
+    wl = synth.WORKLOADS["tiny_d2"]
+    d = wl.dims
+    inp = synth.make_inputs(d, wl.sigma, wl.seed)
+    rows = np.arange(d.seq // d.degree)
+    ref = rm.rank_rows_rounded(inp, d, 0, rows, points=())
+    scale = np.abs(ref).max()
+    for p in rm.POINTS:
+        err = np.abs(rm.rank_rows_rounded(inp, d, 0, rows, points=(p,)) - ref).max()
+        assert 0 < err < 64 * 2.0 ** -11 * scale, p
+
+
+def _floor(name):
+    wl = synth.WORKLOADS[name]
+    d = wl.dims
+    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
+    inp = synth.make_inputs(d, wl.sigma, wl.seed)
+    rows = sample_rows(T, c)
+    g = orc.local_to_global(d.seq, d.degree, d.rank)[rows]
+    kv = orc.project_kv(inp, d, 0, int(g.max()) + 1)
+    w = {n: orc.bf16_bits_to_f64(inp[n]) for n in ("w_q", "w_o", "w_g", "w_u", "w_d")}
+    ref = orc.rank_rows_forward(inp, d, 0, rows, kv=kv, weights=w)["y"]
+    y = rm.rank_rows_rounded(inp, d, 0, rows, kv=kv, weights=w)
+    return np.abs(y - ref).max(), np.linalg.norm(y - ref) / np.linalg.norm(ref)
+
+
+def test_llama7b_floor_is_inside_the_tolerance():
+    max_abs, rel = _floor("llama7b_s8k_d8")
+    assert max_abs < 2e-2 and rel < 5e-3
+
+
+def test_wide70b_floor_exceeds_the_max_abs_bar():
+    # the 70B-like layer (hidden 8192, |y| ~ 50 at the first tokens) cannot
+    # meet max-abs 2e-2 with f16 storage at all; rel-Frobenius stays ~10x inside
+    max_abs, rel = _floor("wide70b_s32k_d8")
+    assert 2e-2 < max_abs < 3e-2
+    assert rel < 1e-3
