@@ -180,11 +180,11 @@ def main():
         prob.layer()
     torch.cuda.synchronize()
 
-    # per-kernel durations (one profiled call each, untimed) -> dominant kernel
+    # per-kernel durations (ten profiled calls each, untimed) -> dominant kernel
     kms = {}
     for k in KERNELS:
-        B.tsp_profile_kernel(k, 4)
-        for _ in range(3):
+        B.tsp_profile_kernel(k, 10)
+        for _ in range(10):
             prob.layer()
         n, ms = B.tsp_profile_result()
         kms[k] = ms / max(n, 1)

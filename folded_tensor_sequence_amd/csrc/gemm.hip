@@ -550,7 +550,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
   constexpr int KS = BK / 16;
   constexpr int NFRAG = MB + NB * NBL, NMFMA = MB * NB * NBL;
   static_assert(NW % WGM == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
-  static_assert(BM % RS == 0 && BN % RS == 0, "chunk rounds must not straddle operands");
+  static_assert(BM % RS == 0, "chunk rounds must not straddle A and B");
+  static_assert(NB == 2 || BN % RS == 0, "a single weight fills whole chunk rounds");
   static_assert(2 * STAGE <= 160 * 1024, "LDS");
   __shared__ __align__(16) unsigned char smem[2 * STAGE];
 
@@ -589,8 +590,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
       m = m < a.M ? m : a.M - 1;
       goff[i] = (uint32_t)(((int64_t)m * a.lda + slot_k) * 2);
     } else {
+      // B rows [0, BN) are W_0's, [BN, 2 BN) W_1's; a round of RS rows may
+      // straddle the two when BN is not a multiple of RS
       const int brow = row - BM;
-      const int which = (RS * i - BM) / BN;  // compile-time per i
+      const int which = brow >= BN ? 1 : 0;
       int n = n0 + brow - which * BN;
       n = n < a.N ? n : a.N - 1;
       goff[i] = (uint32_t)(((int64_t)n * a.ldb + slot_k) * 2);
@@ -635,7 +638,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
       base = reinterpret_cast<const unsigned char*>(a.A);
       off += ak;
     } else {
-      const int which = (RS * i - BM) / BN;
+      const int first = (RS * i - BM) / BN, last = (RS * i + RS - 1 - BM) / BN;  // compile-time
+      int which = first;
+      if (first != last) which = (crow + RS * i - BM) >= BN ? 1 : 0;            // straddling round
       base = reinterpret_cast<const unsigned char*>((NB == 2 && which == 1) ? a.B1 : a.B0);
       off += bk;
     }
@@ -974,11 +979,13 @@ hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_
   // Dual-weight (gate and up) configurations:
   //   0: staged, 128x192 (x2) tile, 8 waves (4x2);  1: staged, 128x192 (x2), 4 waves (2x2)
   //   2: direct-load ring, 128x128 (x2), 4 waves, K step 64, 3 stages
+  //   3: staged, 256x96 (x2) tile, 8 waves (8x1)
   int cfg = env_choice("GATEUP", nullptr);
-  if (cfg < 0) cfg = 0;
+  if (cfg < 0) cfg = 3;
   hipError_t e = hipErrorNotSupported;
   if (cfg == 0) e = launch_staged<128, 192, 2, 4, 8, true, true, EPI_SWIGLU>(a, 1, st);
   if (cfg == 1) e = launch_staged<128, 192, 2, 2, 4, true, true, EPI_SWIGLU>(a, 1, st);
+  if (cfg == 3) e = launch_staged<256, 96, 2, 8, 8, true, true, EPI_SWIGLU>(a, 1, st);
   if (e != hipErrorNotSupported) return e;
   return launch_tile<128, 128, 2, 2, 4, 64, 3, true, true, EPI_SWIGLU, 1>(a, 1, st);
 }
