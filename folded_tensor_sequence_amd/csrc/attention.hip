@@ -323,7 +323,13 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
       mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * sc);
+      // The reference maximum m_run moves only when the row maximum passes it
+      // by more than 8 (log2 units).  Exponents then stay <= 8 (probabilities
+      // < 256: fine for f16 P and the float32 sums), numerator and denominator
+      // share the reference so the result is the same, and most tiles skip
+      // the rescale of O.
+      const float m_max = fmaxf(m_run, mx * sc);
+      const float m_new = m_max > m_run + 8.0f ? m_max : m_run;
       // a row with no unmasked key yet keeps m = -inf; its probabilities are 0
       const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
       float rs = 0.0f;
