@@ -38,6 +38,8 @@
 // across it.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   __shared__ __align__(16) unsigned char smem[NST * STAGE];
 
   const Shape& s = a.s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, lgrp = lane >> 5;
   // transposing V reads: lane (group gq = lane / 16, s = lane % 16) points at
   // key row 8 (gq / 2) + s / 4 (+ the step's key base) and head-dim columns
@@ -228,17 +230,38 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
       lcol[i] = (4 * ((slot >> 2) ^ vswz<DH>(row)) + (slot & 3)) * 8;
     }
   }
+  // CH64: byte offset of each lane's 16 bytes from the tile's first K row
+  // (V rows sit v_step elements further), the same for every tile; the
+  // host checks that they fit in 31 bits.  The tile cursor (chunk kq, key
+  // kr within it) advances by one tile per issue, as issue() is called for
+  // consecutive tiles.
+  uint32_t loff[QW];
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+    const int q = wave + 4 * i;
+    loff[i] = (uint32_t)(((q < K_INS ? 0 : v_step) + (int64_t)lkey[i] * kvd + lcol[i]) * 2);
+  }
+  int kq = (kt_begin * BN) / s.c, kr = kt_begin * BN - kq * s.c;
   auto issue = [&](int kt, int stage) {
     unsigned char* sb = smem + stage * STAGE;
     const int key0 = kt * BN;
     if constexpr (CH64) {
-      const int64_t kb0 = gathered_row(s, jsh, 0, b, key0) * kvd + head_off;
+      const int g_src = kq < s.D ? kq : 2 * s.D - 1 - kq;
+      const int t = (kq < s.D ? 0 : s.c) + kr;
+      const int64_t row0 = ((((int64_t)jsh * s.D + g_src) * 2) * s.B + b) * s.T + t;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.kv + row0 * kvd + head_off), (short)0, 0x7fffffff, 0x00020000);
+      kr += BN;
+      if (kr >= s.c) {
+        kr -= s.c;
+        ++kq;
+      }
 #pragma unroll
       for (int i = 0; i < QW; ++i) {
         const int q = wave + 4 * i;
-        const int64_t off = kb0 + (q < K_INS ? 0 : v_step) + (int64_t)lkey[i] * kvd + lcol[i];
-        attn_load_lds16(a.kv + off, sb + q * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sb + q * 1024), 16, (int)loff[i], 0, 0, 0);
       }
+      (void)key0;
     } else {
 #pragma unroll
       for (int i = 0; i < QW; ++i) {
@@ -284,10 +307,11 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
     wait_tile(issued - 1);
     barrier();
   }
-  int stage = 0;
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    int fill = stage + NST - 1;
-    fill = fill >= NST ? fill - NST : fill;
+  // one key tile; the LDS stage is a compile-time constant so that every LDS
+  // address is a per-lane base plus an immediate
+  auto step = [&](int kt, auto ST_) __attribute__((always_inline)) {
+    constexpr int stage = decltype(ST_)::value;
+    constexpr int fill = (stage + NST - 1) % NST;
     if (kt + NST - 1 < kt_end) issue(kt + NST - 1, fill);
     const int key0 = kt * BN;
     if (wave_active && key0 <= wave_maxpos) {
@@ -378,8 +402,14 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
     const int last_issued = (kt + NST - 1 < kt_end) ? kt + NST - 1 : kt_end - 1;
     wait_tile(last_issued - (kt + 1));
     barrier();
-    stage = stage + 1 == NST ? 0 : stage + 1;
+  };
+  static_assert(NST == 2, "the tile loop below alternates two stages");
+  int kt = kt_begin;
+  for (; kt + 1 < kt_end; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
   }
+  if (kt < kt_end) step(kt, std::integral_constant<int, 0>{});
 
   // ---- store: final f16 output, or the piece's partial state ------------
   const float l_tot = pair_sum(l_run);
@@ -526,7 +556,9 @@ hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* 
   a.nrb = p.nrb;
   a.kt_max = p.kt_max;
   dim3 grid((unsigned)p.units);
-  const bool ch64 = s.c % 64 == 0;
+  // the whole-tile path addresses a tile's K and V rows with 31-bit offsets
+  const int64_t kvd = (int64_t)s.Hkv_s * s.dh;
+  const bool ch64 = s.c % 64 == 0 && ((int64_t)s.B * s.T * kvd + 64 * kvd) * 2 < ((int64_t)1 << 31);
   if (s.dh == 128) {
     if (ch64)
       hipLaunchKernelGGL((flash_attn_kernel<128, 2, true>), grid, dim3(256), 0, st, a);
