@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tsp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -23,6 +25,17 @@ struct Shape {
   int32_t B, S, D, r, h, Hq, Hkv, dh, F;
   int32_t T, c, M, Hq_s, Hkv_s, F_s, kmax, kmax_pad, nqkv_s;
 };
+
+// Compile-time loop: f(integral_constant<int, J>) for J = J0 .. N-1.
+template <int J, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>{});
+    static_for<J + 1, N>(f);
+  }
+}
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 // 32x32x16 matrix-core products (float32 accumulate).  Operand i-index is
 // the lane's low 5 bits, the 8 k-values live in the lane's 16 bytes; the

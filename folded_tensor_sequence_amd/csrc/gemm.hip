@@ -523,16 +523,6 @@ __device__ __forceinline__ void sched_stage_step(std::integer_sequence<int, I...
   (sched_stage_one<I, NMFMA, NFRAG, CPT, LOADS>(), ...);
 }
 
-template <int J, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (J < N) {
-    f(std::integral_constant<int, J>{});
-    static_for<J + 1, N>(f);
-  }
-}
-template <int V>
-using IC = std::integral_constant<int, V>;
-
 template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
   // LDS rows of 64 K-values padded from 128 to 144 bytes: the 16 rows one
