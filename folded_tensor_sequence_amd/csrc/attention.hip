@@ -37,6 +37,7 @@
 // tiles carries no memory fence, so the loads of later tiles stay in flight
 // across it.
 #include <math.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -514,11 +515,17 @@ AttnPlan attn_plan(const Shape& s) {
   int64_t tiles = 0;
   for (int bi = 0; bi < 2 * p.nrb; ++bi) tiles += host_nkt(s, p.nrb, bi);
   tiles *= (int64_t)s.B * s.Hq;
-  // split only when there are too few blocks to fill 256 CUs twice over
+  // split only when there are too few blocks to fill 256 CUs twice over;
+  // pieces then hold about tiles / 512 key tiles (tuning override, no effect
+  // unless set: TSP_ATTN_PIECES=<target number of work units>)
+  int64_t target = 512;
+  if (const char* ev = getenv("TSP_ATTN_PIECES")) {
+    if (atoi(ev) > 0) target = atoi(ev);
+  }
   if (blocks >= 1024) {
     p.kt_max = 1 << 30;
   } else {
-    int64_t kt = (tiles + 511) / 512;
+    int64_t kt = (tiles + target - 1) / target;
     p.kt_max = (int)(kt < 16 ? 16 : kt);
   }
   p.units = 0;
