@@ -763,19 +763,21 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
 // float32 when EPI_RESID_F32), plus the f16 copy when out16 != nullptr.
 template <int EPI>
 __global__ void gemm_reduce_kernel(GemmArgs a) {
-  const int64_t n4 = (int64_t)a.M * a.N / 4;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const int64_t off = i * 4;
+  // block (x, y): four consecutive columns of rows y, y + gridDim.y, ... per
+  // thread (no division)
+  const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (n >= a.N) return;
+  const int64_t plane = (int64_t)a.M * a.N;
+  for (int m = blockIdx.y; m < a.M; m += gridDim.y) {
+    const int64_t off = (int64_t)m * a.N + n;
     f32x4 acc = *reinterpret_cast<const f32x4*>(a.partial + off);
     for (int p = 1; p < a.nsplit; ++p) {
-      const f32x4 t = *reinterpret_cast<const f32x4*>(a.partial + (int64_t)p * a.M * a.N + off);
+      const f32x4 t = *reinterpret_cast<const f32x4*>(a.partial + p * plane + off);
       acc[0] += t[0];
       acc[1] += t[1];
       acc[2] += t[2];
       acc[3] += t[3];
     }
-    const int m = (int)(off / a.N), n = (int)(off - (int64_t)m * a.N);
     float v[4] = {acc[0], acc[1], acc[2], acc[3]};
     epilogue4<EPI>(a, m, n, v, v);
   }
@@ -795,9 +797,9 @@ static hipError_t launch_tile_seg(GemmArgs a, int nsplit, hipStream_t st) {
                          dim3(mt * nt * nsplit), dim3(64 * NW), 0, st, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      int64_t blocks = ((int64_t)a.M * a.N / 4 + 255) / 256;
-      if (blocks > 2048) blocks = 2048;
-      hipLaunchKernelGGL((gemm_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((gemm_reduce_kernel<EPI>),
+                         dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535)), dim3(256),
+                         0, st, a);
       return hipGetLastError();
     }
   }
@@ -834,9 +836,9 @@ static hipError_t launch_staged_seg(GemmArgs a, int nsplit, hipStream_t st) {
                          dim3(mt * nt * nsplit), dim3(64 * NW), 0, st, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      int64_t blocks = ((int64_t)a.M * a.N / 4 + 255) / 256;
-      if (blocks > 2048) blocks = 2048;
-      hipLaunchKernelGGL((gemm_reduce_kernel<EPI>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((gemm_reduce_kernel<EPI>),
+                         dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535)), dim3(256),
+                         0, st, a);
       return hipGetLastError();
     }
   }
