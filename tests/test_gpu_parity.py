@@ -196,6 +196,32 @@ def test_layer_fwd(name):
     assert torch.equal(y, y2)
 
 
+# The alternative GEMM kernels: the direct-load ring kernel (the fallback when
+# operands need 64-bit offsets; its configuration is chosen here through the
+# library's tuning variables) and the staged kernel with two register sets.
+ALT_GEMMS = {
+    "ring": {"TSP_GEMM_QKV": "3", "TSP_GEMM_OPROJ": "3:2", "TSP_GEMM_DOWN": "3:2", "TSP_GEMM_GATEUP": "2"},
+    "staged_two_sets": {"TSP_GEMM_OPROJ": "7:2", "TSP_GEMM_DOWN": "7:2", "TSP_GEMM_GATEUP": "4"},
+    "staged_4wave": {"TSP_GEMM_QKV": "2", "TSP_GEMM_OPROJ": "1:2", "TSP_GEMM_DOWN": "1:2", "TSP_GEMM_GATEUP": "1"},
+}
+
+
+@pytest.mark.parametrize("name", ["mha_d2_r1", "ffn_tail_d4_r3", "gqa2_b2_dh128_c80"])
+@pytest.mark.parametrize("alt", list(ALT_GEMMS))
+def test_layer_fwd_alternative_gemms(name, alt, monkeypatch):
+    for k, v in ALT_GEMMS[alt].items():
+        monkeypatch.setenv(k, v)
+    shape, sigma, seed = _shape(name)
+    d = dims_of(shape)
+    _case(f"layer_fwd {name} gemms={alt}")
+    inp = inputs_for(shape, sigma, seed)
+    prob = RankProblem.build(d, inp)
+    y = prob.layer().clone()
+    torch.cuda.synchronize()
+    ref = orc.layer_rank_rows(inp, d)
+    assert_close(y.cpu().numpy(), ref["y"], what="y")
+
+
 # --------------------------------------------------------------------------- #
 # Full-size workloads in the benchmark's launch configuration: the whole
 # layer runs on the GPU, sampled rows are checked against the oracle.
