@@ -249,8 +249,11 @@ int tsp_profile_kernel(int32_t kernel_id, int32_t max_launches) {
     return fail(TSP_ERR_INVALID_ARG, "max_launches %d not in [1, 100000]", max_launches);
   TSP_TRY(check_device("tsp_profile_kernel"));
   g_prof.ev.resize(2 * (size_t)max_launches, nullptr);
+  // timing-only events: no system-scope release/acquire (an L2 write-back
+  // per record), which would stall the stream between the bracketed kernel
+  // and its neighbours
   for (hipEvent_t& e : g_prof.ev) {
-    hipError_t err = hipEventCreate(&e);
+    hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     if (err != hipSuccess) {
       prof_release();
       return hip_fail(err, "tsp_profile_kernel");

@@ -192,8 +192,10 @@ typedef enum {
 /* Live timing of one kernel: after tsp_profile_kernel(id, n) the next n
  * launches of kernel `id` made by this thread (through any entry point) are
  * bracketed by a pair of HIP events recorded on the launch stream.  The
- * events are created here, once, not inside the timed calls.  id = TSP_K_NONE
- * stops and releases them.  Not for use while a HIP graph is being captured. */
+ * events are created here, once, not inside the timed calls, as timing-only
+ * events (no system-scope fence, so recording them does not write back the
+ * caches between the kernels).  id = TSP_K_NONE stops and releases them.
+ * Not for use while a HIP graph is being captured. */
 int tsp_profile_kernel(int32_t kernel_id, int32_t max_launches);
 
 /* Waits for the recorded events of the current profile and returns the number
