@@ -523,22 +523,30 @@ __device__ __forceinline__ void sched_stage_step(std::integer_sequence<int, I...
   (sched_stage_one<I, NMFMA, NFRAG, CPT, LOADS>(), ...);
 }
 
-template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG>
+template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG,
+          bool SPLIT>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
   // LDS rows of 64 K-values padded from 128 to 144 bytes: the 16 rows one
   // operand read touches then start in 16 different bank groups, and the
   // K step and stage enter the read address as immediates
   constexpr int BK = 64, ROWB = 144;
+  // SPLIT (two weights): the wave columns take one weight each over the
+  // whole BN columns (wave column 0 W_0, column 1 W_1) instead of both
+  // weights over BN / WGN columns, so a wave reads half the weight rows per
+  // MFMA; the epilogue pairs the two results through LDS.
   constexpr int WGN = NW / WGM;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
+  static_assert(!SPLIT || (NB == 2 && WGN == 2), "split needs two weights and two wave columns");
+  constexpr int NBW = SPLIT ? 1 : NB;   // weights per wave
+  constexpr int WM = BM / WGM, WN = SPLIT ? BN : BN / WGN;
   constexpr int MB = WM / 32, NBL = WN / 32;
+  static_assert(!SPLIT || MB % 2 == 0, "split pairs halves of the wave rows");
   constexpr int R = BM + NB * BN;       // LDS rows per stage
   constexpr int STAGE = R * ROWB;
   constexpr int RS = 8 * NW;            // rows covered by one chunk round
   constexpr int CPT = R / RS;           // staged 16-byte chunks per thread per tile
   constexpr int CA = BM / RS;           // ... of which rows of A
   constexpr int KS = BK / 16;
-  constexpr int NFRAG = MB + NB * NBL, NMFMA = MB * NB * NBL;
+  constexpr int NFRAG = MB + NBW * NBL, NMFMA = MB * NBW * NBL;
   static_assert(NW % WGM == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(BM % RS == 0, "chunk rounds must not straddle A and B");
   static_assert(NB == 2 || BN % RS == 0, "a single weight fills whole chunk rounds");
@@ -652,9 +660,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
     for (int i = 0; i < CPT; ++i) load_chunk(dst[i], i);
   };
 
-  f32x16 acc[NB][NBL][MB];
+  f32x16 acc[NBW][NBL][MB];
 #pragma unroll
-  for (int x = 0; x < NB; ++x)
+  for (int x = 0; x < NBW; ++x)
 #pragma unroll
     for (int y = 0; y < NBL; ++y)
 #pragma unroll
@@ -663,7 +671,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
         for (int e = 0; e < 16; ++e) acc[x][y][z][e] = 0.0f;
 
   const int lrow = lane & 31, lgrp = lane >> 5;
-  u32x4 af[2][MB], bf[2][NB][NBL];
+  u32x4 af[2][MB], bf[2][NBW][NBL];
   auto read_frags = [&](int stage, int ks, int buf) __attribute__((always_inline)) {
     const unsigned char* sa = smem + stage * STAGE;
     const unsigned char* sb = sa + BM * ROWB;
@@ -672,14 +680,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
     for (int z = 0; z < MB; ++z)
       af[buf][z] = *reinterpret_cast<const u32x4*>(sa + (wm * WM + z * 32 + lrow) * ROWB + pch);
 #pragma unroll
-    for (int x = 0; x < NB; ++x)
+    for (int x = 0; x < NBW; ++x)
 #pragma unroll
-      for (int y = 0; y < NBL; ++y)
-        bf[buf][x][y] = *reinterpret_cast<const u32x4*>(sb + (x * BN + wn * WN + y * 32 + lrow) * ROWB + pch);
+      for (int y = 0; y < NBL; ++y) {
+        const int brow = SPLIT ? wn * BN + y * 32 : x * BN + wn * WN + y * 32;
+        bf[buf][x][y] = *reinterpret_cast<const u32x4*>(sb + (brow + lrow) * ROWB + pch);
+      }
   };
   auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < NB; ++x)
+    for (int x = 0; x < NBW; ++x)
 #pragma unroll
       for (int y = 0; y < NBL; ++y)
 #pragma unroll
@@ -755,7 +765,52 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
     }
     if (t < ntile) iteration(IC<0>{}, IC<1>{});
   }
-  store_tile<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lrow, lgrp, split);
+  if constexpr (SPLIT) {
+    // Waves (wm, 0) and (wm, 1) hold W_0 and W_1 results for the same WM x BN
+    // block, in the same lane layout.  Wave column 0 finishes the first half
+    // of the row blocks, column 1 the second: each writes the half it does
+    // not finish to LDS (register-major, lane-minor: conflict-free), and
+    // reads its partner's matching half.
+    constexpr int HB = MB / 2;                        // row blocks per half
+    constexpr int XF = NBL * HB * 16;                 // floats exchanged per lane
+    static_assert(NW * 64 * XF * 4 <= 2 * STAGE, "exchange fits in the stages");
+    float* xch = reinterpret_cast<float*>(smem);
+    wait_vmcnt<63>();                                 // (waits for this wave's LDS operations)
+    lds_barrier();                                    // every wave's last operand reads are done
+    // (register indices stay compile-time: the wave column only selects)
+    const bool col0 = wn == 0;
+    {
+      float* mine = xch + (wave * XF) * 64 + lane;
+#pragma unroll
+      for (int y = 0; y < NBL; ++y)
+#pragma unroll
+        for (int z = 0; z < HB; ++z)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)  // the half the partner finishes
+            mine[((y * HB + z) * 16 + e) * 64] = col0 ? acc[0][y][z + HB][e] : acc[0][y][z][e];
+    }
+    wait_vmcnt<63>();
+    lds_barrier();
+    f32x16 pair[2][NBL][HB];                          // [W_0, W_1][col block][row block of the half]
+    {
+      const int partner = wm + WGM * (1 - wn);
+      const float* theirs = xch + (partner * XF) * 64 + lane;
+#pragma unroll
+      for (int y = 0; y < NBL; ++y)
+#pragma unroll
+        for (int z = 0; z < HB; ++z)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float t = theirs[((y * HB + z) * 16 + e) * 64];
+            const float own = col0 ? acc[0][y][z][e] : acc[0][y][z + HB][e];  // the half this wave finishes
+            pair[0][y][z][e] = col0 ? own : t;
+            pair[1][y][z][e] = col0 ? t : own;
+          }
+    }
+    store_tile<HB, NBL, 2, EPI>(a, pair, m0 + wm * WM + (wn == 0 ? 0 : HB * 32), n0, lrow, lgrp, split);
+  } else {
+    store_tile<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lrow, lgrp, split);
+  }
 }
 
 // Sums the split-K partials in split order and applies the residual epilogue:
@@ -826,13 +881,13 @@ static bool staged_fits(const GemmArgs& a) {
   return a_end < ((int64_t)1 << 32) - 64 && b_end < ((int64_t)1 << 32) - 64 && a.K % 64 == 0;
 }
 
-template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG>
+template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG, bool SPLIT>
 static hipError_t launch_staged_seg(GemmArgs a, int nsplit, hipStream_t st) {
   const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
   if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BF16X) {
     if (nsplit > 1 && a.partial != nullptr) {
       a.nsplit = nsplit;
-      hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI_PARTIAL, NSTG>),
+      hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI_PARTIAL, NSTG, SPLIT>),
                          dim3(mt * nt * nsplit), dim3(64 * NW), 0, st, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -843,19 +898,19 @@ static hipError_t launch_staged_seg(GemmArgs a, int nsplit, hipStream_t st) {
     }
   }
   a.nsplit = 1;
-  hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI, NSTG>), dim3(mt * nt),
+  hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI, NSTG, SPLIT>), dim3(mt * nt),
                      dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
 // Returns hipErrorNotSupported (nothing launched) when the operands are too
 // large for 32-bit offsets; callers then use the direct-load kernel.
-template <int BM, int BN, int NB, int WGM, int NW, bool F16, bool CONVB, int EPI, int NSTG = 1>
+template <int BM, int BN, int NB, int WGM, int NW, bool F16, bool CONVB, int EPI, int NSTG = 1, bool SPLIT = false>
 static hipError_t launch_staged(const GemmArgs& a, int nsplit, hipStream_t st) {
   if (!staged_fits(a)) return hipErrorNotSupported;
   if (a.seg_len % 64 == 0)
-    return launch_staged_seg<BM, BN, NB, WGM, NW, true, F16, CONVB, EPI, NSTG>(a, nsplit, st);
-  return launch_staged_seg<BM, BN, NB, WGM, NW, false, F16, CONVB, EPI, NSTG>(a, nsplit, st);
+    return launch_staged_seg<BM, BN, NB, WGM, NW, true, F16, CONVB, EPI, NSTG, SPLIT>(a, nsplit, st);
+  return launch_staged_seg<BM, BN, NB, WGM, NW, false, F16, CONVB, EPI, NSTG, SPLIT>(a, nsplit, st);
 }
 
 // Tuning override (no effect unless set): TSP_GEMM_<NAME>=<config>[:<nsplit>].
@@ -980,13 +1035,15 @@ hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_
   //   0: staged, 128x192 (x2) tile, 8 waves (4x2);  1: staged, 128x192 (x2), 4 waves (2x2)
   //   2: direct-load ring, 128x128 (x2), 4 waves, K step 64, 3 stages
   //   3: staged, 256x96 (x2) tile, 8 waves (8x1);  4: as 3 with two register sets
+  //   5: staged, 256x96 (x2) tile, 8 waves (4x2) with one weight per wave column
   int cfg = env_choice("GATEUP", nullptr);
-  if (cfg < 0) cfg = 3;
+  if (cfg < 0) cfg = 5;
   hipError_t e = hipErrorNotSupported;
   if (cfg == 0) e = launch_staged<128, 192, 2, 4, 8, true, true, EPI_SWIGLU>(a, 1, st);
   if (cfg == 1) e = launch_staged<128, 192, 2, 2, 4, true, true, EPI_SWIGLU>(a, 1, st);
   if (cfg == 3) e = launch_staged<256, 96, 2, 8, 8, true, true, EPI_SWIGLU>(a, 1, st);
   if (cfg == 4) e = launch_staged<256, 96, 2, 8, 8, true, true, EPI_SWIGLU, 2>(a, 1, st);
+  if (cfg == 5) e = launch_staged<256, 96, 2, 4, 8, true, true, EPI_SWIGLU, 1, true>(a, 1, st);
   if (e != hipErrorNotSupported) return e;
   return launch_tile<128, 128, 2, 2, 4, 64, 3, true, true, EPI_SWIGLU, 1>(a, 1, st);
 }
