@@ -56,6 +56,7 @@ struct AttnArgs {
   float scale_log2;      // log2(e) / sqrt(dh)
   int32_t nrb;           // 128-row blocks per chunk
   int32_t kt_max;        // key tiles per piece at most
+  int32_t pair;          // 1: each earlier-chunk block rides with a later-chunk block
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -113,17 +114,19 @@ __device__ __forceinline__ int64_t gathered_row(const Shape& s, int j, int sel, 
   return ((((int64_t)j * s.D + g) * 2 + sel) * s.B + b) * s.T + t;
 }
 
-// Block geometry shared by the attention and merge kernels.  Block index
-// bi in [0, 2 nrb): the later chunk's blocks first, last rows first.
+// Block geometry shared by the attention and merge kernels and the host
+// plan.  Block index bi in [0, 2 nrb): the later chunk's blocks first, last
+// rows first.
 struct BlockGeo {
   int row_begin, row_end;  // local rows of the chunk
   int gstart;              // global position of the chunk's first row
   int t0;                  // first local row of the block
   int nkt;                 // key tiles the block needs
-  int ns;                  // pieces
+  int ns;                  // pieces (0: the block runs inside its partner's last piece)
+  int tper;                // key tiles per piece (the last piece may hold fewer)
 };
 
-__device__ __forceinline__ BlockGeo block_geo(const Shape& s, int nrb, int kt_max, int bi) {
+__host__ __device__ inline BlockGeo block_rows(const Shape& s, int nrb, int bi) {
   BlockGeo g;
   const int late = bi < nrb ? 1 : 0;
   const int rb = nrb - 1 - (late ? bi : bi - nrb);
@@ -133,7 +136,34 @@ __device__ __forceinline__ BlockGeo block_geo(const Shape& s, int nrb, int kt_ma
   g.t0 = g.row_begin + rb * 128;
   const int last = g.t0 + 127 < g.row_end ? g.t0 + 127 : g.row_end - 1;
   g.nkt = (g.gstart + (last - g.row_begin) + 64) / 64;
-  g.ns = (g.nkt + kt_max - 1) / kt_max;
+  g.ns = 1;
+  g.tper = g.nkt;
+  return g;
+}
+
+// Pieces along the keys.  Unpaired: every block is cut into pieces of at
+// most kt_max tiles.  Paired: the later-chunk block bi (heavy: its keys reach
+// back over both chunks) and the earlier-chunk block 2 nrb - 1 - bi (light)
+// share their work units: the heavy block's key range is cut so that its
+// last piece plus the whole light block weigh about as much as each other
+// piece, and the unit of that last piece then runs the light block too.
+__host__ __device__ inline BlockGeo block_geo(const Shape& s, int nrb, int kt_max, int pair, int bi) {
+  BlockGeo g = block_rows(s, nrb, bi);
+  if (!pair) {
+    g.ns = (g.nkt + kt_max - 1) / kt_max;
+    g.tper = (g.nkt + g.ns - 1) / g.ns;
+  } else if (bi >= nrb) {
+    g.ns = 0;
+  } else {
+    const int tot = g.nkt + block_rows(s, nrb, 2 * nrb - 1 - bi).nkt;
+    int ns = (tot + kt_max - 1) / kt_max, tper = (tot + ns - 1) / ns;
+    while (ns > 1 && (ns - 1) * tper >= g.nkt) {  // the last piece keeps at least one heavy tile
+      --ns;
+      tper = (tot + ns - 1) / ns;
+    }
+    g.ns = ns;
+    g.tper = tper;
+  }
   return g;
 }
 
@@ -174,44 +204,27 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   // ---- work unit -> (block, piece, sequence, q-head) --------------------
   const int per_bh = s.B * s.Hq;
   int u = blockIdx.x, bi = 0, piece_base = 0;
-  BlockGeo g = block_geo(s, a.nrb, a.kt_max, 0);
+  BlockGeo g = block_geo(s, a.nrb, a.kt_max, a.pair, 0);
   for (;;) {
     const int n = g.ns * per_bh;
     if (u < n || bi + 1 >= 2 * a.nrb) break;
     u -= n;
     if (g.ns > 1) piece_base += g.ns;
     ++bi;
-    g = block_geo(s, a.nrb, a.kt_max, bi);
+    g = block_geo(s, a.nrb, a.kt_max, a.pair, bi);
   }
   const int piece = u / per_bh, bh = u - piece * per_bh;
   const int b = bh / s.Hq, qh = bh - b * s.Hq;
-  const int tper = (g.nkt + g.ns - 1) / g.ns;
-  const int kt_begin = piece * tper;
-  const int kt_end = kt_begin + tper < g.nkt ? kt_begin + tper : g.nkt;
-
-  const int wt0 = g.t0 + wave * 32;
-  const bool wave_active = wt0 < g.row_end;
-  int t_lane = wt0 + lrow;
-  const bool lane_valid = t_lane < g.row_end;
-  t_lane = lane_valid ? t_lane : g.row_end - 1;
-  const int qpos = g.gstart + (t_lane - g.row_begin);
-  const int w_last = (wt0 + 31 < g.row_end ? wt0 + 31 : g.row_end - 1);
-  const int wave_maxpos = g.gstart + (w_last - g.row_begin);
-  const int wave_minpos = g.gstart + (wt0 - g.row_begin);
+  // paired plan: the last piece of a later-chunk block also runs its
+  // earlier-chunk partner block (whole, final output)
+  const int heavy_bi = bi;
+  const int nparts = a.pair && piece == g.ns - 1 ? 2 : 1;
 
   const int G = qh / (s.Hq / s.Hkv);
   const int jsh = G / s.Hkv_s, hk = G - jsh * s.Hkv_s;
   const int kvd = s.Hkv_s * DH;
   const int64_t head_off = (int64_t)hk * DH;
   const int64_t v_step = (int64_t)s.B * s.T * kvd;  // K slot -> V slot of the same rows
-
-  // ---- Q fragments (second operand of S^T = K Q^T) ---------------------
-  u32x4 qf[NKS];
-  {
-    const uint16_t* qrow = a.q + (((int64_t)b * s.Hq + qh) * s.T + t_lane) * DH;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + lgrp * 8);
-  }
 
   // ---- direct-load assignment: wave instruction q = wave + 4 i ------------
   // K rows go to LDS in permuted order with XOR-swizzled 16-byte slots; V
@@ -242,206 +255,232 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
     const int q = wave + 4 * i;
     loff[i] = (uint32_t)(((q < K_INS ? 0 : v_step) + (int64_t)lkey[i] * kvd + lcol[i]) * 2);
   }
-  int kq = (kt_begin * BN) / s.c, kr = kt_begin * BN - kq * s.c;
-  auto issue = [&](int kt, int stage) {
-    unsigned char* sb = smem + stage * STAGE;
-    const int key0 = kt * BN;
-    if constexpr (CH64) {
-      const int g_src = kq < s.D ? kq : 2 * s.D - 1 - kq;
-      const int t = (kq < s.D ? 0 : s.c) + kr;
-      const int64_t row0 = ((((int64_t)jsh * s.D + g_src) * 2) * s.B + b) * s.T + t;
-      const __amdgpu_buffer_rsrc_t rsrc =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.kv + row0 * kvd + head_off), (short)0, 0x7fffffff, 0x00020000);
-      kr += BN;
-      if (kr >= s.c) {
-        kr -= s.c;
-        ++kq;
-      }
-#pragma unroll
-      for (int i = 0; i < QW; ++i) {
-        const int q = wave + 4 * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sb + q * 1024), 16, (int)loff[i], 0, 0, 0);
-      }
-      (void)key0;
-    } else {
-#pragma unroll
-      for (int i = 0; i < QW; ++i) {
-        const int q = wave + 4 * i;
-        int p = key0 + lkey[i];
-        p = p < s.S ? p : s.S - 1;  // keys past the sequence end are masked
-        const int64_t off = gathered_row(s, jsh, q < K_INS ? 0 : 1, b, p) * kvd + head_off + lcol[i];
-        attn_load_lds16(a.kv + off, sb + q * 1024);
-      }
-    }
-  };
-  auto wait_tile = [&](int newer) {  // loads of later tiles may stay in flight
-    if constexpr (NST >= 3) {
-      if (newer >= 1) {
-        __builtin_amdgcn_s_waitcnt((QW & 15) | ((QW >> 4) << 14) | (7 << 4) | (0 << 8));
-        return;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
-  };
-  auto barrier = [&]() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  };
 
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int x = 0; x < NDB; ++x)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[x][e] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-  const float sc = a.scale_log2;
+  for (int part = 0; part < nparts; ++part) {
+    if (part == 1) g = block_rows(s, a.nrb, 2 * a.nrb - 1 - heavy_bi);
+    // split: this piece's partial state goes to the workspace for the merge
+    const bool split = part == 0 && g.ns > 1;
+    const int kt_begin = part == 0 ? piece * g.tper : 0;
+    const int kt_end = part == 0 ? (kt_begin + g.tper < g.nkt ? kt_begin + g.tper : g.nkt) : g.nkt;
+    const int wt0 = g.t0 + wave * 32;
+    const bool wave_active = wt0 < g.row_end;
+    int t_lane = wt0 + lrow;
+    const bool lane_valid = t_lane < g.row_end;
+    t_lane = lane_valid ? t_lane : g.row_end - 1;
+    const int qpos = g.gstart + (t_lane - g.row_begin);
+    const int w_last = (wt0 + 31 < g.row_end ? wt0 + 31 : g.row_end - 1);
+    const int wave_maxpos = g.gstart + (w_last - g.row_begin);
+    const int wave_minpos = g.gstart + (wt0 - g.row_begin);
 
-  {
-    int issued = 0;
+    // ---- Q fragments (second operand of S^T = K Q^T) ---------------------
+    u32x4 qf[NKS];
+    {
+      const uint16_t* qrow = a.q + (((int64_t)b * s.Hq + qh) * s.T + t_lane) * DH;
 #pragma unroll
-    for (int i = 0; i < NST - 1; ++i)
-      if (kt_begin + i < kt_end) {
-        issue(kt_begin + i, i);
-        ++issued;
-      }
-    wait_tile(issued - 1);
-    barrier();
-  }
-  // one key tile; the LDS stage is a compile-time constant so that every LDS
-  // address is a per-lane base plus an immediate
-  auto step = [&](int kt, auto ST_) __attribute__((always_inline)) {
-    constexpr int stage = decltype(ST_)::value;
-    constexpr int fill = (stage + NST - 1) % NST;
-    if (kt + NST - 1 < kt_end) issue(kt + NST - 1, fill);
-    const int key0 = kt * BN;
-    if (wave_active && key0 <= wave_maxpos) {
-      const unsigned char* sk = smem + stage * STAGE;
-      const unsigned char* sv = sk + K_BYTES;
-      f32x16 sacc[2];
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qrow + ks * 16 + lgrp * 8);
+    }
+
+    int kq = (kt_begin * BN) / s.c, kr = kt_begin * BN - kq * s.c;
+    auto issue = [&](int kt, int stage) {
+      unsigned char* sb = smem + stage * STAGE;
+      const int key0 = kt * BN;
+      if constexpr (CH64) {
+        const int g_src = kq < s.D ? kq : 2 * s.D - 1 - kq;
+        const int t = (kq < s.D ? 0 : s.c) + kr;
+        const int64_t row0 = ((((int64_t)jsh * s.D + g_src) * 2) * s.B + b) * s.T + t;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.kv + row0 * kvd + head_off), (short)0, 0x7fffffff, 0x00020000);
+        kr += BN;
+        if (kr >= s.c) {
+          kr -= s.c;
+          ++kq;
+        }
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+        for (int i = 0; i < QW; ++i) {
+          const int q = wave + 4 * i;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sb + q * 1024), 16, (int)loff[i], 0, 0, 0);
+        }
+        (void)key0;
+      } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[x][e] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int pch = ((2 * ks + lgrp) ^ kswz<DH>(lrow)) << 4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lrow) * KROW + pch);
-          sacc[kb] = mfma_f16(kf, qf[ks], sacc[kb]);
+        for (int i = 0; i < QW; ++i) {
+          const int q = wave + 4 * i;
+          int p = key0 + lkey[i];
+          p = p < s.S ? p : s.S - 1;  // keys past the sequence end are masked
+          const int64_t off = gathered_row(s, jsh, q < K_INS ? 0 : 1, b, p) * kvd + head_off + lcol[i];
+          attn_load_lds16(a.kv + off, sb + q * 1024);
         }
       }
-      // causal mask: register v of key group kb is key key0 + 32kb + 16(v/8) + 8 lgrp + v%8
-      if (key0 + BN - 1 > wave_minpos) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + 32 * kb + 16 * (v >> 3) + 8 * lgrp + (v & 7);
-            if (key > qpos) sacc[kb][v] = -INFINITY;
-          }
+    };
+    auto wait_tile = [&](int newer) {  // loads of later tiles may stay in flight
+      if constexpr (NST >= 3) {
+        if (newer >= 1) {
+          __builtin_amdgcn_s_waitcnt((QW & 15) | ((QW >> 4) << 14) | (7 << 4) | (0 << 8));
+          return;
+        }
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-      mx = pair_max(mx);
-      // The reference maximum m_run moves only when the row maximum passes it
-      // by more than 8 (log2 units).  Exponents then stay <= 8 (probabilities
-      // < 256: fine for f16 P and the float32 sums), numerator and denominator
-      // share the reference so the result is the same, and most tiles skip
-      // the rescale of O.
-      const float m_max = fmaxf(m_run, mx * sc);
-      const float m_new = m_max > m_run + 8.0f ? m_max : m_run;
-      // a row with no unmasked key yet keeps m = -inf; its probabilities are 0
-      const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
-      float rs = 0.0f;
-      u32x4 pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_sub));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_sub));
-            const uint32_t pk = pack_f16x2(p0, p1);
-            pf[kb][st][w] = pk;
-            // the row sum is taken over the f16 probabilities that P V uses
-            rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, pk),
-                                        (__attribute__((ext_vector_type(2))) _Float16){1.0f16, 1.0f16}, rs, false);
-          }
-      // rescale only when some row's maximum moved (alpha == 1 otherwise)
-      if (__any(m_new != m_run)) {
-        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int x = 0; x < NDB; ++x)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
-      }
-      l_run += rs;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            // keys 32 kb + 16 st + 8 (lane / 32) + 4 r + (0..3), head-dim column db * 32 + lane % 32
-            const unsigned char* vp = sv + vlane[db] + (32 * kb + 16 * st) * KROW;
-            const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp);
-            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KROW));
-            const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
-            const u32x4 vf{h0[0], h0[1], h1[0], h1[1]};
-            oacc[db] = mfma_f16(vf, pf[kb][st], oacc[db]);
-          }
-      }
-    }
-    const int last_issued = (kt + NST - 1 < kt_end) ? kt + NST - 1 : kt_end - 1;
-    wait_tile(last_issued - (kt + 1));
-    barrier();
-  };
-  static_assert(NST == 2, "the tile loop below alternates two stages");
-  int kt = kt_begin;
-  for (; kt + 1 < kt_end; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
-  }
-  if (kt < kt_end) step(kt, std::integral_constant<int, 0>{});
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));
+    };
+    auto barrier = [&]() {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
 
-  // ---- store: final f16 output, or the piece's partial state ------------
-  const float l_tot = pair_sum(l_run);
-  if (!wave_active || !lane_valid) return;
-  if (g.ns == 1) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = a.o + ((int64_t)b * s.T + t_lane) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH;
+    f32x16 oacc[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int x = 0; x < NDB; ++x)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * lgrp;
-        u32x2 pk{pack_f16x2(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv),
-                 pack_f16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = pk;
+      for (int e = 0; e < 16; ++e) oacc[x][e] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    const float sc = a.scale_log2;
+
+    {
+      int issued = 0;
+#pragma unroll
+      for (int i = 0; i < NST - 1; ++i)
+        if (kt_begin + i < kt_end) {
+          issue(kt_begin + i, i);
+          ++issued;
+        }
+      wait_tile(issued - 1);
+      barrier();
+    }
+    // one key tile; the LDS stage is a compile-time constant so that every LDS
+    // address is a per-lane base plus an immediate
+    auto step = [&](int kt, auto ST_) __attribute__((always_inline)) {
+      constexpr int stage = decltype(ST_)::value;
+      constexpr int fill = (stage + NST - 1) % NST;
+      if (kt + NST - 1 < kt_end) issue(kt + NST - 1, fill);
+      const int key0 = kt * BN;
+      if (wave_active && key0 <= wave_maxpos) {
+        const unsigned char* sk = smem + stage * STAGE;
+        const unsigned char* sv = sk + K_BYTES;
+        f32x16 sacc[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[x][e] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int pch = ((2 * ks + lgrp) ^ kswz<DH>(lrow)) << 4;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lrow) * KROW + pch);
+            sacc[kb] = mfma_f16(kf, qf[ks], sacc[kb]);
+          }
+        }
+        // causal mask: register v of key group kb is key key0 + 32kb + 16(v/8) + 8 lgrp + v%8
+        if (key0 + BN - 1 > wave_minpos) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int key = key0 + 32 * kb + 16 * (v >> 3) + 8 * lgrp + (v & 7);
+              if (key > qpos) sacc[kb][v] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+        mx = pair_max(mx);
+        // The reference maximum m_run moves only when the row maximum passes it
+        // by more than 8 (log2 units).  Exponents then stay <= 8 (probabilities
+        // < 256: fine for f16 P and the float32 sums), numerator and denominator
+        // share the reference so the result is the same, and most tiles skip
+        // the rescale of O.
+        const float m_max = fmaxf(m_run, mx * sc);
+        const float m_new = m_max > m_run + 8.0f ? m_max : m_run;
+        // a row with no unmasked key yet keeps m = -inf; its probabilities are 0
+        const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+        float rs = 0.0f;
+        u32x4 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_sub));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_sub));
+              const uint32_t pk = pack_f16x2(p0, p1);
+              pf[kb][st][w] = pk;
+              // the row sum is taken over the f16 probabilities that P V uses
+              rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, pk),
+                                          (__attribute__((ext_vector_type(2))) _Float16){1.0f16, 1.0f16}, rs, false);
+            }
+        // rescale only when some row's maximum moved (alpha == 1 otherwise)
+        if (__any(m_new != m_run)) {
+          const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int x = 0; x < NDB; ++x)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
+        }
+        l_run += rs;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              // keys 32 kb + 16 st + 8 (lane / 32) + 4 r + (0..3), head-dim column db * 32 + lane % 32
+              const unsigned char* vp = sv + vlane[db] + (32 * kb + 16 * st) * KROW;
+              const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp);
+              const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KROW));
+              const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
+              const u32x4 vf{h0[0], h0[1], h1[0], h1[1]};
+              oacc[db] = mfma_f16(vf, pf[kb][st], oacc[db]);
+            }
+        }
       }
-  } else {
-    const int64_t pidx = (int64_t)(piece_base + piece) * per_bh + bh;
-    const int r = t_lane - g.t0;
-    float* po = a.part_o + (pidx * 128 + r) * DH;
+      const int last_issued = (kt + NST - 1 < kt_end) ? kt + NST - 1 : kt_end - 1;
+      wait_tile(last_issued - (kt + 1));
+      barrier();
+    };
+    static_assert(NST == 2, "the tile loop below alternates two stages");
+    int kt = kt_begin;
+    for (; kt + 1 < kt_end; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if (kt < kt_end) step(kt, std::integral_constant<int, 0>{});
+
+    // ---- store: final f16 output, or the piece's partial state ------------
+    const float l_tot = pair_sum(l_run);
+    if (!wave_active || !lane_valid) continue;
+    if (!split) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = a.o + ((int64_t)b * s.T + t_lane) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * lgrp;
-        f32x4 v{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
-        *reinterpret_cast<f32x4*>(po + d) = v;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = db * 32 + 8 * q4 + 4 * lgrp;
+          u32x2 pk{pack_f16x2(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv),
+                   pack_f16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d) = pk;
+        }
+    } else {
+      const int64_t pidx = (int64_t)(piece_base + piece) * per_bh + bh;
+      const int r = t_lane - g.t0;
+      float* po = a.part_o + (pidx * 128 + r) * DH;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = db * 32 + 8 * q4 + 4 * lgrp;
+          f32x4 v{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
+          *reinterpret_cast<f32x4*>(po + d) = v;
+        }
+      if (lgrp == 0) {
+        a.part_ml[(pidx * 2 + 0) * 128 + r] = m_run;
+        a.part_ml[(pidx * 2 + 1) * 128 + r] = l_tot;
       }
-    if (lgrp == 0) {
-      a.part_ml[(pidx * 2 + 0) * 128 + r] = m_run;
-      a.part_ml[(pidx * 2 + 1) * 128 + r] = l_tot;
     }
   }
 }
@@ -458,8 +497,8 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   // locate the split block this item belongs to
   int piece_base = 0;
   for (int bi = 0; bi < 2 * a.nrb; ++bi) {
-    const BlockGeo g = block_geo(s, a.nrb, a.kt_max, bi);
-    if (g.ns == 1) continue;
+    const BlockGeo g = block_geo(s, a.nrb, a.kt_max, a.pair, bi);
+    if (g.ns <= 1) continue;
     const int64_t n = (int64_t)per_bh * 128 * cols;
     if (item >= n) {
       item -= n;
@@ -498,55 +537,55 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 }
 
 // ---- host-side plan (shared with workspace sizing) -----------------------
-static int host_nkt(const Shape& s, int nrb, int bi) {
-  const int late = bi < nrb ? 1 : 0;
-  const int rb = nrb - 1 - (late ? bi : bi - nrb);
-  const int row_begin = late * s.c, row_end = row_begin + s.c;
-  const int gstart = (late ? (2 * s.D - 1 - s.r) : s.r) * s.c;
-  const int t0 = row_begin + rb * 128;
-  const int last = t0 + 127 < row_end ? t0 + 127 : row_end - 1;
-  return (gstart + (last - row_begin) + 64) / 64;
-}
-
-AttnPlan attn_plan(const Shape& s) {
+// pair < 0: the default (paired whenever blocks are split).
+static AttnPlan plan_for(const Shape& s, int pair) {
   AttnPlan p;
   p.nrb = (s.c + 127) / 128;
   const int64_t blocks = (int64_t)2 * p.nrb * s.B * s.Hq;
   int64_t tiles = 0;
-  for (int bi = 0; bi < 2 * p.nrb; ++bi) tiles += host_nkt(s, p.nrb, bi);
+  for (int bi = 0; bi < 2 * p.nrb; ++bi) tiles += block_rows(s, p.nrb, bi).nkt;
   tiles *= (int64_t)s.B * s.Hq;
   // split only when there are too few blocks to fill 256 CUs twice over;
-  // pieces then hold about tiles / 512 key tiles (tuning override, no effect
-  // unless set: TSP_ATTN_PIECES=<target number of work units>)
+  // pieces then hold about tiles / 512 key tiles (tuning overrides, no effect
+  // unless set: TSP_ATTN_PIECES=<target number of work units>,
+  // TSP_ATTN_PAIR=0 to give the earlier chunk's blocks units of their own)
   int64_t target = 512;
   if (const char* ev = getenv("TSP_ATTN_PIECES")) {
     if (atoi(ev) > 0) target = atoi(ev);
   }
   if (blocks >= 1024) {
     p.kt_max = 1 << 30;
+    p.pair = 0;
   } else {
     int64_t kt = (tiles + target - 1) / target;
     p.kt_max = (int)(kt < 16 ? 16 : kt);
+    if (pair < 0) {
+      const char* ev = getenv("TSP_ATTN_PAIR");
+      pair = (ev != nullptr && ev[0] == '0') ? 0 : 1;
+    }
+    p.pair = pair;
   }
   p.units = 0;
   p.pieces = 0;
-  for (int bi = 0; bi < 2 * p.nrb; ++bi) {
-    const int nkt = host_nkt(s, p.nrb, bi);
-    const int ns = (nkt + p.kt_max - 1) / p.kt_max;
-    p.units += (int64_t)ns * s.B * s.Hq;
-    if (ns > 1) p.pieces += ns;
-  }
   p.split_rows = 0;
   for (int bi = 0; bi < 2 * p.nrb; ++bi) {
-    const int nkt = host_nkt(s, p.nrb, bi);
-    if ((nkt + p.kt_max - 1) / p.kt_max > 1) p.split_rows += 128;
+    const BlockGeo g = block_geo(s, p.nrb, p.kt_max, p.pair, bi);
+    p.units += (int64_t)g.ns * s.B * s.Hq;
+    if (g.ns > 1) {
+      p.pieces += g.ns;
+      p.split_rows += 128;
+    }
   }
   return p;
 }
 
+AttnPlan attn_plan(const Shape& s) { return plan_for(s, -1); }
+
+// Enough for either plan, so that a workspace sized once serves both.
 size_t attn_partial_bytes(const Shape& s) {
-  const AttnPlan p = attn_plan(s);
-  return (size_t)p.pieces * s.B * s.Hq * 128 * (s.dh + 2) * sizeof(float);
+  const AttnPlan p0 = plan_for(s, 0), p1 = plan_for(s, 1);
+  const int pieces = p0.pieces > p1.pieces ? p0.pieces : p1.pieces;
+  return (size_t)pieces * s.B * s.Hq * 128 * (s.dh + 2) * sizeof(float);
 }
 
 hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, uint16_t* o,
@@ -562,6 +601,7 @@ hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* 
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.dh));
   a.nrb = p.nrb;
   a.kt_max = p.kt_max;
+  a.pair = p.pair;
   dim3 grid((unsigned)p.units);
   // the whole-tile path addresses a tile's K and V rows with 31-bit offsets
   const int64_t kvd = (int64_t)s.Hkv_s * s.dh;

@@ -57,6 +57,7 @@ hipError_t launch_f32_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t
 struct AttnPlan {
   int nrb;          // 128-row blocks per zigzag chunk
   int kt_max;       // key tiles (64 keys) per piece at most
+  int pair;         // 1: earlier-chunk blocks run inside their later-chunk partner's last piece
   int64_t units;    // work groups of the attention kernel
   int pieces;       // pieces of split blocks, summed over the block list
   int split_rows;   // 128 x (number of split blocks)

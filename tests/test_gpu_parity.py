@@ -136,9 +136,22 @@ def _shape(name):
 
 @pytest.mark.parametrize("name", SMALL)
 def test_attn_fwd(name):
+    _check_attn_fwd(name, f"attn_fwd {name}")
+
+
+# The attention work plan without pairing (the library's tuning variable): the
+# earlier zigzag chunk's row blocks get work units of their own instead of
+# running inside the last key piece of their later-chunk partner.
+@pytest.mark.parametrize("name", ["split_keys_dh128", "split_keys_gqa_b2", "wide_tiles_dh128", "mha_d2_r1"])
+def test_attn_fwd_unpaired_plan(name, monkeypatch):
+    monkeypatch.setenv("TSP_ATTN_PAIR", "0")
+    _check_attn_fwd(name, f"attn_fwd {name} unpaired")
+
+
+def _check_attn_fwd(name, case):
     shape, sigma, seed = _shape(name)
     d = dims_of(shape)
-    _case(f"attn_fwd {name}")
+    _case(case)
     inp = inputs_for(shape, sigma, seed)
     prob = RankProblem.build(d, inp)
     T = d.seq // d.degree
