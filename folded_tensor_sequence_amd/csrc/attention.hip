@@ -9,13 +9,14 @@
 // контексту: Ring Attention против Ulysses": the online-softmax accumulator),
 // so the S x S score matrix is never stored.
 //
-// Work: a block is 128 consecutive local rows of one zigzag chunk for one
-// (sequence, q-head); 4 waves x 32 query rows.  The rank's later chunk sees a
-// key prefix up to 2D-1 times longer than its earlier one, so a block whose
-// key range exceeds kt_max tiles of 64 keys is cut into pieces along the keys
-// (each piece keeps its own max / sum / unnormalised output, merged afterwards
-// in piece order, so results are deterministic).  Units are ordered heaviest
-// block first.
+// Work: a block is 32 x (waves per block) consecutive local rows of one
+// zigzag chunk for one (sequence, q-head), 32 query rows per wave; its waves
+// share every K/V tile loaded into LDS.  The rank's later chunk sees a key
+// prefix up to 2D-1 times longer than its earlier one, so a block whose key
+// range exceeds kt_max tiles of 64 keys is cut into pieces along the keys
+// (each piece keeps its own max / sum / unnormalised output, merged
+// afterwards in piece order, so results are deterministic).  Units are
+// ordered heaviest block first.
 //
 // Per 64-key tile:
 //   S^T = K Q^T   (32x32x16 MFMA, K from LDS as the first operand, the wave's
@@ -37,7 +38,9 @@
 // tiles carries no memory fence, so the loads of later tiles stay in flight
 // across it.
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <type_traits>
 
@@ -50,11 +53,12 @@ struct AttnArgs {
   const uint16_t* q;     // f16 [B][Hq][T][dh]
   const uint16_t* kv;    // f16 all-gathered K/V [D shard][D src][K|V][B][T][Hkv/D * dh]
   uint16_t* o;           // f16 [B][T][Hq*dh]
-  float* part_o;         // [pieces][B*Hq][128][dh] unnormalised outputs of split blocks
-  float* part_ml;        // [pieces][B*Hq][2][128] (scaled max, sum)
+  float* part_o;         // [pieces][B*Hq][rb][dh] unnormalised outputs of split blocks
+  float* part_ml;        // [pieces][B*Hq][2][rb] (scaled max, sum)
   Shape s;
   float scale_log2;      // log2(e) / sqrt(dh)
-  int32_t nrb;           // 128-row blocks per chunk
+  int32_t rb;            // rows per block: 32 per wave (128 or 256)
+  int32_t nrb;           // row blocks per chunk
   int32_t kt_max;        // key tiles per piece at most
   int32_t pair;          // 1: each earlier-chunk block rides with a later-chunk block
 };
@@ -126,15 +130,15 @@ struct BlockGeo {
   int tper;                // key tiles per piece (the last piece may hold fewer)
 };
 
-__host__ __device__ inline BlockGeo block_rows(const Shape& s, int nrb, int bi) {
+__host__ __device__ inline BlockGeo block_rows(const Shape& s, int rbr, int nrb, int bi) {
   BlockGeo g;
   const int late = bi < nrb ? 1 : 0;
   const int rb = nrb - 1 - (late ? bi : bi - nrb);
   g.row_begin = late * s.c;
   g.row_end = g.row_begin + s.c;
   g.gstart = (late ? (2 * s.D - 1 - s.r) : s.r) * s.c;
-  g.t0 = g.row_begin + rb * 128;
-  const int last = g.t0 + 127 < g.row_end ? g.t0 + 127 : g.row_end - 1;
+  g.t0 = g.row_begin + rb * rbr;
+  const int last = g.t0 + rbr - 1 < g.row_end ? g.t0 + rbr - 1 : g.row_end - 1;
   g.nkt = (g.gstart + (last - g.row_begin) + 64) / 64;
   g.ns = 1;
   g.tper = g.nkt;
@@ -147,15 +151,15 @@ __host__ __device__ inline BlockGeo block_rows(const Shape& s, int nrb, int bi) 
 // share their work units: the heavy block's key range is cut so that its
 // last piece plus the whole light block weigh about as much as each other
 // piece, and the unit of that last piece then runs the light block too.
-__host__ __device__ inline BlockGeo block_geo(const Shape& s, int nrb, int kt_max, int pair, int bi) {
-  BlockGeo g = block_rows(s, nrb, bi);
+__host__ __device__ inline BlockGeo block_geo(const Shape& s, int rbr, int nrb, int kt_max, int pair, int bi) {
+  BlockGeo g = block_rows(s, rbr, nrb, bi);
   if (!pair) {
     g.ns = (g.nkt + kt_max - 1) / kt_max;
     g.tper = (g.nkt + g.ns - 1) / g.ns;
   } else if (bi >= nrb) {
     g.ns = 0;
   } else {
-    const int tot = g.nkt + block_rows(s, nrb, 2 * nrb - 1 - bi).nkt;
+    const int tot = g.nkt + block_rows(s, rbr, nrb, 2 * nrb - 1 - bi).nkt;
     int ns = (tot + kt_max - 1) / kt_max, tper = (tot + ns - 1) / ns;
     while (ns > 1 && (ns - 1) * tper >= g.nkt) {  // the last piece keeps at least one heavy tile
       --ns;
@@ -169,8 +173,9 @@ __host__ __device__ inline BlockGeo block_geo(const Shape& s, int nrb, int kt_ma
 
 // CH64: chunks are whole multiples of 64 keys, so a key tile never straddles
 // two chunks and its gathered rows are consecutive (one address per tile).
-template <int DH, int NST, bool CH64>
-__global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnArgs a) {
+// NWV waves per block (block rows 32 NWV), NST-deep LDS ring of K/V tiles.
+template <int DH, int NST, bool CH64, int NWV>
+__global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_attn_kernel(AttnArgs a) {
   constexpr int BN = 64;
   constexpr int KROW = DH * 2;
   constexpr int K_BYTES = BN * KROW;
@@ -180,8 +185,9 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   constexpr int K_INS = BN / KRPI;           // instructions per K tile
   constexpr int V_INS = BN / KRPI;           // ... per V tile
   constexpr int QT = K_INS + V_INS;
-  static_assert(QT % 4 == 0, "loads split evenly over 4 waves");
-  constexpr int QW = QT / 4;                 // per wave
+  static_assert(QT % NWV == 0, "loads split evenly over the waves");
+  constexpr int QW = QT / NWV;               // per wave
+  constexpr int RBR = 32 * NWV;              // rows per block
   constexpr int NDB = DH / 32;
   constexpr int NKS = DH / 16;
   __shared__ __align__(16) unsigned char smem[NST * STAGE];
@@ -204,14 +210,14 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   // ---- work unit -> (block, piece, sequence, q-head) --------------------
   const int per_bh = s.B * s.Hq;
   int u = blockIdx.x, bi = 0, piece_base = 0;
-  BlockGeo g = block_geo(s, a.nrb, a.kt_max, a.pair, 0);
+  BlockGeo g = block_geo(s, RBR, a.nrb, a.kt_max, a.pair, 0);
   for (;;) {
     const int n = g.ns * per_bh;
     if (u < n || bi + 1 >= 2 * a.nrb) break;
     u -= n;
     if (g.ns > 1) piece_base += g.ns;
     ++bi;
-    g = block_geo(s, a.nrb, a.kt_max, a.pair, bi);
+    g = block_geo(s, RBR, a.nrb, a.kt_max, a.pair, bi);
   }
   const int piece = u / per_bh, bh = u - piece * per_bh;
   const int b = bh / s.Hq, qh = bh - b * s.Hq;
@@ -226,13 +232,13 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   const int64_t head_off = (int64_t)hk * DH;
   const int64_t v_step = (int64_t)s.B * s.T * kvd;  // K slot -> V slot of the same rows
 
-  // ---- direct-load assignment: wave instruction q = wave + 4 i ------------
+  // ---- direct-load assignment: wave instruction q = wave + NWV i ----------
   // K rows go to LDS in permuted order with XOR-swizzled 16-byte slots; V
   // rows in natural order with XOR-swizzled 64-byte chunks.
   int lkey[QW], lcol[QW];
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
-    const int q = wave + 4 * i;
+    const int q = wave + NWV * i;
     const int slot = lane % (KROW / 16);
     if (q < K_INS) {
       const int row = KRPI * q + lane / (KROW / 16);
@@ -252,12 +258,12 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
   uint32_t loff[QW];
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
-    const int q = wave + 4 * i;
+    const int q = wave + NWV * i;
     loff[i] = (uint32_t)(((q < K_INS ? 0 : v_step) + (int64_t)lkey[i] * kvd + lcol[i]) * 2);
   }
 
   for (int part = 0; part < nparts; ++part) {
-    if (part == 1) g = block_rows(s, a.nrb, 2 * a.nrb - 1 - heavy_bi);
+    if (part == 1) g = block_rows(s, RBR, a.nrb, 2 * a.nrb - 1 - heavy_bi);
     // split: this piece's partial state goes to the workspace for the merge
     const bool split = part == 0 && g.ns > 1;
     const int kt_begin = part == 0 ? piece * g.tper : 0;
@@ -297,14 +303,14 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
         }
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
-          const int q = wave + 4 * i;
+          const int q = wave + NWV * i;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sb + q * 1024), 16, (int)loff[i], 0, 0, 0);
         }
         (void)key0;
       } else {
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
-          const int q = wave + 4 * i;
+          const int q = wave + NWV * i;
           int p = key0 + lkey[i];
           p = p < s.S ? p : s.S - 1;  // keys past the sequence end are masked
           const int64_t off = gathered_row(s, jsh, q < K_INS ? 0 : 1, b, p) * kvd + head_off + lcol[i];
@@ -335,6 +341,97 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
     float m_run = -INFINITY, l_run = 0.0f;
     const float sc = a.scale_log2;
 
+    // ---- the three parts of one key tile ----------------------------------
+    // S^T = K Q^T with K at sk
+    auto s_block = [&](const unsigned char* sk, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[x][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int pch = ((2 * ks + lgrp) ^ kswz<DH>(lrow)) << 4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lrow) * KROW + pch);
+          sacc[kb] = mfma_f16(kf, qf[ks], sacc[kb]);
+        }
+      }
+    };
+    // causal mask and online softmax of the tile at key0: probabilities to
+    // pf (f16), running max / sum updated, O rescaled when the max moved
+    auto softmax_block = [&](int key0, f32x16 (&sacc)[2], u32x4 (&pf)[2][2]) __attribute__((always_inline)) {
+      // causal mask: register v of key group kb is key key0 + 32kb + 16(v/8) + 8 lgrp + v%8
+      if (key0 + BN - 1 > wave_minpos) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = key0 + 32 * kb + 16 * (v >> 3) + 8 * lgrp + (v & 7);
+            if (key > qpos) sacc[kb][v] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+      mx = pair_max(mx);
+      // The reference maximum m_run moves only when the row maximum passes it
+      // by more than 8 (log2 units).  Exponents then stay <= 8 (probabilities
+      // < 256: fine for f16 P and the float32 sums), numerator and denominator
+      // share the reference so the result is the same, and most tiles skip
+      // the rescale of O.
+      const float m_max = fmaxf(m_run, mx * sc);
+      const float m_new = m_max > m_run + 8.0f ? m_max : m_run;
+      // a row with no unmasked key yet keeps m = -inf; its probabilities are 0
+      const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_sub));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_sub));
+            const uint32_t pk = pack_f16x2(p0, p1);
+            pf[kb][st][w] = pk;
+            // the row sum is taken over the f16 probabilities that P V uses
+            rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, pk),
+                                        (__attribute__((ext_vector_type(2))) _Float16){1.0f16, 1.0f16}, rs, false);
+          }
+      // rescale only when some row's maximum moved (alpha == 1 otherwise)
+      if (__any(m_new != m_run)) {
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int x = 0; x < NDB; ++x)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
+      }
+      l_run += rs;
+      m_run = m_new;
+    };
+    // O^T += V^T P with V at sv
+    auto pv_block = [&](const unsigned char* sv, const u32x4 (&pf)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            // keys 32 kb + 16 st + 8 (lane / 32) + 4 r + (0..3), head-dim column db * 32 + lane % 32
+            const unsigned char* vp = sv + vlane[db] + (32 * kb + 16 * st) * KROW;
+            const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp);
+            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KROW));
+            const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
+            const u32x4 vf{h0[0], h0[1], h1[0], h1[1]};
+            oacc[db] = mfma_f16(vf, pf[kb][st], oacc[db]);
+          }
+      }
+    };
+
     {
       int issued = 0;
 #pragma unroll
@@ -346,8 +443,8 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
       wait_tile(issued - 1);
       barrier();
     }
-    // one key tile; the LDS stage is a compile-time constant so that every LDS
-    // address is a per-lane base plus an immediate
+    // one key tile; the LDS stage is a compile-time constant so that every
+    // LDS address is a per-lane base plus an immediate
     auto step = [&](int kt, auto ST_) __attribute__((always_inline)) {
       constexpr int stage = decltype(ST_)::value;
       constexpr int fill = (stage + NST - 1) % NST;
@@ -355,100 +452,23 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
       const int key0 = kt * BN;
       if (wave_active && key0 <= wave_maxpos) {
         const unsigned char* sk = smem + stage * STAGE;
-        const unsigned char* sv = sk + K_BYTES;
         f32x16 sacc[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sacc[x][e] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int pch = ((2 * ks + lgrp) ^ kswz<DH>(lrow)) << 4;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(sk + (kb * 32 + lrow) * KROW + pch);
-            sacc[kb] = mfma_f16(kf, qf[ks], sacc[kb]);
-          }
-        }
-        // causal mask: register v of key group kb is key key0 + 32kb + 16(v/8) + 8 lgrp + v%8
-        if (key0 + BN - 1 > wave_minpos) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = key0 + 32 * kb + 16 * (v >> 3) + 8 * lgrp + (v & 7);
-              if (key > qpos) sacc[kb][v] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-        mx = pair_max(mx);
-        // The reference maximum m_run moves only when the row maximum passes it
-        // by more than 8 (log2 units).  Exponents then stay <= 8 (probabilities
-        // < 256: fine for f16 P and the float32 sums), numerator and denominator
-        // share the reference so the result is the same, and most tiles skip
-        // the rescale of O.
-        const float m_max = fmaxf(m_run, mx * sc);
-        const float m_new = m_max > m_run + 8.0f ? m_max : m_run;
-        // a row with no unmasked key yet keeps m = -inf; its probabilities are 0
-        const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
-        float rs = 0.0f;
         u32x4 pf[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w], sc, -m_sub));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * st + 2 * w + 1], sc, -m_sub));
-              const uint32_t pk = pack_f16x2(p0, p1);
-              pf[kb][st][w] = pk;
-              // the row sum is taken over the f16 probabilities that P V uses
-              rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, pk),
-                                          (__attribute__((ext_vector_type(2))) _Float16){1.0f16, 1.0f16}, rs, false);
-            }
-        // rescale only when some row's maximum moved (alpha == 1 otherwise)
-        if (__any(m_new != m_run)) {
-          const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int x = 0; x < NDB; ++x)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
-        }
-        l_run += rs;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-              // keys 32 kb + 16 st + 8 (lane / 32) + 4 r + (0..3), head-dim column db * 32 + lane % 32
-              const unsigned char* vp = sv + vlane[db] + (32 * kb + 16 * st) * KROW;
-              const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp);
-              const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KROW));
-              const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
-              const u32x4 vf{h0[0], h0[1], h1[0], h1[1]};
-              oacc[db] = mfma_f16(vf, pf[kb][st], oacc[db]);
-            }
-        }
+        s_block(sk, sacc);
+        softmax_block(key0, sacc, pf);
+        pv_block(sk + K_BYTES, pf);
       }
       const int last_issued = (kt + NST - 1 < kt_end) ? kt + NST - 1 : kt_end - 1;
       wait_tile(last_issued - (kt + 1));
       barrier();
     };
-    static_assert(NST == 2, "the tile loop below alternates two stages");
+    // tile kt_begin + j sits in stage j mod NST
     int kt = kt_begin;
-    for (; kt + 1 < kt_end; kt += 2) {
-      step(kt, std::integral_constant<int, 0>{});
-      step(kt + 1, std::integral_constant<int, 1>{});
-    }
-    if (kt < kt_end) step(kt, std::integral_constant<int, 0>{});
+    for (; kt + NST - 1 < kt_end; kt += NST)
+      static_for<0, NST>([&](auto I) __attribute__((always_inline)) { step(kt + decltype(I)::value, I); });
+    static_for<0, NST - 1>([&](auto I) __attribute__((always_inline)) {
+      if (kt + decltype(I)::value < kt_end) step(kt + decltype(I)::value, I);
+    });
 
     // ---- store: final f16 output, or the piece's partial state ------------
     const float l_tot = pair_sum(l_run);
@@ -468,7 +488,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
     } else {
       const int64_t pidx = (int64_t)(piece_base + piece) * per_bh + bh;
       const int r = t_lane - g.t0;
-      float* po = a.part_o + (pidx * 128 + r) * DH;
+      float* po = a.part_o + (pidx * RBR + r) * DH;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -478,8 +498,8 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void flash_attn_kernel(AttnA
           *reinterpret_cast<f32x4*>(po + d) = v;
         }
       if (lgrp == 0) {
-        a.part_ml[(pidx * 2 + 0) * 128 + r] = m_run;
-        a.part_ml[(pidx * 2 + 1) * 128 + r] = l_tot;
+        a.part_ml[(pidx * 2 + 0) * RBR + r] = m_run;
+        a.part_ml[(pidx * 2 + 1) * RBR + r] = l_tot;
       }
     }
   }
@@ -497,31 +517,31 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   // locate the split block this item belongs to
   int piece_base = 0;
   for (int bi = 0; bi < 2 * a.nrb; ++bi) {
-    const BlockGeo g = block_geo(s, a.nrb, a.kt_max, a.pair, bi);
+    const BlockGeo g = block_geo(s, a.rb, a.nrb, a.kt_max, a.pair, bi);
     if (g.ns <= 1) continue;
-    const int64_t n = (int64_t)per_bh * 128 * cols;
+    const int64_t n = (int64_t)per_bh * a.rb * cols;
     if (item >= n) {
       item -= n;
       piece_base += g.ns;
       continue;
     }
     const int c4 = (int)(item % cols);
-    const int r = (int)((item / cols) % 128);
-    const int bh = (int)(item / (cols * 128));
+    const int r = (int)((item / cols) % a.rb);
+    const int bh = (int)(item / (cols * a.rb));
     const int t = g.t0 + r;
     if (t >= g.row_end) return;
     float mmax = -INFINITY;
     for (int p = 0; p < g.ns; ++p) {
       const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
-      mmax = fmaxf(mmax, a.part_ml[(pidx * 2 + 0) * 128 + r]);
+      mmax = fmaxf(mmax, a.part_ml[(pidx * 2 + 0) * a.rb + r]);
     }
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
     float l = 0.f;
     for (int p = 0; p < g.ns; ++p) {
       const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
-      const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * 128 + r] - mmax);
-      l += w * a.part_ml[(pidx * 2 + 1) * 128 + r];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (pidx * 128 + r) * DH + 4 * c4);
+      const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * a.rb + r] - mmax);
+      l += w * a.part_ml[(pidx * 2 + 1) * a.rb + r];
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (pidx * a.rb + r) * DH + 4 * c4);
       acc[0] += w * v[0];
       acc[1] += w * v[1];
       acc[2] += w * v[2];
@@ -537,23 +557,48 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 }
 
 // ---- host-side plan (shared with workspace sizing) -----------------------
+// Kernel shape: waves per block (32 rows each) and depth of the K/V ring.
+// The default, 4 waves and 2 stages, fits two blocks per CU; 8 waves and 3
+// stages (one block per CU, each K/V tile shared by 256 query rows) is the
+// alternative.  Tuning override (no effect unless set):
+// TSP_ATTN_SHAPE=<waves>x<stages>, 4x2 or 8x3.
+struct AttnShape {
+  int nwv, nst;
+};
+static const AttnShape kShapes[] = {{4, 2}, {8, 3}};
+
+static AttnShape attn_shape() {
+  if (const char* ev = getenv("TSP_ATTN_SHAPE")) {
+    for (const AttnShape& k : kShapes) {
+      char name[8];
+      snprintf(name, sizeof name, "%dx%d", k.nwv, k.nst);
+      if (strcmp(ev, name) == 0) return k;
+    }
+  }
+  return kShapes[0];
+}
+
 // pair < 0: the default (paired whenever blocks are split).
-static AttnPlan plan_for(const Shape& s, int pair) {
+static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   AttnPlan p;
-  p.nrb = (s.c + 127) / 128;
+  p.nwv = k.nwv;
+  p.nst = k.nst;
+  p.rb = 32 * k.nwv;
+  p.nrb = (s.c + p.rb - 1) / p.rb;
+  const int64_t slots = k.nwv == 4 && k.nst == 2 ? 512 : 256;  // resident blocks on 256 CUs
   const int64_t blocks = (int64_t)2 * p.nrb * s.B * s.Hq;
   int64_t tiles = 0;
-  for (int bi = 0; bi < 2 * p.nrb; ++bi) tiles += block_rows(s, p.nrb, bi).nkt;
+  for (int bi = 0; bi < 2 * p.nrb; ++bi) tiles += block_rows(s, p.rb, p.nrb, bi).nkt;
   tiles *= (int64_t)s.B * s.Hq;
-  // split only when there are too few blocks to fill 256 CUs twice over;
-  // pieces then hold about tiles / 512 key tiles (tuning overrides, no effect
-  // unless set: TSP_ATTN_PIECES=<target number of work units>,
+  // split only when there are too few blocks to fill the CUs twice over;
+  // pieces then hold about tiles / slots key tiles (tuning overrides, no
+  // effect unless set: TSP_ATTN_PIECES=<target number of work units>,
   // TSP_ATTN_PAIR=0 to give the earlier chunk's blocks units of their own)
-  int64_t target = 512;
+  int64_t target = slots;
   if (const char* ev = getenv("TSP_ATTN_PIECES")) {
     if (atoi(ev) > 0) target = atoi(ev);
   }
-  if (blocks >= 1024) {
+  if (blocks >= 2 * slots) {
     p.kt_max = 1 << 30;
     p.pair = 0;
   } else {
@@ -569,23 +614,45 @@ static AttnPlan plan_for(const Shape& s, int pair) {
   p.pieces = 0;
   p.split_rows = 0;
   for (int bi = 0; bi < 2 * p.nrb; ++bi) {
-    const BlockGeo g = block_geo(s, p.nrb, p.kt_max, p.pair, bi);
+    const BlockGeo g = block_geo(s, p.rb, p.nrb, p.kt_max, p.pair, bi);
     p.units += (int64_t)g.ns * s.B * s.Hq;
     if (g.ns > 1) {
       p.pieces += g.ns;
-      p.split_rows += 128;
+      p.split_rows += p.rb;
     }
   }
   return p;
 }
 
-AttnPlan attn_plan(const Shape& s) { return plan_for(s, -1); }
+AttnPlan attn_plan(const Shape& s) { return plan_for(s, -1, attn_shape()); }
 
-// Enough for either plan, so that a workspace sized once serves both.
+// Enough for every plan, so that a workspace sized once serves them all.
 size_t attn_partial_bytes(const Shape& s) {
-  const AttnPlan p0 = plan_for(s, 0), p1 = plan_for(s, 1);
-  const int pieces = p0.pieces > p1.pieces ? p0.pieces : p1.pieces;
-  return (size_t)pieces * s.B * s.Hq * 128 * (s.dh + 2) * sizeof(float);
+  size_t most = 0;
+  for (const AttnShape& k : kShapes)
+    for (int pair = 0; pair < 2; ++pair) {
+      const AttnPlan p = plan_for(s, pair, k);
+      const size_t b = (size_t)p.pieces * s.B * s.Hq * p.rb * (s.dh + 2) * sizeof(float);
+      most = b > most ? b : most;
+    }
+  return most;
+}
+
+template <int DH, int NST, int NWV>
+static void launch_fa(const AttnArgs& a, bool ch64, unsigned units, hipStream_t st) {
+  if (ch64)
+    hipLaunchKernelGGL((flash_attn_kernel<DH, NST, true, NWV>), dim3(units), dim3(64 * NWV), 0, st, a);
+  else
+    hipLaunchKernelGGL((flash_attn_kernel<DH, NST, false, NWV>), dim3(units), dim3(64 * NWV), 0, st, a);
+}
+
+template <int DH>
+static void launch_fa_shape(const AttnPlan& p, const AttnArgs& a, bool ch64, hipStream_t st) {
+  const unsigned units = (unsigned)p.units;
+  if (p.nwv == 4)
+    launch_fa<DH, 2, 4>(a, ch64, units, st);
+  else
+    launch_fa<DH, 3, 8>(a, ch64, units, st);
 }
 
 hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, uint16_t* o,
@@ -596,27 +663,20 @@ hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* 
   a.kv = kv_gathered;
   a.o = o;
   a.part_o = partial;
-  a.part_ml = partial + (size_t)p.pieces * s.B * s.Hq * 128 * s.dh;
+  a.part_ml = partial + (size_t)p.pieces * s.B * s.Hq * p.rb * s.dh;
   a.s = s;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.dh));
+  a.rb = p.rb;
   a.nrb = p.nrb;
   a.kt_max = p.kt_max;
   a.pair = p.pair;
-  dim3 grid((unsigned)p.units);
   // the whole-tile path addresses a tile's K and V rows with 31-bit offsets
   const int64_t kvd = (int64_t)s.Hkv_s * s.dh;
   const bool ch64 = s.c % 64 == 0 && ((int64_t)s.B * s.T * kvd + 64 * kvd) * 2 < ((int64_t)1 << 31);
-  if (s.dh == 128) {
-    if (ch64)
-      hipLaunchKernelGGL((flash_attn_kernel<128, 2, true>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((flash_attn_kernel<128, 2, false>), grid, dim3(256), 0, st, a);
-  } else {
-    if (ch64)
-      hipLaunchKernelGGL((flash_attn_kernel<64, 2, true>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((flash_attn_kernel<64, 2, false>), grid, dim3(256), 0, st, a);
-  }
+  if (s.dh == 128)
+    launch_fa_shape<128>(p, a, ch64, st);
+  else
+    launch_fa_shape<64>(p, a, ch64, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.pieces == 0) return e;
   const int64_t items = (int64_t)p.split_rows * s.B * s.Hq * (s.dh / 4);

@@ -55,12 +55,14 @@ hipError_t launch_f32_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t
 // the keys (plan below); `partial` holds the pieces' state
 // (attn_partial_bytes) and may be nullptr only when the plan has no pieces.
 struct AttnPlan {
-  int nrb;          // 128-row blocks per zigzag chunk
+  int nwv, nst;     // waves per block, depth of the K/V ring
+  int rb;           // rows per block (32 per wave)
+  int nrb;          // row blocks per zigzag chunk
   int kt_max;       // key tiles (64 keys) per piece at most
   int pair;         // 1: earlier-chunk blocks run inside their later-chunk partner's last piece
   int64_t units;    // work groups of the attention kernel
   int pieces;       // pieces of split blocks, summed over the block list
-  int split_rows;   // 128 x (number of split blocks)
+  int split_rows;   // rb x (number of split blocks)
 };
 AttnPlan attn_plan(const Shape& s);
 size_t attn_partial_bytes(const Shape& s);

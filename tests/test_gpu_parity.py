@@ -148,6 +148,18 @@ def test_attn_fwd_unpaired_plan(name, monkeypatch):
     _check_attn_fwd(name, f"attn_fwd {name} unpaired")
 
 
+# The attention kernel's other shape (the library's tuning variable): 8 waves
+# (256 query rows) per block sharing each K/V tile, 3 tiles in the LDS ring;
+# head_dim 64 and 128, whole-tile and per-row K/V addressing (chunks that are
+# not multiples of 64 keys).
+@pytest.mark.parametrize("shape", ["8x3"])
+@pytest.mark.parametrize("name", ["split_keys_dh128", "split_keys_gqa_b2", "gqa8_b2_c96", "c24_generic_reorder",
+                                  "wide_tiles_dh128"])
+def test_attn_fwd_block_shapes(name, shape, monkeypatch):
+    monkeypatch.setenv("TSP_ATTN_SHAPE", shape)
+    _check_attn_fwd(name, f"attn_fwd {name} shape={shape}")
+
+
 def _check_attn_fwd(name, case):
     shape, sigma, seed = _shape(name)
     d = dims_of(shape)
