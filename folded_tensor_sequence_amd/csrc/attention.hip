@@ -507,24 +507,28 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
 
 // Combines the pieces of every split block, in piece order:
 // O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p, m = max_p m_p.
-// One thread per (row, 4 head-dim columns).
+// One thread per (row, 4 head-dim columns).  A split block holds
+// B Hq rb DH / 4 items, a multiple of the 256-thread work group, so the
+// block is located from the work group's first item: that search is the same
+// for every lane (scalar), and only the item within the block is per lane.
 template <int DH>
 __global__ void attn_merge_kernel(AttnArgs a) {
   const Shape& s = a.s;
   const int per_bh = s.B * s.Hq;
-  const int cols = DH / 4;
-  int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // locate the split block this item belongs to
+  constexpr int cols = DH / 4;
+  int64_t wg_item = (int64_t)blockIdx.x * blockDim.x;
+  // locate the split block this work group belongs to
   int piece_base = 0;
+  const int64_t n = (int64_t)per_bh * a.rb * cols;
   for (int bi = 0; bi < 2 * a.nrb; ++bi) {
     const BlockGeo g = block_geo(s, a.rb, a.nrb, a.kt_max, a.pair, bi);
     if (g.ns <= 1) continue;
-    const int64_t n = (int64_t)per_bh * a.rb * cols;
-    if (item >= n) {
-      item -= n;
+    if (wg_item >= n) {
+      wg_item -= n;
       piece_base += g.ns;
       continue;
     }
+    const int64_t item = wg_item + threadIdx.x;
     const int c4 = (int)(item % cols);
     const int r = (int)((item / cols) % a.rb);
     const int bh = (int)(item / (cols * a.rb));
