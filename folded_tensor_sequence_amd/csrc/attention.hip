@@ -16,7 +16,9 @@
 // range exceeds kt_max tiles of 64 keys is cut into pieces along the keys
 // (each piece keeps its own max / sum / unnormalised output, merged
 // afterwards in piece order, so results are deterministic).  Units are
-// ordered heaviest block first.
+// ordered heaviest block first; when blocks are cut, each earlier-chunk block
+// runs inside the last key piece of a later-chunk partner, so the units weigh
+// about the same (block_geo).
 //
 // Per 64-key tile:
 //   S^T = K Q^T   (32x32x16 MFMA, K from LDS as the first operand, the wave's

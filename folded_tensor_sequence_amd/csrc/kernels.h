@@ -51,8 +51,8 @@ hipError_t launch_f32_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t
 
 // Causal flash attention of the rank's queries over the all-gathered K/V
 // (read in zigzag order through the position -> slot map, no reordered copy).
-// Blocks of 128 query rows whose key range is long are cut into pieces along
-// the keys (plan below); `partial` holds the pieces' state
+// Row blocks whose key range is long are cut into pieces along the keys
+// (plan below); `partial` holds the pieces' state
 // (attn_partial_bytes) and may be nullptr only when the plan has no pieces.
 struct AttnPlan {
   int nwv, nst;     // waves per block, depth of the K/V ring
