@@ -135,11 +135,11 @@ struct BlockGeo {
 __host__ __device__ inline BlockGeo block_rows(const Shape& s, int rbr, int nrb, int bi) {
   BlockGeo g;
   const int late = bi < nrb ? 1 : 0;
-  const int rb = nrb - 1 - (late ? bi : bi - nrb);
+  const int rbi = nrb - 1 - (late ? bi : bi - nrb);  // row block within the chunk
   g.row_begin = late * s.c;
   g.row_end = g.row_begin + s.c;
   g.gstart = (late ? (2 * s.D - 1 - s.r) : s.r) * s.c;
-  g.t0 = g.row_begin + rb * rbr;
+  g.t0 = g.row_begin + rbi * rbr;
   const int last = g.t0 + rbr - 1 < g.row_end ? g.t0 + rbr - 1 : g.row_end - 1;
   g.nkt = (g.gstart + (last - g.row_begin) + 64) / 64;
   g.ns = 1;
