@@ -46,6 +46,7 @@
 
 #include <type_traits>
 
+#include "attn_plan.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -120,59 +121,6 @@ __device__ __forceinline__ int64_t gathered_row(const Shape& s, int j, int sel, 
   return ((((int64_t)j * s.D + g) * 2 + sel) * s.B + b) * s.T + t;
 }
 
-// Block geometry shared by the attention and merge kernels and the host
-// plan.  Block index bi in [0, 2 nrb): the later chunk's blocks first, last
-// rows first.
-struct BlockGeo {
-  int row_begin, row_end;  // local rows of the chunk
-  int gstart;              // global position of the chunk's first row
-  int t0;                  // first local row of the block
-  int nkt;                 // key tiles the block needs
-  int ns;                  // pieces (0: the block runs inside its partner's last piece)
-  int tper;                // key tiles per piece (the last piece may hold fewer)
-};
-
-__host__ __device__ inline BlockGeo block_rows(const Shape& s, int rbr, int nrb, int bi) {
-  BlockGeo g;
-  const int late = bi < nrb ? 1 : 0;
-  const int rbi = nrb - 1 - (late ? bi : bi - nrb);  // row block within the chunk
-  g.row_begin = late * s.c;
-  g.row_end = g.row_begin + s.c;
-  g.gstart = (late ? (2 * s.D - 1 - s.r) : s.r) * s.c;
-  g.t0 = g.row_begin + rbi * rbr;
-  const int last = g.t0 + rbr - 1 < g.row_end ? g.t0 + rbr - 1 : g.row_end - 1;
-  g.nkt = (g.gstart + (last - g.row_begin) + 64) / 64;
-  g.ns = 1;
-  g.tper = g.nkt;
-  return g;
-}
-
-// Pieces along the keys.  Unpaired: every block is cut into pieces of at
-// most kt_max tiles.  Paired: the later-chunk block bi (heavy: its keys reach
-// back over both chunks) and the earlier-chunk block 2 nrb - 1 - bi (light)
-// share their work units: the heavy block's key range is cut so that its
-// last piece plus the whole light block weigh about as much as each other
-// piece, and the unit of that last piece then runs the light block too.
-__host__ __device__ inline BlockGeo block_geo(const Shape& s, int rbr, int nrb, int kt_max, int pair, int bi) {
-  BlockGeo g = block_rows(s, rbr, nrb, bi);
-  if (!pair) {
-    g.ns = (g.nkt + kt_max - 1) / kt_max;
-    g.tper = (g.nkt + g.ns - 1) / g.ns;
-  } else if (bi >= nrb) {
-    g.ns = 0;
-  } else {
-    const int tot = g.nkt + block_rows(s, rbr, nrb, 2 * nrb - 1 - bi).nkt;
-    int ns = (tot + kt_max - 1) / kt_max, tper = (tot + ns - 1) / ns;
-    while (ns > 1 && (ns - 1) * tper >= g.nkt) {  // the last piece keeps at least one heavy tile
-      --ns;
-      tper = (tot + ns - 1) / ns;
-    }
-    g.ns = ns;
-    g.tper = tper;
-  }
-  return g;
-}
-
 // CH64: chunks are whole multiples of 64 keys, so a key tile never straddles
 // two chunks and its gathered rows are consecutive (one address per tile).
 // NWV waves per block (block rows 32 NWV), NST-deep LDS ring of K/V tiles.
@@ -211,21 +159,14 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
 
   // ---- work unit -> (block, piece, sequence, q-head) --------------------
   const int per_bh = s.B * s.Hq;
-  int u = blockIdx.x, bi = 0, piece_base = 0;
-  BlockGeo g = block_geo(s, RBR, a.nrb, a.kt_max, a.pair, 0);
-  for (;;) {
-    const int n = g.ns * per_bh;
-    if (u < n || bi + 1 >= 2 * a.nrb) break;
-    u -= n;
-    if (g.ns > 1) piece_base += g.ns;
-    ++bi;
-    g = block_geo(s, RBR, a.nrb, a.kt_max, a.pair, bi);
-  }
-  const int piece = u / per_bh, bh = u - piece * per_bh;
+  const PlanKey pk{s.c, s.D, s.r, RBR, a.nrb, a.kt_max, a.pair};
+  const UnitPos up = unit_of(pk, per_bh, blockIdx.x);
+  BlockGeo g = up.g;
+  const int piece = up.piece, bh = up.bh, piece_base = up.piece_base;
   const int b = bh / s.Hq, qh = bh - b * s.Hq;
   // paired plan: the last piece of a later-chunk block also runs its
   // earlier-chunk partner block (whole, final output)
-  const int heavy_bi = bi;
+  const int heavy_bi = up.bi;
   const int nparts = a.pair && piece == g.ns - 1 ? 2 : 1;
 
   const int G = qh / (s.Hq / s.Hkv);
@@ -265,7 +206,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
   }
 
   for (int part = 0; part < nparts; ++part) {
-    if (part == 1) g = block_rows(s, RBR, a.nrb, 2 * a.nrb - 1 - heavy_bi);
+    if (part == 1) g = block_rows(s.c, s.D, s.r, RBR, a.nrb, 2 * a.nrb - 1 - heavy_bi);
     // split: this piece's partial state goes to the workspace for the merge
     const bool split = part == 0 && g.ns > 1;
     const int kt_begin = part == 0 ? piece * g.tper : 0;
@@ -518,48 +459,39 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   const Shape& s = a.s;
   const int per_bh = s.B * s.Hq;
   constexpr int cols = DH / 4;
-  int64_t wg_item = (int64_t)blockIdx.x * blockDim.x;
   // locate the split block this work group belongs to
-  int piece_base = 0;
-  const int64_t n = (int64_t)per_bh * a.rb * cols;
-  for (int bi = 0; bi < 2 * a.nrb; ++bi) {
-    const BlockGeo g = block_geo(s, a.rb, a.nrb, a.kt_max, a.pair, bi);
-    if (g.ns <= 1) continue;
-    if (wg_item >= n) {
-      wg_item -= n;
-      piece_base += g.ns;
-      continue;
-    }
-    const int64_t item = wg_item + threadIdx.x;
-    const int c4 = (int)(item % cols);
-    const int r = (int)((item / cols) % a.rb);
-    const int bh = (int)(item / (cols * a.rb));
-    const int t = g.t0 + r;
-    if (t >= g.row_end) return;
-    float mmax = -INFINITY;
-    for (int p = 0; p < g.ns; ++p) {
-      const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
-      mmax = fmaxf(mmax, a.part_ml[(pidx * 2 + 0) * a.rb + r]);
-    }
-    f32x4 acc{0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int p = 0; p < g.ns; ++p) {
-      const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
-      const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * a.rb + r] - mmax);
-      l += w * a.part_ml[(pidx * 2 + 1) * a.rb + r];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (pidx * a.rb + r) * DH + 4 * c4);
-      acc[0] += w * v[0];
-      acc[1] += w * v[1];
-      acc[2] += w * v[2];
-      acc[3] += w * v[3];
-    }
-    const float inv = 1.0f / l;
-    const int b = bh / s.Hq, qh = bh - b * s.Hq;
-    uint16_t* orow = a.o + ((int64_t)b * s.T + t) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH + 4 * c4;
-    u32x2 pk{pack_f16x2(acc[0] * inv, acc[1] * inv), pack_f16x2(acc[2] * inv, acc[3] * inv)};
-    *reinterpret_cast<u32x2*>(orow) = pk;
-    return;
+  const PlanKey plan{s.c, s.D, s.r, a.rb, a.nrb, a.kt_max, a.pair};
+  const MergePos mp = merge_block_of(plan, (long long)per_bh * a.rb * cols, (long long)blockIdx.x * blockDim.x);
+  if (mp.bi < 0) return;
+  const BlockGeo& g = mp.g;
+  const int64_t item = mp.item + threadIdx.x;
+  const int c4 = (int)(item % cols);
+  const int r = (int)((item / cols) % a.rb);
+  const int bh = (int)(item / (cols * a.rb));
+  const int t = g.t0 + r;
+  if (t >= g.row_end) return;
+  float mmax = -INFINITY;
+  for (int p = 0; p < g.ns; ++p) {
+    const int64_t pidx = (int64_t)(mp.piece_base + p) * per_bh + bh;
+    mmax = fmaxf(mmax, a.part_ml[(pidx * 2 + 0) * a.rb + r]);
   }
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int p = 0; p < g.ns; ++p) {
+    const int64_t pidx = (int64_t)(mp.piece_base + p) * per_bh + bh;
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * a.rb + r] - mmax);
+    l += w * a.part_ml[(pidx * 2 + 1) * a.rb + r];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (pidx * a.rb + r) * DH + 4 * c4);
+    acc[0] += w * v[0];
+    acc[1] += w * v[1];
+    acc[2] += w * v[2];
+    acc[3] += w * v[3];
+  }
+  const float inv = 1.0f / l;
+  const int b = bh / s.Hq, qh = bh - b * s.Hq;
+  uint16_t* orow = a.o + ((int64_t)b * s.T + t) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH + 4 * c4;
+  u32x2 pk{pack_f16x2(acc[0] * inv, acc[1] * inv), pack_f16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(orow) = pk;
 }
 
 // ---- host-side plan (shared with workspace sizing) -----------------------
@@ -584,49 +516,34 @@ static AttnShape attn_shape() {
   return kShapes[0];
 }
 
-// pair < 0: the default (paired whenever blocks are split).
+// pair < 0: the default (paired whenever blocks are split).  Blocks are
+// split when there are fewer than twice as many as resident work groups;
+// pieces then hold about tiles / (resident work groups) key tiles (tuning
+// overrides, no effect unless set: TSP_ATTN_PIECES=<target number of work
+// units>, TSP_ATTN_PAIR=0 to give the earlier chunk's blocks units of their
+// own).
 static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   AttnPlan p;
   p.nwv = k.nwv;
   p.nst = k.nst;
   p.rb = 32 * k.nwv;
-  p.nrb = (s.c + p.rb - 1) / p.rb;
-  const int64_t slots = k.nwv == 4 && k.nst == 2 ? 512 : 256;  // resident blocks on 256 CUs
-  const int64_t blocks = (int64_t)2 * p.nrb * s.B * s.Hq;
-  int64_t tiles = 0;
-  for (int bi = 0; bi < 2 * p.nrb; ++bi) tiles += block_rows(s, p.rb, p.nrb, bi).nkt;
-  tiles *= (int64_t)s.B * s.Hq;
-  // split only when there are too few blocks to fill the CUs twice over;
-  // pieces then hold about tiles / slots key tiles (tuning overrides, no
-  // effect unless set: TSP_ATTN_PIECES=<target number of work units>,
-  // TSP_ATTN_PAIR=0 to give the earlier chunk's blocks units of their own)
-  int64_t target = slots;
+  const long long slots = k.nwv == 4 && k.nst == 2 ? 512 : 256;  // resident blocks on 256 CUs
+  long long target = slots;
   if (const char* ev = getenv("TSP_ATTN_PIECES")) {
     if (atoi(ev) > 0) target = atoi(ev);
   }
-  if (blocks >= 2 * slots) {
-    p.kt_max = 1 << 30;
-    p.pair = 0;
-  } else {
-    int64_t kt = (tiles + target - 1) / target;
-    p.kt_max = (int)(kt < 16 ? 16 : kt);
-    if (pair < 0) {
-      const char* ev = getenv("TSP_ATTN_PAIR");
-      pair = (ev != nullptr && ev[0] == '0') ? 0 : 1;
-    }
-    p.pair = pair;
+  if (pair < 0) {
+    const char* ev = getenv("TSP_ATTN_PAIR");
+    pair = (ev != nullptr && ev[0] == '0') ? 0 : 1;
   }
-  p.units = 0;
-  p.pieces = 0;
-  p.split_rows = 0;
-  for (int bi = 0; bi < 2 * p.nrb; ++bi) {
-    const BlockGeo g = block_geo(s, p.rb, p.nrb, p.kt_max, p.pair, bi);
-    p.units += (int64_t)g.ns * s.B * s.Hq;
-    if (g.ns > 1) {
-      p.pieces += g.ns;
-      p.split_rows += p.rb;
-    }
-  }
+  const PlanKey key = plan_key(s.c, s.D, s.r, s.B, s.Hq, p.rb, slots, target, pair);
+  const PlanCounts n = plan_counts(key);
+  p.nrb = key.nrb;
+  p.kt_max = key.kt_max;
+  p.pair = key.pair;
+  p.units = n.units_per_bh * s.B * s.Hq;
+  p.pieces = n.pieces;
+  p.split_rows = n.split_rows;
   return p;
 }
 

@@ -1,0 +1,179 @@
+// Work plan of the attention kernels: which rows and key tiles each work
+// group processes.  Plain integer code shared by the attention kernel, the
+// merge kernel and the host plan, and compiled on its own by the host test
+// of the plan (so no HIP header is needed here).
+//
+// A rank holds two zigzag chunks of c rows each (Zyphra TSP article on
+// ai-trends.today, section "How to Fold a Book"): chunk r, whose queries see
+// keys [0, (r + 1) c), and chunk 2D-1-r, whose queries see keys up to
+// (2D - r) c.  Rows are grouped in blocks of rb rows; block index bi in
+// [0, 2 nrb) lists the later chunk's blocks first, last rows first.
+#pragma once
+
+#ifndef TSP_HD
+#define TSP_HD __host__ __device__
+#endif
+
+namespace tsp {
+
+struct BlockGeo {
+  int row_begin, row_end;  // local rows of the chunk
+  int gstart;              // global position of the chunk's first row
+  int t0;                  // first local row of the block
+  int nkt;                 // key tiles (64 keys) the block needs
+  int ns;                  // pieces (0: the block runs inside its partner's last piece)
+  int tper;                // key tiles per piece (the last piece may hold fewer)
+};
+
+// Rows and key range of block bi (chunk length c, degree D, rank r, rb rows
+// per block, nrb blocks per chunk), not cut into pieces.
+TSP_HD inline BlockGeo block_rows(int c, int D, int r, int rbr, int nrb, int bi) {
+  BlockGeo g;
+  const int late = bi < nrb ? 1 : 0;
+  const int rbi = nrb - 1 - (late ? bi : bi - nrb);  // row block within the chunk
+  g.row_begin = late * c;
+  g.row_end = g.row_begin + c;
+  g.gstart = (late ? (2 * D - 1 - r) : r) * c;
+  g.t0 = g.row_begin + rbi * rbr;
+  const int last = g.t0 + rbr - 1 < g.row_end ? g.t0 + rbr - 1 : g.row_end - 1;
+  g.nkt = (g.gstart + (last - g.row_begin) + 64) / 64;
+  g.ns = 1;
+  g.tper = g.nkt;
+  return g;
+}
+
+// Pieces along the keys.  Unpaired: every block is cut into pieces of at
+// most kt_max tiles.  Paired: the later-chunk block bi (heavy: its keys reach
+// back over both chunks) and the earlier-chunk block 2 nrb - 1 - bi (light)
+// share their work units: the heavy block's key range is cut so that its
+// last piece plus the whole light block weigh about as much as each other
+// piece, and the unit of that last piece then runs the light block too.
+TSP_HD inline BlockGeo block_geo(int c, int D, int r, int rbr, int nrb, int kt_max, int pair, int bi) {
+  BlockGeo g = block_rows(c, D, r, rbr, nrb, bi);
+  if (!pair) {
+    g.ns = (g.nkt + kt_max - 1) / kt_max;
+    g.tper = (g.nkt + g.ns - 1) / g.ns;
+  } else if (bi >= nrb) {
+    g.ns = 0;
+  } else {
+    const int tot = g.nkt + block_rows(c, D, r, rbr, nrb, 2 * nrb - 1 - bi).nkt;
+    int ns = (tot + kt_max - 1) / kt_max, tper = (tot + ns - 1) / ns;
+    while (ns > 1 && (ns - 1) * tper >= g.nkt) {  // the last piece keeps at least one heavy tile
+      --ns;
+      tper = (tot + ns - 1) / ns;
+    }
+    g.ns = ns;
+    g.tper = tper;
+  }
+  return g;
+}
+
+// Parameters that fix a plan.
+struct PlanKey {
+  int c, D, r, rbr, nrb, kt_max, pair;
+};
+
+// Work unit u of the attention kernel: block bi, key piece `piece` of
+// (sequence, q-head) pair bh; piece_base = pieces of the split blocks listed
+// before bi (the index of the block's first piece in the workspace).
+struct UnitPos {
+  BlockGeo g;
+  int bi, piece, bh, piece_base;
+};
+
+TSP_HD inline UnitPos unit_of(const PlanKey& k, int per_bh, int u) {
+  UnitPos p;
+  p.bi = 0;
+  p.piece_base = 0;
+  p.g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, 0);
+  for (;;) {
+    const int n = p.g.ns * per_bh;
+    if (u < n || p.bi + 1 >= 2 * k.nrb) break;
+    u -= n;
+    if (p.g.ns > 1) p.piece_base += p.g.ns;
+    ++p.bi;
+    p.g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, p.bi);
+  }
+  p.piece = u / per_bh;
+  p.bh = u - p.piece * per_bh;
+  return p;
+}
+
+// The split block (ns > 1) holding merge item `item` when every split block
+// holds items_per_block items: its geometry, index, first piece and the item
+// within it; bi = -1 past the last one.
+struct MergePos {
+  BlockGeo g;
+  int bi, piece_base;
+  long long item;
+};
+
+TSP_HD inline MergePos merge_block_of(const PlanKey& k, long long items_per_block, long long item) {
+  MergePos m;
+  m.piece_base = 0;
+  for (int bi = 0; bi < 2 * k.nrb; ++bi) {
+    const BlockGeo g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    if (g.ns <= 1) continue;
+    if (item >= items_per_block) {
+      item -= items_per_block;
+      m.piece_base += g.ns;
+      continue;
+    }
+    m.g = g;
+    m.bi = bi;
+    m.item = item;
+    return m;
+  }
+  m.bi = -1;
+  m.item = item;
+  return m;
+}
+
+// Whole-plan counts: work units per (sequence, q-head) pair, pieces of the
+// split blocks, rows of the split blocks.
+struct PlanCounts {
+  long long units_per_bh;
+  int pieces, split_rows;
+};
+
+TSP_HD inline PlanCounts plan_counts(const PlanKey& k) {
+  PlanCounts n{0, 0, 0};
+  for (int bi = 0; bi < 2 * k.nrb; ++bi) {
+    const BlockGeo g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    n.units_per_bh += g.ns;
+    if (g.ns > 1) {
+      n.pieces += g.ns;
+      n.split_rows += k.rbr;
+    }
+  }
+  return n;
+}
+
+// kt_max and pairing for a rank: blocks are split only when there are fewer
+// than 2 x slots of them (slots = work groups resident on the GPU at once);
+// pieces then hold about tiles / target key tiles (at least 16).  pair_req:
+// 0 or 1 when blocks are split (ignored otherwise).
+TSP_HD inline PlanKey plan_key(int c, int D, int r, int B, int Hq, int rbr, long long slots, long long target,
+                               int pair_req) {
+  PlanKey k;
+  k.c = c;
+  k.D = D;
+  k.r = r;
+  k.rbr = rbr;
+  k.nrb = (c + rbr - 1) / rbr;
+  const long long blocks = 2LL * k.nrb * B * Hq;
+  long long tiles = 0;
+  for (int bi = 0; bi < 2 * k.nrb; ++bi) tiles += block_rows(c, D, r, rbr, k.nrb, bi).nkt;
+  tiles *= (long long)B * Hq;
+  if (blocks >= 2 * slots) {
+    k.kt_max = 1 << 30;
+    k.pair = 0;
+  } else {
+    const long long kt = (tiles + target - 1) / target;
+    k.kt_max = (int)(kt < 16 ? 16 : kt);
+    k.pair = pair_req;
+  }
+  return k;
+}
+
+}  // namespace tsp

@@ -1,0 +1,115 @@
+// Host check of the attention work plan (folded_tensor_sequence_amd/csrc/
+// attn_plan.h, the code the attention and merge kernels run): for many rank
+// shapes, both row-block sizes and both pairings, every (row block, sequence
+// x q-head, key tile) is computed by exactly one work unit, every row of the
+// rank's two zigzag chunks lies in exactly one block, split pieces get
+// distinct workspace slots, and the merge kernel finds each split block with
+// the same first piece the attention units used.  Prints "ok <cases>" or the
+// first failure.
+#include <cstdio>
+#include <vector>
+
+#include "attn_plan.h"
+
+using namespace tsp;
+
+static int fail(const char* what, int B, int S, int D, int r, int Hq, int rbr, long long target, int pair) {
+  std::printf("FAIL %s: B=%d S=%d D=%d r=%d Hq=%d rb=%d target=%lld pair=%d\n", what, B, S, D, r, Hq, rbr, target,
+              pair);
+  return 1;
+}
+
+static int check(int B, int S, int D, int r, int Hq, int rbr, long long slots, long long target, int pair_req) {
+  const int c = S / (2 * D);
+  const PlanKey k = plan_key(c, D, r, B, Hq, rbr, slots, target, pair_req);
+  const PlanCounts n = plan_counts(k);
+  const int per_bh = B * Hq;
+  const int nb = 2 * k.nrb;
+#define FAIL(what) return fail(what, B, S, D, r, Hq, rbr, target, pair_req)
+  // rows: each of the 2c local rows in exactly one block
+  std::vector<int> row_seen(2 * c, 0);
+  int max_nkt = 0;
+  for (int bi = 0; bi < nb; ++bi) {
+    const BlockGeo g = block_rows(c, D, r, rbr, k.nrb, bi);
+    for (int t = g.t0; t < g.t0 + rbr && t < g.row_end; ++t) ++row_seen[t];
+    if (g.nkt > max_nkt) max_nkt = g.nkt;
+    // the key range covers the block's last row (position gstart + offset)
+    const int last = (g.t0 + rbr - 1 < g.row_end ? g.t0 + rbr - 1 : g.row_end - 1) - g.row_begin + g.gstart;
+    if (g.nkt * 64 <= last || (g.nkt - 1) * 64 > last) FAIL("key range");
+  }
+  for (int t = 0; t < 2 * c; ++t)
+    if (row_seen[t] != 1) FAIL("rows");
+  // units: every (block, bh, key tile) exactly once
+  std::vector<int> cover((size_t)nb * per_bh * max_nkt, 0);
+  std::vector<int> slot_used((size_t)(n.pieces > 0 ? n.pieces : 1) * per_bh, 0);
+  std::vector<int> first_piece(nb, -1);
+  const long long units = n.units_per_bh * per_bh;
+  for (long long u = 0; u < units; ++u) {
+    const UnitPos p = unit_of(k, per_bh, (int)u);
+    if (p.piece < 0 || p.piece >= p.g.ns || p.bh < 0 || p.bh >= per_bh) FAIL("unit decode");
+    if (p.g.ns > 1) {
+      if (first_piece[p.bi] < 0) first_piece[p.bi] = p.piece_base;
+      if (first_piece[p.bi] != p.piece_base) FAIL("piece base");
+    }
+    const int nparts = k.pair && p.piece == p.g.ns - 1 ? 2 : 1;
+    for (int part = 0; part < nparts; ++part) {
+      const int bi = part == 0 ? p.bi : nb - 1 - p.bi;
+      const BlockGeo g = part == 0 ? p.g : block_rows(c, D, r, rbr, k.nrb, bi);
+      const bool split = part == 0 && g.ns > 1;
+      const int kb = part == 0 ? p.piece * g.tper : 0;
+      const int ke = part == 0 ? (kb + g.tper < g.nkt ? kb + g.tper : g.nkt) : g.nkt;
+      if (kb >= ke) FAIL("empty piece");
+      for (int kt = kb; kt < ke; ++kt) ++cover[((size_t)bi * per_bh + p.bh) * max_nkt + kt];
+      if (split) {
+        const long long slot = (long long)(p.piece_base + p.piece) * per_bh + p.bh;
+        if (slot < 0 || slot >= (long long)n.pieces * per_bh) FAIL("piece slot range");
+        ++slot_used[slot];
+      }
+    }
+  }
+  for (int bi = 0; bi < nb; ++bi) {
+    const int nkt = block_rows(c, D, r, rbr, k.nrb, bi).nkt;
+    for (int bh = 0; bh < per_bh; ++bh)
+      for (int kt = 0; kt < max_nkt; ++kt)
+        if (cover[((size_t)bi * per_bh + bh) * max_nkt + kt] != (kt < nkt ? 1 : 0)) FAIL("tile coverage");
+  }
+  for (long long i = 0; i < (long long)n.pieces * per_bh; ++i)
+    if (slot_used[i] != 1) FAIL("piece slots");
+  // merge: work groups of 256 items, 32 items (4 head-dim columns each) per row
+  const long long ipb = (long long)per_bh * rbr * 32;
+  const long long total = (long long)n.split_rows * per_bh * 32;
+  for (long long item = 0; item < total; item += 256) {
+    const MergePos m = merge_block_of(k, ipb, item);
+    if (m.bi < 0 || m.g.ns <= 1 || m.piece_base != first_piece[m.bi]) FAIL("merge block");
+    if (m.item < 0 || m.item + 256 > ipb) FAIL("merge item");
+  }
+  if (merge_block_of(k, ipb, total).bi != -1) FAIL("merge end");
+#undef FAIL
+  return 0;
+}
+
+int main() {
+  struct Case {
+    int B, S, D, Hq;
+  };
+  // the test and benchmark shapes, plus a grid of small ones
+  std::vector<Case> cases = {{1, 256, 2, 4},     {1, 512, 4, 16},    {2, 384, 2, 16},   {1, 256, 4, 8},
+                             {1, 128, 1, 2},     {1, 16, 8, 8},      {1, 96, 2, 4},     {1, 1024, 2, 8},
+                             {2, 320, 2, 8},     {1, 4096, 2, 2},    {2, 2048, 2, 4},   {1, 8192, 8, 32},
+                             {2, 16384, 8, 32},  {1, 32768, 8, 64},  {1, 131072, 8, 32}};
+  for (int D = 1; D <= 8; D *= 2)
+    for (int c = 1; c <= 1200; c = c * 3 + 7)
+      for (int Hq = 1; Hq <= 16; Hq *= 4) cases.push_back({1 + (c & 1), 2 * D * c, D, Hq});
+  int checked = 0;
+  for (const Case& cs : cases)
+    for (int r = 0; r < cs.D; ++r)
+      for (int rbr : {128, 256})
+        for (long long target : {512LL, 256LL, 97LL, 2000LL})
+          for (int pair = 0; pair < 2; ++pair) {
+            const long long slots = rbr == 128 ? 512 : 256;
+            if (check(cs.B, cs.S, cs.D, r, cs.Hq, rbr, slots, target, pair)) return 1;
+            ++checked;
+          }
+  std::printf("ok %d\n", checked);
+  return 0;
+}
