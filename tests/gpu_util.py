@@ -30,6 +30,8 @@ SWEEP = {
     # key pieces and merges them
     "split_keys_dh128": (1, 4096, 2, 0, 128, 2, 2, 128, 256),
     "split_keys_gqa_b2": (2, 2048, 2, 1, 128, 4, 2, 64, 256),
+    # degree 8, a middle rank: both chunks split into key pieces and paired
+    "split_keys_d8_r5": (1, 8192, 8, 5, 128, 8, 8, 128, 256),
 }
 
 
