@@ -157,8 +157,8 @@ def main():
                          "reference for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one rank of a TSP axis on one GPU; runs on more than one GPU "
-              "are not part of this build (--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one rank of a TSP axis on one GPU; the library has no "
+              "multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -72,7 +72,7 @@ typedef struct {
 typedef enum {
   TSP_OK = 0,
   TSP_ERR_INVALID_ARG = -1, /* shape rule broken, NULL or misaligned pointer */
-  TSP_ERR_UNSUPPORTED = -2, /* valid TSP shape this build does not handle */
+  TSP_ERR_UNSUPPORTED = -2, /* valid TSP shape the library does not handle */
   TSP_ERR_WORKSPACE = -3,   /* ws too small (see tsp_workspace_bytes) */
   TSP_ERR_HIP = -4          /* HIP runtime error (no device, launch failure) */
 } tsp_status;
