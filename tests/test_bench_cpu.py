@@ -37,3 +37,18 @@ def test_recorded_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypat
     assert bench.recorded_traffic("w", "qkv") is None          # no record for that kernel
     src.write_text("kernel v2")
     assert bench.recorded_traffic("w", "gateup") is None       # counters predate the change
+
+
+def test_more_than_one_gpu_is_refused():
+    # the library computes one rank on one GPU: any other --gpus exits with
+    # status 2 and says so, before touching a GPU
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert out.returncode == 2
+    assert "--gpus must be 1" in out.stderr
+    assert out.stdout == ""
+
