@@ -251,11 +251,15 @@ def test_layer_fwd(name):
 
 # The alternative GEMM kernels: the direct-load ring kernel (the fallback when
 # operands need 64-bit offsets; its configuration is chosen here through the
-# library's tuning variables) and the staged kernel with two register sets.
+# library's tuning variables), the staged kernel with two register sets or
+# four waves, and split-K factors 2 and 3 for the output and down projections.
 ALT_GEMMS = {
     "ring": {"TSP_GEMM_QKV": "3", "TSP_GEMM_OPROJ": "3:2", "TSP_GEMM_DOWN": "3:2", "TSP_GEMM_GATEUP": "2"},
     "staged_two_sets": {"TSP_GEMM_OPROJ": "7:2", "TSP_GEMM_DOWN": "7:2", "TSP_GEMM_GATEUP": "4"},
     "staged_4wave": {"TSP_GEMM_QKV": "2", "TSP_GEMM_OPROJ": "1:2", "TSP_GEMM_DOWN": "1:2", "TSP_GEMM_GATEUP": "1"},
+    # split-K factors other than the plan's (small shapes plan 4)
+    "split_k_2": {"TSP_GEMM_OPROJ": "6:2", "TSP_GEMM_DOWN": "6:2"},
+    "split_k_3": {"TSP_GEMM_OPROJ": "6:3", "TSP_GEMM_DOWN": "6:3"},
 }
 
 
