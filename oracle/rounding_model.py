@@ -50,7 +50,7 @@ def rank_rows_rounded(inputs: dict, dims, b: int, rows, points=POINTS, kv=None, 
     R = (lambda name, a: f16(a) if name in points else a)
     B, S, D, r, h, Hq, Hkv, dh, F = orc._dims(dims)
     rows = np.asarray(rows, dtype=np.int64)
-    g = orc.local_to_global(S, D, r)[rows]
+    g = orc.local_to_global(S, D, r, orc._part(dims))[rows]
     if weights is None:
         weights = {n: orc.bf16_bits_to_f64(inputs[n]) for n in ("w_q", "w_o", "w_g", "w_u", "w_d")}
     n_keys = int(g.max()) + 1

@@ -35,6 +35,8 @@ Readings where the pages are silent (each one is listed in the design notes):
   * gated MLP = SwiGLU: (silu(x Wg^T) * (x Wu^T)) Wd^T, silu(z) = z/(1+e^-z);
   * zigzag: rank r holds chunks r and 2D-1-r of 2D equal chunks, local order
     chunk r first; GQA q-head i reads kv-head floor(i*Hkv/Hq);
+  * striped (the pages only name it beside zigzag): position g on rank
+    g mod D at local row g div D, token by token;
   * shard j = contiguous head group j (q-heads [j*Hq/D, (j+1)*Hq/D), kv-heads
     likewise) and MLP rows/cols [j*F/D, (j+1)*F/D);
   * ring order: at step s rank r uses MLP shard (r - s) mod D;
@@ -55,6 +57,8 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64",
+    "ZIGZAG",
+    "STRIPED",
     "local_to_global",
     "global_to_slot",
     "causal_pairs",
@@ -81,38 +85,48 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- #
-# Zigzag partition (TSP article, "How to Fold a Book": K/V are collected and
-# reordered with a zigzag partition to balance causal work; r007.github.io
+# Token partitions.
+# Zigzag (TSP article, "How to Fold a Book": K/V are collected and reordered
+# with a zigzag partition to balance causal work; r007.github.io
 # "Распределенное обучение", "Параллелизм по контексту: Ring Attention против
-# Ulysses", item 1: zigzag token partitions spread the causal tiles evenly).
-# Exact form: the sequence is cut into 2D equal chunks and rank r holds chunk
-# r followed by chunk 2D-1-r.
+# Ulysses", item 1: zigzag or striped token partitions spread the causal tiles
+# evenly).  Exact form: the sequence is cut into 2D equal chunks and rank r
+# holds chunk r followed by chunk 2D-1-r.
+# Striped (the other partition that passage names): position g belongs to
+# rank g mod D, as its local row g div D.
 # --------------------------------------------------------------------------- #
-def local_to_global(S: int, D: int, r: int) -> np.ndarray:
+ZIGZAG, STRIPED = 0, 1
+
+
+def local_to_global(S: int, D: int, r: int, partition: int = ZIGZAG) -> np.ndarray:
     """Global sequence position of each of rank r's S/D local rows."""
     if S % (2 * D) or not 0 <= r < D:
         raise ValueError("need S % 2D == 0 and 0 <= r < D")
+    if partition == STRIPED:
+        return np.array([t * D + r for t in range(S // D)], dtype=np.int64)
+    if partition != ZIGZAG:
+        raise ValueError(f"unknown partition {partition}")
     c = S // (2 * D)
     first = [r * c + i for i in range(c)]
     second = [(2 * D - 1 - r) * c + i for i in range(c)]
     return np.array(first + second, dtype=np.int64)
 
 
-def global_to_slot(S: int, D: int) -> np.ndarray:
+def global_to_slot(S: int, D: int, partition: int = ZIGZAG) -> np.ndarray:
     """For each global position g, its slot rank*(S/D) + local_row in a
     rank-major all-gathered buffer (inverse of the per-rank local_to_global)."""
     T = S // D
     slot = np.full(S, -1, dtype=np.int64)
     for r in range(D):
-        for t, g in enumerate(local_to_global(S, D, r)):
+        for t, g in enumerate(local_to_global(S, D, r, partition)):
             slot[g] = r * T + t
     return slot
 
 
-def causal_pairs(S: int, D: int, r: int) -> int:
+def causal_pairs(S: int, D: int, r: int, partition: int = ZIGZAG) -> int:
     """Number of causal (query, key) pairs, key <= query, for rank r's rows
     (brute-force count over the rows' global positions)."""
-    return int(sum(int(g) + 1 for g in local_to_global(S, D, r)))
+    return int(sum(int(g) + 1 for g in local_to_global(S, D, r, partition)))
 
 
 # --------------------------------------------------------------------------- #
@@ -173,6 +187,10 @@ def _dims(d):
             d.head_dim, d.ffn)
 
 
+def _part(d) -> int:
+    return getattr(d, "partition", ZIGZAG)
+
+
 def project_kv(inputs: dict, dims, b: int, n_keys: int, block: int = 4096):
     """K = X_b[:n_keys] W_k^T, V = X_b[:n_keys] W_v^T in float64."""
     w_k = bf16_bits_to_f64(inputs["w_k"])
@@ -198,7 +216,7 @@ def rank_rows_forward(inputs: dict, dims, b: int, rows: np.ndarray, kv=None,
     """
     B, S, D, r, h, Hq, Hkv, dh, F = _dims(dims)
     rows = np.asarray(rows, dtype=np.int64)
-    g = local_to_global(S, D, r)[rows]
+    g = local_to_global(S, D, r, _part(dims))[rows]
     if weights is None:
         weights = {n: bf16_bits_to_f64(inputs[n]) for n in ("w_q", "w_o", "w_g", "w_u", "w_d")}
     n_keys = int(g.max()) + 1
@@ -224,7 +242,7 @@ def qkv_rows(inputs: dict, dims, b: int, rows, rank=None) -> dict:
     """Q, K, V projections X W^T of local rows ``rows`` of sequence b on rank
     ``rank`` (default dims.rank), float64, unsharded head order."""
     r = dims.rank if rank is None else rank
-    g = local_to_global(dims.seq, dims.degree, r)[np.asarray(rows, dtype=np.int64)]
+    g = local_to_global(dims.seq, dims.degree, r, _part(dims))[np.asarray(rows, dtype=np.int64)]
     x = bf16_bits_to_f64(inputs["x"][b, g])
     return {n: x @ bf16_bits_to_f64(inputs["w_" + n]).T for n in ("q", "k", "v")}
 
@@ -265,8 +283,8 @@ def tsp_schedule(inputs: dict, dims) -> np.ndarray:
     w_q, w_k, w_v, w_o, w_g, w_u, w_d = (bf16_bits_to_f64(inputs[n]) for n in
                                          ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d"))
     x_all = bf16_bits_to_f64(inputs["x"])
-    l2g = [local_to_global(S, D, r) for r in range(D)]
-    slot = global_to_slot(S, D)
+    l2g = [local_to_global(S, D, r, _part(dims)) for r in range(D)]
+    slot = global_to_slot(S, D, _part(dims))
     x_loc = [x_all[:, l2g[r]] for r in range(D)]          # each [B][T][h]
     attn = [np.zeros((B, T, h)) for _ in range(D)]
     group = Hq // Hkv
@@ -277,7 +295,7 @@ def tsp_schedule(inputs: dict, dims) -> np.ndarray:
         wq_j, wk_j, wv_j = w_q[qrows], w_k[kvrows], w_v[kvrows]
         wo_j = w_o[:, qrows]
         q_j = [x_loc[r] @ wq_j.T for r in range(D)]
-        # all-gather: rank-major [D*T] per sequence, then zigzag reorder
+        # all-gather: rank-major [D*T] per sequence, then reorder to sequence order
         k_gath = np.concatenate([x_loc[r] @ wk_j.T for r in range(D)], axis=1)
         v_gath = np.concatenate([x_loc[r] @ wv_j.T for r in range(D)], axis=1)
         k_nat = k_gath[:, slot]
@@ -312,7 +330,7 @@ def tsp_schedule(inputs: dict, dims) -> np.ndarray:
 def algorithmic_flops(dims, rows_per_seq=None) -> dict:
     B, S, D, r, h, Hq, Hkv, dh, F = _dims(dims)
     T = S // D
-    g = local_to_global(S, D, r)
+    g = local_to_global(S, D, r, _part(dims))
     if rows_per_seq is not None:
         g = g[np.asarray(rows_per_seq)]
     m = B * len(g)

@@ -35,6 +35,7 @@ class Dims:
     n_kv_heads: int
     head_dim: int
     ffn: int
+    partition: int = 0  # token partition: 0 zigzag, 1 striped
 
     def astuple(self):
         return dataclasses.astuple(self)

@@ -7,6 +7,7 @@ term, a wrong sign or index, or a transposed operand in the oracle fails one of
 them.  CPU only.
 """
 import itertools
+import dataclasses
 import math
 import os
 
@@ -50,9 +51,9 @@ def test_generator_row_prefix_is_stable():
 # --------------------------------------------------------------------------- #
 # P1: zigzag maps
 # --------------------------------------------------------------------------- #
-def _golden_zigzag():
+def _golden_zigzag(name="zigzag_maps.txt"):
     l2g, g2s = {}, {}
-    with open(os.path.join(GOLDEN, "zigzag_maps.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -103,11 +104,42 @@ def test_zigzag_equal_causal_pairs(name):
         assert orc.causal_pairs(S, D, r) == want
 
 
+# Striped partition (the alternative to zigzag): golden maps written by hand,
+# permutation / inverse, and a closed form for the causal pairs, which are no
+# longer equal over ranks: rank r's row t sits at tD + r, so it has
+# D T (T - 1) / 2 + T (r + 1) pairs.
+def test_striped_golden():
+    l2g, g2s = _golden_zigzag("striped_maps.txt")
+    assert len(l2g) >= 6 and len(g2s) >= 2
+    for (S, D, r), want in l2g.items():
+        assert orc.local_to_global(S, D, r, orc.STRIPED).tolist() == want
+    for (S, D), want in g2s.items():
+        assert orc.global_to_slot(S, D, orc.STRIPED).tolist() == want
+
+
+@pytest.mark.parametrize("S,D", [(4, 1), (8, 2), (48, 3), (96, 8), (8192, 8)])
+def test_striped_is_permutation_and_inverse(S, D):
+    T = S // D
+    allg = np.concatenate([orc.local_to_global(S, D, r, orc.STRIPED) for r in range(D)])
+    assert sorted(allg.tolist()) == list(range(S))
+    slot = orc.global_to_slot(S, D, orc.STRIPED)
+    for r in range(D):
+        g = orc.local_to_global(S, D, r, orc.STRIPED)
+        assert slot[g].tolist() == list(range(r * T, (r + 1) * T))
+        assert orc.causal_pairs(S, D, r, orc.STRIPED) == D * T * (T - 1) // 2 + T * (r + 1)
+    # every rank's pairs sum to the whole causal triangle, as for zigzag
+    assert sum(orc.causal_pairs(S, D, r, orc.STRIPED) for r in range(D)) == S * (S + 1) // 2
+    if D == 1:
+        assert orc.local_to_global(S, 1, 0, orc.STRIPED).tolist() == list(range(S))
+
+
 def test_zigzag_rejects_bad_dims():
     with pytest.raises(ValueError):
         orc.local_to_global(10, 3, 0)
     with pytest.raises(ValueError):
         orc.local_to_global(16, 2, 2)
+    with pytest.raises(ValueError):
+        orc.local_to_global(16, 2, 0, partition=2)
 
 
 # --------------------------------------------------------------------------- #
@@ -306,13 +338,21 @@ def test_mlp_shard_sum_identity():
     (2, 48, 3, 0, 12, 6, 3, 4, 18),    # GQA 2:1, D=3, B=2
     (1, 64, 4, 0, 16, 8, 4, 4, 32),    # GQA, D=4
 ])
-def test_tsp_schedule_equals_unsharded_layer(shape):
+@pytest.mark.parametrize("partition", [0, 1], ids=["zigzag", "striped"])
+def test_tsp_schedule_equals_unsharded_layer(shape, partition):
     d0, inp = synth.make_custom(*shape, sigma=0.3, seed=31)
+    d0 = dataclasses.replace(d0, partition=partition)
     ys = orc.tsp_schedule(inp, d0)
     for r in range(d0.degree):
-        d = synth.Dims(*(list(shape[:3]) + [r] + list(shape[4:])))
+        d = dataclasses.replace(d0, rank=r)
         ref = orc.layer_rank_rows(inp, d)["y"]
         np.testing.assert_allclose(ys[r], ref, rtol=1e-12, atol=1e-12)
+        # the rank's rows are the unsharded layer's rows at its positions:
+        # slicing the full-sequence result by the partition map gives them too
+        if r == 0:
+            full = orc.layer_rank_rows(inp, dataclasses.replace(d0, degree=1, rank=0))["y"]
+            np.testing.assert_allclose(ys[r], full[:, orc.local_to_global(d0.seq, d0.degree, 0, partition)],
+                                       rtol=1e-12, atol=1e-12)
 
 
 def test_rows_subset_equals_full_slice():
