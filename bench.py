@@ -18,6 +18,7 @@ not counted).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -34,18 +35,32 @@ PEAK_HBM_GBS = 8000.0
 KERNELS = ("qkv", "attn", "oproj", "gateup", "down")
 
 
+def rank_pairs(d):
+    """Causal (query, key) pairs of one sequence on rank d.rank: the sum over
+    its rows of (position + 1).  Zigzag chunks r and 2D-1-r (c tokens each)
+    give c^2 (2D-1) + c (c+1), the same on every rank (the load balance the
+    zigzag split exists for); striped rows tD + r give D T (T-1)/2 + T (r+1)."""
+    T, c, D, r = d.seq // d.degree, d.seq // (2 * d.degree), d.degree, d.rank
+    if getattr(d, "partition", 0) == 1:
+        return D * T * (T - 1) // 2 + T * (r + 1)
+    return c * c * (2 * D - 1) + c * (c + 1)
+
+
+def rank_kmax(d):
+    """One past the largest position rank d.rank attends to."""
+    T, c, D, r = d.seq // d.degree, d.seq // (2 * d.degree), d.degree, d.rank
+    return (T - 1) * D + r + 1 if getattr(d, "partition", 0) == 1 else (2 * D - r) * c
+
+
 def layer_flops(d):
     """Algorithmic FLOPs of one rank's layer forward, per part.
 
     GEMMs count 2*M*N*K.  Attention counts 4*dh per (query, key) pair per
-    query head over the causal pairs of the rank's rows: a rank holding
-    zigzag chunks r and 2D-1-r (c tokens each) sees, per sequence,
-    sum over its rows of (position + 1) = c^2 (2D-1) + c (c+1) pairs, the
-    same count on every rank (the load balance the zigzag split exists for).
+    query head over the causal pairs of the rank's rows (rank_pairs).
     """
-    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
+    T = d.seq // d.degree
     m = d.batch * T
-    pairs = d.batch * (c * c * (2 * d.degree - 1) + c * (c + 1))
+    pairs = d.batch * rank_pairs(d)
     qkv = 2.0 * m * (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim * d.hidden
     o = 2.0 * m * d.n_q_heads * d.head_dim * d.hidden
     attn = 4.0 * d.head_dim * d.n_q_heads * pairs
@@ -56,8 +71,7 @@ def layer_flops(d):
 def kernel_work(d):
     """Algorithmic work per launch of each kernel: (amount, unit, bound)."""
     f = layer_flops(d)
-    c = d.seq // (2 * d.degree)
-    kmax = (2 * d.degree - d.rank) * c
+    kmax = rank_kmax(d)
     reorder_bytes = 2 * 2 * d.n_kv_heads * d.batch * kmax * d.head_dim * 2  # K,V x (read + write)
     return {
         "qkv": (f["qkv"], "flop", "mfma"),
@@ -95,7 +109,7 @@ def recorded_traffic(workload, kernel):
     return rec["traffic_bytes_per_launch"]
 
 
-def cpu_baseline(wl, inp, target_s: float, max_rows: int):
+def cpu_baseline(d, inp, target_s: float, max_rows: int):
     """Times the oracle (float64 numpy, host cores) on a sample of the rank's rows:
     own Q/K/V projection, attention over the full causal prefix, output
     projection and MLP.  The K/V of all keys is computed before the clock
@@ -105,18 +119,17 @@ def cpu_baseline(wl, inp, target_s: float, max_rows: int):
 
     from oracle import tsp_oracle as orc
 
-    d = wl.dims
     cores = len(os.sched_getaffinity(0))
     T, c = d.seq // d.degree, d.seq // (2 * d.degree)
     with threadpool_limits(limits=cores):
-        kmax = (2 * d.degree - d.rank) * c
+        kmax = rank_kmax(d)
         kv = orc.project_kv(inp, d, 0, kmax)
         w = {n: orc.bf16_bits_to_f64(inp[n]) for n in ("w_q", "w_o", "w_g", "w_u", "w_d")}
         w_k, w_v = orc.bf16_bits_to_f64(inp["w_k"]), orc.bf16_bits_to_f64(inp["w_v"])
 
         def run(rows):
             t0 = time.perf_counter()
-            g = orc.local_to_global(d.seq, d.degree, d.rank)[rows]
+            g = orc.local_to_global(d.seq, d.degree, d.rank, d.partition)[rows]
             x = orc.bf16_bits_to_f64(inp["x"][0, g])
             _ = x @ w_k.T, x @ w_v.T          # own K/V projection of these rows
             orc.rank_rows_forward(inp, d, 0, rows, kv=kv, weights=w)
@@ -124,7 +137,7 @@ def cpu_baseline(wl, inp, target_s: float, max_rows: int):
 
         rng = np.random.default_rng(1234)
 
-        def sample(n):  # half from each zigzag chunk, seeded
+        def sample(n):  # half from each half of the rank's rows, seeded
             n1 = max(1, n // 2)
             a = np.sort(rng.choice(c, size=min(n1, c), replace=False))
             b = np.sort(c + rng.choice(c, size=min(n - n1, c), replace=False))
@@ -138,7 +151,7 @@ def cpu_baseline(wl, inp, target_s: float, max_rows: int):
     fl = orc.algorithmic_flops(d, rows_per_seq=rows)["total"]
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "tokens_per_s": len(rows) / dt, "seconds": dt,
-            "sample": f"{len(rows)} of the rank's {T} rows (seeded, half per zigzag chunk) of "
+            "sample": f"{len(rows)} of the rank's {T} rows (seeded, half per half of its rows) of "
                       f"sequence 0, float64 numpy/OpenBLAS on {cores} host threads; K/V of all "
                       f"{kmax} keys precomputed before timing"}
 
@@ -149,6 +162,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_s8k_d8")
+    ap.add_argument("--partition", choices=["zigzag", "striped"], default="zigzag",
+                    help="token partition of the sequence over the TSP ranks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -168,7 +183,7 @@ def main():
     from folded_tensor_sequence_amd.harness import RankProblem
 
     wl = synth.WORKLOADS[args.workload]
-    d = wl.dims
+    d = dataclasses.replace(wl.dims, partition=1 if args.partition == "striped" else 0)
     torch.cuda.set_device(0)
     print(f"[bench] building {wl.name}: {wl.about}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(d, wl.sigma, wl.seed)
@@ -240,7 +255,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,sigma^2) bf16 weights)",
         "config": {"workload": wl.name, "batch": d.batch, "seq_len": d.seq, "degree": d.degree,
                    "rank": d.rank, "hidden": d.hidden, "q_heads": d.n_q_heads, "kv_heads": d.n_kv_heads,
-                   "head_dim": d.head_dim, "ffn": d.ffn, "rank_tokens": M},
+                   "head_dim": d.head_dim, "ffn": d.ffn, "rank_tokens": M, "partition": args.partition},
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
         "pct_of_bf16_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
         "gflop_per_step": round(total_flop / 1e9, 2),
@@ -267,7 +282,8 @@ def main():
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(re_bytes / re_s / 1e9 / PEAK_HBM_GBS, 4)}
     del nat
-    out["roofline"]["traffic"] = recorded_traffic(wl.name, dominant)
+    # HBM byte counters were recorded for the zigzag runs only
+    out["roofline"]["traffic"] = recorded_traffic(wl.name, dominant) if d.partition == 0 else None
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -279,7 +295,7 @@ def main():
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         del prob
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, max_rows=d.seq // d.degree)
+        out["cpu_baseline"] = cpu_baseline(d, inp, args.cpu_seconds, max_rows=d.seq // d.degree)
     print(json.dumps(out), flush=True)
 
 

@@ -36,7 +36,8 @@ EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd"
 
 class TspDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "seq", "degree", "rank", "hidden",
-                                               "n_q_heads", "n_kv_heads", "head_dim", "ffn")]
+                                               "n_q_heads", "n_kv_heads", "head_dim", "ffn",
+                                               "partition")]
 
 
 class TspError(RuntimeError):
@@ -87,7 +88,8 @@ def dims_struct(dims) -> TspDims:
     if isinstance(dims, TspDims):
         return dims
     return TspDims(dims.batch, dims.seq, dims.degree, dims.rank, dims.hidden,
-                   dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn)
+                   dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn,
+                   getattr(dims, "partition", 0))
 
 
 def _p(t):

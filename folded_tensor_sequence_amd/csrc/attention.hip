@@ -1,5 +1,5 @@
-// Causal flash attention of one rank's zigzag queries over the natural-order
-// K/V (gfx950, f16 matrix cores, float32 online softmax).
+// Causal flash attention of one rank's queries over the natural-order K/V
+// (gfx950, f16 matrix cores, float32 online softmax).
 //
 // Zyphra TSP article on ai-trends.today, section "How to Fold a Book": after
 // the all-gather and the zigzag reorder, every rank runs attention of its own
@@ -10,15 +10,15 @@
 // so the S x S score matrix is never stored.
 //
 // Work: a block is 32 x (waves per block) consecutive local rows of one
-// zigzag chunk for one (sequence, q-head), 32 query rows per wave; its waves
-// share every K/V tile loaded into LDS.  The rank's later chunk sees a key
-// prefix up to 2D-1 times longer than its earlier one, so a block whose key
-// range exceeds kt_max tiles of 64 keys is cut into pieces along the keys
-// (each piece keeps its own max / sum / unnormalised output, merged
-// afterwards in piece order, so results are deterministic).  Units are
-// ordered heaviest block first; when blocks are cut, each earlier-chunk block
-// runs inside the last key piece of a later-chunk partner, so the units weigh
-// about the same (block_geo).
+// half of the rank's rows (a zigzag chunk, or half of the striped rows) for
+// one (sequence, q-head), 32 query rows per wave; its waves share every K/V
+// tile loaded into LDS.  With zigzag the later chunk sees a key prefix up to
+// 2D-1 times longer than the earlier one, so a block whose key range exceeds
+// kt_max tiles of 64 keys is cut into pieces along the keys (each piece keeps
+// its own max / sum / unnormalised output, merged afterwards in piece order,
+// so results are deterministic).  Units are ordered heaviest block first;
+// when blocks are cut, each earlier-half block runs inside the last key piece
+// of a later-half partner, so the units weigh about the same (block_geo).
 //
 // Per 64-key tile:
 //   S^T = K Q^T   (32x32x16 MFMA, K from LDS as the first operand, the wave's
@@ -34,9 +34,10 @@
 //   column), two of which give a lane its 8 keys.
 //   O^T += V^T P  (32x32x16 MFMA, probabilities rounded to f16).
 // K and V tiles are copied global -> LDS with 16-byte direct loads into an
-// NST-deep ring, straight from the all-gathered K/V slots: the zigzag map
-// (position p -> chunk p / c -> source rank and local row) is applied to the
-// row addresses, so no reordered copy of K/V is made.  The barrier between
+// NST-deep ring, straight from the all-gathered K/V slots: the partition's
+// map (zigzag: position p -> chunk p / c -> source rank and local row;
+// striped: rank p mod D, row p div D) is applied to the row addresses, so no
+// reordered copy of K/V is made.  The barrier between
 // tiles carries no memory fence, so the loads of later tiles stay in flight
 // across it.
 #include <math.h>
@@ -44,7 +45,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <functional>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 #include "attn_plan.h"
 #include "common.h"
@@ -111,20 +115,35 @@ __device__ __forceinline__ float pair_sum(float x) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// Row of the all-gathered K/V buffer holding global position p (zigzag map:
-// chunk q = p / c lives on rank q (q < D) or 2D-1-q, at local row
-// p mod c (+ c for the later chunk)).
+// Row of the all-gathered K/V buffer holding global position p.  Zigzag:
+// chunk q = p / c lives on rank q (q < D) or 2D-1-q, at local row p mod c
+// (+ c for the later chunk).  Striped: rank p mod D, local row p div D.
 __device__ __forceinline__ int64_t gathered_row(const Shape& s, int j, int sel, int b, int p) {
-  const int qc = p / s.c;
-  const int g = qc < s.D ? qc : 2 * s.D - 1 - qc;
-  const int t = (qc < s.D ? 0 : s.c) + (p - qc * s.c);
+  int g, t;
+  if (s.part == 1) {
+    g = p % s.D;
+    t = p / s.D;
+  } else {
+    const int qc = p / s.c;
+    g = qc < s.D ? qc : 2 * s.D - 1 - qc;
+    t = (qc < s.D ? 0 : s.c) + (p - qc * s.c);
+  }
   return ((((int64_t)j * s.D + g) * 2 + sel) * s.B + b) * s.T + t;
 }
 
-// CH64: chunks are whole multiples of 64 keys, so a key tile never straddles
-// two chunks and its gathered rows are consecutive (one address per tile).
+// K/V tile addressing (KM):
+//   KM_ROW    any shape: every lane maps its own key through gathered_row;
+//   KM_CHUNK  zigzag with chunks a whole multiple of 64 keys: a key tile
+//             never straddles two chunks, so its gathered rows are
+//             consecutive (one address per tile, fixed lane offsets);
+//   KM_STRIPE striped with D dividing 64 and S a multiple of 64: key
+//             key0 + k sits on rank k mod D (key0 is a multiple of D) at row
+//             key0 / D + k div D, so every lane keeps a fixed offset from the
+//             tile's row key0 / D of rank 0.
+enum { KM_ROW = 0, KM_CHUNK = 1, KM_STRIPE = 2 };
+
 // NWV waves per block (block rows 32 NWV), NST-deep LDS ring of K/V tiles.
-template <int DH, int NST, bool CH64, int NWV>
+template <int DH, int NST, int KM, int NWV>
 __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_attn_kernel(AttnArgs a) {
   constexpr int BN = 64;
   constexpr int KROW = DH * 2;
@@ -159,7 +178,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
 
   // ---- work unit -> (block, piece, sequence, q-head) --------------------
   const int per_bh = s.B * s.Hq;
-  const PlanKey pk{s.c, s.D, s.r, RBR, a.nrb, a.kt_max, a.pair};
+  const PlanKey pk{s.c, s.D, s.r, s.part, RBR, a.nrb, a.kt_max, a.pair};
   const UnitPos up = unit_of(pk, per_bh, blockIdx.x);
   BlockGeo g = up.g;
   const int piece = up.piece, bh = up.bh, piece_base = up.piece_base;
@@ -193,20 +212,23 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
       lcol[i] = (4 * ((slot >> 2) ^ vswz<DH>(row)) + (slot & 3)) * 8;
     }
   }
-  // CH64: byte offset of each lane's 16 bytes from the tile's first K row
-  // (V rows sit v_step elements further), the same for every tile; the
-  // host checks that they fit in 31 bits.  The tile cursor (chunk kq, key
-  // kr within it) advances by one tile per issue, as issue() is called for
-  // consecutive tiles.
+  // KM_CHUNK / KM_STRIPE: byte offset of each lane's 16 bytes from the
+  // tile's base row (V rows sit v_step elements further), the same for every
+  // tile; the host checks that they fit in 31 bits.  KM_CHUNK: the tile
+  // cursor (chunk kq, key kr within it) advances by one tile per issue, as
+  // issue() is called for consecutive tiles.
+  const int64_t src_step = 2 * v_step;  // rank src -> src + 1, same rows
   uint32_t loff[QW];
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
     const int q = wave + NWV * i;
-    loff[i] = (uint32_t)(((q < K_INS ? 0 : v_step) + (int64_t)lkey[i] * kvd + lcol[i]) * 2);
+    const int64_t row_off = KM == KM_STRIPE ? (int64_t)(lkey[i] % s.D) * src_step + (int64_t)(lkey[i] / s.D) * kvd
+                                            : (int64_t)lkey[i] * kvd;
+    loff[i] = (uint32_t)(((q < K_INS ? 0 : v_step) + row_off + lcol[i]) * 2);
   }
 
   for (int part = 0; part < nparts; ++part) {
-    if (part == 1) g = block_rows(s.c, s.D, s.r, RBR, a.nrb, 2 * a.nrb - 1 - heavy_bi);
+    if (part == 1) g = block_rows(s.c, s.D, s.r, s.part, RBR, a.nrb, 2 * a.nrb - 1 - heavy_bi);
     // split: this piece's partial state goes to the workspace for the merge
     const bool split = part == 0 && g.ns > 1;
     const int kt_begin = part == 0 ? piece * g.tper : 0;
@@ -216,10 +238,10 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
     int t_lane = wt0 + lrow;
     const bool lane_valid = t_lane < g.row_end;
     t_lane = lane_valid ? t_lane : g.row_end - 1;
-    const int qpos = g.gstart + (t_lane - g.row_begin);
+    const int qpos = g.gstart + (t_lane - g.row_begin) * g.pstride;
     const int w_last = (wt0 + 31 < g.row_end ? wt0 + 31 : g.row_end - 1);
-    const int wave_maxpos = g.gstart + (w_last - g.row_begin);
-    const int wave_minpos = g.gstart + (wt0 - g.row_begin);
+    const int wave_maxpos = g.gstart + (w_last - g.row_begin) * g.pstride;
+    const int wave_minpos = g.gstart + (wt0 - g.row_begin) * g.pstride;
 
     // ---- Q fragments (second operand of S^T = K Q^T) ---------------------
     u32x4 qf[NKS];
@@ -233,7 +255,16 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
     auto issue = [&](int kt, int stage) {
       unsigned char* sb = smem + stage * STAGE;
       const int key0 = kt * BN;
-      if constexpr (CH64) {
+      if constexpr (KM == KM_STRIPE) {
+        const int64_t row0 = ((int64_t)jsh * s.D * 2 * s.B + b) * s.T + key0 / s.D;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.kv + row0 * kvd + head_off), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+          const int q = wave + NWV * i;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(sb + q * 1024), 16, (int)loff[i], 0, 0, 0);
+        }
+      } else if constexpr (KM == KM_CHUNK) {
         const int g_src = kq < s.D ? kq : 2 * s.D - 1 - kq;
         const int t = (kq < s.D ? 0 : s.c) + kr;
         const int64_t row0 = ((((int64_t)jsh * s.D + g_src) * 2) * s.B + b) * s.T + t;
@@ -460,7 +491,7 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   const int per_bh = s.B * s.Hq;
   constexpr int cols = DH / 4;
   // locate the split block this work group belongs to
-  const PlanKey plan{s.c, s.D, s.r, a.rb, a.nrb, a.kt_max, a.pair};
+  const PlanKey plan{s.c, s.D, s.r, s.part, a.rb, a.nrb, a.kt_max, a.pair};
   const MergePos mp = merge_block_of(plan, (long long)per_bh * a.rb * cols, (long long)blockIdx.x * blockDim.x);
   if (mp.bi < 0) return;
   const BlockGeo& g = mp.g;
@@ -516,12 +547,39 @@ static AttnShape attn_shape() {
   return kShapes[0];
 }
 
-// pair < 0: the default (paired whenever blocks are split).  Blocks are
-// split when there are fewer than twice as many as resident work groups;
-// pieces then hold about tiles / (resident work groups) key tiles (tuning
-// overrides, no effect unless set: TSP_ATTN_PIECES=<target number of work
-// units>, TSP_ATTN_PAIR=0 to give the earlier chunk's blocks units of their
-// own).
+// Estimated finishing time of a plan, in key tiles: units are handed out in
+// launch order to the first of `slots` resident work groups to become free;
+// a unit costs its key tiles plus kUnitCost (loading Q, writing the output
+// or the partial state, the merge).
+static long long plan_makespan(const PlanKey& k, int per_bh, long long slots) {
+  constexpr int kUnitCost = 2;
+  std::priority_queue<long long, std::vector<long long>, std::greater<long long>> q;
+  for (long long i = 0; i < slots; ++i) q.push(0);
+  long long end = 0;
+  for (int bi = 0; bi < 2 * k.nrb; ++bi) {
+    const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    for (int p = 0; p < g.ns; ++p) {
+      const int kb = p * g.tper, ke = kb + g.tper < g.nkt ? kb + g.tper : g.nkt;
+      int w = ke - kb + kUnitCost;
+      if (k.pair && p == g.ns - 1) w += block_rows(k.c, k.D, k.r, k.part, k.rbr, k.nrb, 2 * k.nrb - 1 - bi).nkt;
+      for (int bh = 0; bh < per_bh; ++bh) {
+        const long long t = q.top() + w;
+        q.pop();
+        q.push(t);
+        end = t > end ? t : end;
+      }
+    }
+  }
+  return end;
+}
+
+// pair < 0: the default.  Blocks are split when there are fewer than twice
+// as many as resident work groups; pieces then hold about tiles / (resident
+// work groups) key tiles, and the earlier half's blocks ride with the later
+// half's (paired) unless the makespan estimate says that separate units
+// finish sooner (when both halves see long key ranges: zigzag on the middle
+// and last ranks, striped).  Tuning overrides, no effect unless set:
+// TSP_ATTN_PIECES=<target number of work units>, TSP_ATTN_PAIR=0 or 1.
 static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   AttnPlan p;
   p.nwv = k.nwv;
@@ -534,9 +592,18 @@ static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   }
   if (pair < 0) {
     const char* ev = getenv("TSP_ATTN_PAIR");
-    pair = (ev != nullptr && ev[0] == '0') ? 0 : 1;
+    if (ev != nullptr && (ev[0] == '0' || ev[0] == '1')) {
+      pair = ev[0] - '0';
+    } else {
+      const PlanKey kp = plan_key(s.c, s.D, s.r, s.part, s.B, s.Hq, p.rb, slots, target, 1);
+      pair = 1;
+      if (kp.pair) {
+        const PlanKey ku = plan_key(s.c, s.D, s.r, s.part, s.B, s.Hq, p.rb, slots, target, 0);
+        if (plan_makespan(ku, s.B * s.Hq, slots) < plan_makespan(kp, s.B * s.Hq, slots)) pair = 0;
+      }
+    }
   }
-  const PlanKey key = plan_key(s.c, s.D, s.r, s.B, s.Hq, p.rb, slots, target, pair);
+  const PlanKey key = plan_key(s.c, s.D, s.r, s.part, s.B, s.Hq, p.rb, slots, target, pair);
   const PlanCounts n = plan_counts(key);
   p.nrb = key.nrb;
   p.kt_max = key.kt_max;
@@ -547,7 +614,34 @@ static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   return p;
 }
 
-AttnPlan attn_plan(const Shape& s) { return plan_for(s, -1, attn_shape()); }
+// The plan of the last shape asked for is kept, so that the makespan
+// estimate runs once per shape rather than on every launch.
+AttnPlan attn_plan(const Shape& s) {
+  static thread_local struct {
+    bool valid = false;
+    Shape s;
+    int nwv, nst;
+    char pair_env, pieces_env[16];
+    AttnPlan p;
+  } last;
+  const AttnShape k = attn_shape();
+  const char* pe = getenv("TSP_ATTN_PAIR");
+  const char* ne = getenv("TSP_ATTN_PIECES");
+  char pieces[16] = {0};
+  if (ne != nullptr) strncpy(pieces, ne, sizeof pieces - 1);
+  const char pair_env = pe != nullptr ? pe[0] : 0;
+  if (last.valid && memcmp(&last.s, &s, sizeof s) == 0 && last.nwv == k.nwv && last.nst == k.nst &&
+      last.pair_env == pair_env && memcmp(last.pieces_env, pieces, sizeof pieces) == 0)
+    return last.p;
+  last.p = plan_for(s, -1, k);
+  last.s = s;
+  last.nwv = k.nwv;
+  last.nst = k.nst;
+  last.pair_env = pair_env;
+  memcpy(last.pieces_env, pieces, sizeof pieces);
+  last.valid = true;
+  return last.p;
+}
 
 // Enough for every plan, so that a workspace sized once serves them all.
 size_t attn_partial_bytes(const Shape& s) {
@@ -562,20 +656,22 @@ size_t attn_partial_bytes(const Shape& s) {
 }
 
 template <int DH, int NST, int NWV>
-static void launch_fa(const AttnArgs& a, bool ch64, unsigned units, hipStream_t st) {
-  if (ch64)
-    hipLaunchKernelGGL((flash_attn_kernel<DH, NST, true, NWV>), dim3(units), dim3(64 * NWV), 0, st, a);
+static void launch_fa(const AttnArgs& a, int km, unsigned units, hipStream_t st) {
+  if (km == KM_CHUNK)
+    hipLaunchKernelGGL((flash_attn_kernel<DH, NST, KM_CHUNK, NWV>), dim3(units), dim3(64 * NWV), 0, st, a);
+  else if (km == KM_STRIPE)
+    hipLaunchKernelGGL((flash_attn_kernel<DH, NST, KM_STRIPE, NWV>), dim3(units), dim3(64 * NWV), 0, st, a);
   else
-    hipLaunchKernelGGL((flash_attn_kernel<DH, NST, false, NWV>), dim3(units), dim3(64 * NWV), 0, st, a);
+    hipLaunchKernelGGL((flash_attn_kernel<DH, NST, KM_ROW, NWV>), dim3(units), dim3(64 * NWV), 0, st, a);
 }
 
 template <int DH>
-static void launch_fa_shape(const AttnPlan& p, const AttnArgs& a, bool ch64, hipStream_t st) {
+static void launch_fa_shape(const AttnPlan& p, const AttnArgs& a, int km, hipStream_t st) {
   const unsigned units = (unsigned)p.units;
   if (p.nwv == 4)
-    launch_fa<DH, 2, 4>(a, ch64, units, st);
+    launch_fa<DH, 2, 4>(a, km, units, st);
   else
-    launch_fa<DH, 3, 8>(a, ch64, units, st);
+    launch_fa<DH, 3, 8>(a, km, units, st);
 }
 
 hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, uint16_t* o,
@@ -593,13 +689,19 @@ hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* 
   a.nrb = p.nrb;
   a.kt_max = p.kt_max;
   a.pair = p.pair;
-  // the whole-tile path addresses a tile's K and V rows with 31-bit offsets
+  // the whole-tile paths address a tile's K and V rows with 31-bit offsets
+  // (the largest: the V row of the last key, from the tile's base row)
   const int64_t kvd = (int64_t)s.Hkv_s * s.dh;
-  const bool ch64 = s.c % 64 == 0 && ((int64_t)s.B * s.T * kvd + 64 * kvd) * 2 < ((int64_t)1 << 31);
+  const int64_t v_step = (int64_t)s.B * s.T * kvd;
+  int km = KM_ROW;
+  if (s.part == 0 && s.c % 64 == 0 && (v_step + 64 * kvd) * 2 < ((int64_t)1 << 31)) km = KM_CHUNK;
+  if (s.part == 1 && 64 % s.D == 0 && s.S % 64 == 0 &&
+      (v_step + (int64_t)(s.D - 1) * 2 * v_step + (64 / s.D) * kvd) * 2 < ((int64_t)1 << 31))
+    km = KM_STRIPE;
   if (s.dh == 128)
-    launch_fa_shape<128>(p, a, ch64, st);
+    launch_fa_shape<128>(p, a, km, st);
   else
-    launch_fa_shape<64>(p, a, ch64, st);
+    launch_fa_shape<64>(p, a, km, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.pieces == 0) return e;
   const int64_t items = (int64_t)p.split_rows * s.B * s.Hq * (s.dh / 4);

@@ -3,11 +3,16 @@
 // merge kernel and the host plan, and compiled on its own by the host test
 // of the plan (so no HIP header is needed here).
 //
-// A rank holds two zigzag chunks of c rows each (Zyphra TSP article on
-// ai-trends.today, section "How to Fold a Book"): chunk r, whose queries see
-// keys [0, (r + 1) c), and chunk 2D-1-r, whose queries see keys up to
-// (2D - r) c.  Rows are grouped in blocks of rb rows; block index bi in
-// [0, 2 nrb) lists the later chunk's blocks first, last rows first.
+// A rank's T = 2c local rows form two halves of c rows.  Zigzag partition
+// (Zyphra TSP article on ai-trends.today, section "How to Fold a Book"): the
+// halves are chunk r, whose queries see keys [0, (r + 1) c), and chunk
+// 2D-1-r, whose queries see keys up to (2D - r) c; positions step by 1 along
+// a half.  Striped partition (r007.github.io "Распределенное обучение",
+// section "Параллелизм по контексту: Ring Attention против Ulysses", item 1,
+// names it beside zigzag): local row t sits at position tD + r, so positions
+// step by D and the second half sees the longer key prefixes.  Rows are
+// grouped in blocks of rb rows; block index bi in [0, 2 nrb) lists the later
+// half's blocks first, last rows first.
 #pragma once
 
 #ifndef TSP_HD
@@ -17,26 +22,34 @@
 namespace tsp {
 
 struct BlockGeo {
-  int row_begin, row_end;  // local rows of the chunk
-  int gstart;              // global position of the chunk's first row
+  int row_begin, row_end;  // local rows of the half
+  int gstart;              // global position of the half's first row
+  int pstride;             // position step from one local row to the next
   int t0;                  // first local row of the block
   int nkt;                 // key tiles (64 keys) the block needs
   int ns;                  // pieces (0: the block runs inside its partner's last piece)
   int tper;                // key tiles per piece (the last piece may hold fewer)
 };
 
-// Rows and key range of block bi (chunk length c, degree D, rank r, rb rows
-// per block, nrb blocks per chunk), not cut into pieces.
-TSP_HD inline BlockGeo block_rows(int c, int D, int r, int rbr, int nrb, int bi) {
+// Rows and key range of block bi (half length c, degree D, rank r,
+// partition part: 0 zigzag, 1 striped; rb rows per block, nrb blocks per
+// half), not cut into pieces.
+TSP_HD inline BlockGeo block_rows(int c, int D, int r, int part, int rbr, int nrb, int bi) {
   BlockGeo g;
   const int late = bi < nrb ? 1 : 0;
-  const int rbi = nrb - 1 - (late ? bi : bi - nrb);  // row block within the chunk
+  const int rbi = nrb - 1 - (late ? bi : bi - nrb);  // row block within the half
   g.row_begin = late * c;
   g.row_end = g.row_begin + c;
-  g.gstart = (late ? (2 * D - 1 - r) : r) * c;
+  if (part == 1) {
+    g.gstart = late * c * D + r;
+    g.pstride = D;
+  } else {
+    g.gstart = (late ? (2 * D - 1 - r) : r) * c;
+    g.pstride = 1;
+  }
   g.t0 = g.row_begin + rbi * rbr;
   const int last = g.t0 + rbr - 1 < g.row_end ? g.t0 + rbr - 1 : g.row_end - 1;
-  g.nkt = (g.gstart + (last - g.row_begin) + 64) / 64;
+  g.nkt = (g.gstart + (last - g.row_begin) * g.pstride + 64) / 64;
   g.ns = 1;
   g.tper = g.nkt;
   return g;
@@ -48,15 +61,15 @@ TSP_HD inline BlockGeo block_rows(int c, int D, int r, int rbr, int nrb, int bi)
 // share their work units: the heavy block's key range is cut so that its
 // last piece plus the whole light block weigh about as much as each other
 // piece, and the unit of that last piece then runs the light block too.
-TSP_HD inline BlockGeo block_geo(int c, int D, int r, int rbr, int nrb, int kt_max, int pair, int bi) {
-  BlockGeo g = block_rows(c, D, r, rbr, nrb, bi);
+TSP_HD inline BlockGeo block_geo(int c, int D, int r, int part, int rbr, int nrb, int kt_max, int pair, int bi) {
+  BlockGeo g = block_rows(c, D, r, part, rbr, nrb, bi);
   if (!pair) {
     g.ns = (g.nkt + kt_max - 1) / kt_max;
     g.tper = (g.nkt + g.ns - 1) / g.ns;
   } else if (bi >= nrb) {
     g.ns = 0;
   } else {
-    const int tot = g.nkt + block_rows(c, D, r, rbr, nrb, 2 * nrb - 1 - bi).nkt;
+    const int tot = g.nkt + block_rows(c, D, r, part, rbr, nrb, 2 * nrb - 1 - bi).nkt;
     int ns = (tot + kt_max - 1) / kt_max, tper = (tot + ns - 1) / ns;
     while (ns > 1 && (ns - 1) * tper >= g.nkt) {  // the last piece keeps at least one heavy tile
       --ns;
@@ -70,7 +83,7 @@ TSP_HD inline BlockGeo block_geo(int c, int D, int r, int rbr, int nrb, int kt_m
 
 // Parameters that fix a plan.
 struct PlanKey {
-  int c, D, r, rbr, nrb, kt_max, pair;
+  int c, D, r, part, rbr, nrb, kt_max, pair;
 };
 
 // Work unit u of the attention kernel: block bi, key piece `piece` of
@@ -85,14 +98,14 @@ TSP_HD inline UnitPos unit_of(const PlanKey& k, int per_bh, int u) {
   UnitPos p;
   p.bi = 0;
   p.piece_base = 0;
-  p.g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, 0);
+  p.g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, 0);
   for (;;) {
     const int n = p.g.ns * per_bh;
     if (u < n || p.bi + 1 >= 2 * k.nrb) break;
     u -= n;
     if (p.g.ns > 1) p.piece_base += p.g.ns;
     ++p.bi;
-    p.g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, p.bi);
+    p.g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, p.bi);
   }
   p.piece = u / per_bh;
   p.bh = u - p.piece * per_bh;
@@ -112,7 +125,7 @@ TSP_HD inline MergePos merge_block_of(const PlanKey& k, long long items_per_bloc
   MergePos m;
   m.piece_base = 0;
   for (int bi = 0; bi < 2 * k.nrb; ++bi) {
-    const BlockGeo g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
     if (g.ns <= 1) continue;
     if (item >= items_per_block) {
       item -= items_per_block;
@@ -139,7 +152,7 @@ struct PlanCounts {
 TSP_HD inline PlanCounts plan_counts(const PlanKey& k) {
   PlanCounts n{0, 0, 0};
   for (int bi = 0; bi < 2 * k.nrb; ++bi) {
-    const BlockGeo g = block_geo(k.c, k.D, k.r, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
     n.units_per_bh += g.ns;
     if (g.ns > 1) {
       n.pieces += g.ns;
@@ -153,17 +166,18 @@ TSP_HD inline PlanCounts plan_counts(const PlanKey& k) {
 // than 2 x slots of them (slots = work groups resident on the GPU at once);
 // pieces then hold about tiles / target key tiles (at least 16).  pair_req:
 // 0 or 1 when blocks are split (ignored otherwise).
-TSP_HD inline PlanKey plan_key(int c, int D, int r, int B, int Hq, int rbr, long long slots, long long target,
-                               int pair_req) {
+TSP_HD inline PlanKey plan_key(int c, int D, int r, int part, int B, int Hq, int rbr, long long slots,
+                               long long target, int pair_req) {
   PlanKey k;
   k.c = c;
   k.D = D;
   k.r = r;
+  k.part = part;
   k.rbr = rbr;
   k.nrb = (c + rbr - 1) / rbr;
   const long long blocks = 2LL * k.nrb * B * Hq;
   long long tiles = 0;
-  for (int bi = 0; bi < 2 * k.nrb; ++bi) tiles += block_rows(c, D, r, rbr, k.nrb, bi).nkt;
+  for (int bi = 0; bi < 2 * k.nrb; ++bi) tiles += block_rows(c, D, r, part, rbr, k.nrb, bi).nkt;
   tiles *= (long long)B * Hq;
   if (blocks >= 2 * slots) {
     k.kt_max = 1 << 30;

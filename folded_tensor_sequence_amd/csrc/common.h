@@ -23,6 +23,7 @@ constexpr int kWave = 64;
 // the host so kernels do no divisions they can avoid).
 struct Shape {
   int32_t B, S, D, r, h, Hq, Hkv, dh, F;
+  int32_t part;  // token partition: 0 zigzag, 1 striped
   int32_t T, c, M, Hq_s, Hkv_s, F_s, kmax, kmax_pad, nqkv_s;
 };
 

@@ -56,6 +56,8 @@ int make_shape(const tsp_dims_t* d, tsp::Shape* s) {
       (d->ffn / d->degree) % 8 != 0)
     return fail(TSP_ERR_INVALID_ARG,
                 "ffn %d must be a positive multiple of 64 with ffn/degree a multiple of 8", d->ffn);
+  if (d->partition != TSP_PARTITION_ZIGZAG && d->partition != TSP_PARTITION_STRIPED)
+    return fail(TSP_ERR_INVALID_ARG, "partition %d unknown (0 zigzag, 1 striped)", d->partition);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(TSP_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if ((int64_t)d->seq > kMaxDim || (int64_t)d->batch * d->seq / d->degree > kMaxDim ||
@@ -71,13 +73,14 @@ int make_shape(const tsp_dims_t* d, tsp::Shape* s) {
   x.Hkv = d->n_kv_heads;
   x.dh = d->head_dim;
   x.F = d->ffn;
+  x.part = d->partition;
   x.T = x.S / x.D;
   x.c = x.S / (2 * x.D);
   x.M = x.B * x.T;
   x.Hq_s = x.Hq / x.D;
   x.Hkv_s = x.Hkv / x.D;
   x.F_s = x.F / x.D;
-  x.kmax = (2 * x.D - x.r) * x.c;
+  x.kmax = x.part == TSP_PARTITION_STRIPED ? (x.T - 1) * x.D + x.r + 1 : (2 * x.D - x.r) * x.c;
   x.kmax_pad = (x.kmax + 63) / 64 * 64;
   x.nqkv_s = (x.Hq_s + 2 * x.Hkv_s) * x.dh;
   return TSP_OK;

@@ -1,11 +1,13 @@
-// Zigzag partition maps and the zigzag K/V reorder (gfx950).
+// Token partition maps and the K/V reorder into sequence order (gfx950).
 //
 // Zigzag partition (Zyphra TSP article on ai-trends.today, section "How to
 // Fold a Book": the gathered K/V are put back in sequence order with a zigzag
 // partition chosen to balance causal attention work across ranks;
 // r007.github.io "Распределенное обучение", section "Параллелизм по
 // контексту: Ring Attention против Ulysses", item 1): the S positions form 2D
-// chunks of c = S/(2D); rank r holds chunk r, then chunk 2D-1-r.
+// chunks of c = S/(2D); rank r holds chunk r, then chunk 2D-1-r.  Striped
+// partition (the alternative that item names): position g lives on rank
+// g mod D at local row g div D.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,10 +23,30 @@ __device__ __forceinline__ int32_t zz_global_to_slot(int32_t g, int32_t c, int32
   return q < D ? q * T + i : (2 * D - 1 - q) * T + c + i;
 }
 
+// Rank and local row of global position g under the shape's partition.
+__device__ __forceinline__ void part_owner(const Shape& s, int32_t g, int32_t& src, int32_t& t) {
+  if (s.part == 1) {
+    src = g % s.D;
+    t = g / s.D;
+  } else {
+    const int32_t q = g / s.c, i = g - q * s.c;
+    src = q < s.D ? q : 2 * s.D - 1 - q;
+    t = q < s.D ? i : s.c + i;
+  }
+}
+
 __global__ void zigzag_index_kernel(Shape s, int32_t* __restrict__ l2g, int32_t* __restrict__ g2s) {
   int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < s.T) l2g[i] = zz_local_to_global(i, s.c, s.D, s.r);
-  if (g2s != nullptr && i < s.S) g2s[i] = zz_global_to_slot(i, s.c, s.D, s.T);
+  if (i < s.T) l2g[i] = s.part == 1 ? i * s.D + s.r : zz_local_to_global(i, s.c, s.D, s.r);
+  if (g2s != nullptr && i < s.S) {
+    if (s.part == 1) {
+      int32_t src, t;
+      part_owner(s, i, src, t);
+      g2s[i] = src * s.T + t;
+    } else {
+      g2s[i] = zz_global_to_slot(i, s.c, s.D, s.T);
+    }
+  }
 }
 
 hipError_t launch_zigzag_index(const Shape& s, int32_t* l2g, int32_t* g2s, hipStream_t st) {
@@ -62,15 +84,15 @@ __global__ __launch_bounds__(8 * (DH / 8)) void kv_reorder_kernel(
   const int hk = G - j * s.Hkv_s;    // head within shard
   const int64_t row_elems = (int64_t)s.Hkv_s * DH;
 
-  // Source rows of the thread's 8 keys.  When c % 8 == 0 the 8 keys sit in
-  // one chunk at consecutive local rows (one address, fixed stride); the
-  // general path walks the chunk index key by key.
+  // Source rows of the thread's 8 keys.  Zigzag with c % 8 == 0: the 8 keys
+  // sit in one chunk at consecutive local rows (one address, fixed stride);
+  // otherwise each key's rank and row are computed on their own.
   const int g0 = tile * 64 + kc * 8;
   const uint16_t* col = gathered + (int64_t)hk * DH + dc * 8;
   const int64_t src_base = (((int64_t)j * s.D * 2 + kv) * s.B + b) * s.T;  // row of (src 0, t 0)
   const int64_t src_step = (int64_t)2 * s.B * s.T;                          // rows per src rank
   u32x4 v[8];
-  if (s.c % 8 == 0) {
+  if (s.part == 0 && s.c % 8 == 0) {
     if (g0 < s.kmax) {
       const int q = g0 / s.c, i = g0 - q * s.c;
       const int src = q < s.D ? q : 2 * s.D - 1 - q;
@@ -83,19 +105,14 @@ __global__ __launch_bounds__(8 * (DH / 8)) void kv_reorder_kernel(
       for (int e = 0; e < 8; ++e) v[e] = u32x4{0u, 0u, 0u, 0u};
     }
   } else {
-    int q = g0 / s.c, i = g0 - q * s.c;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (g0 + e < s.kmax) {
-        const int src = q < s.D ? q : 2 * s.D - 1 - q;
-        const int t = q < s.D ? i : s.c + i;
+        int src, t;
+        part_owner(s, g0 + e, src, t);
         v[e] = *reinterpret_cast<const u32x4*>(col + (src_base + src * src_step + t) * row_elems);
       } else {
         v[e] = u32x4{0u, 0u, 0u, 0u};
-      }
-      if (++i == s.c) {
-        i = 0;
-        ++q;
       }
     }
   }

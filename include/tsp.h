@@ -19,10 +19,15 @@
  * causal attention with scale 1/sqrt(head_dim) and keys k <= query q, no
  * normalisation, rotary embedding, bias or dropout.
  *
- * Zigzag partition: the sequence of S positions is cut into 2D chunks of
- * c = S/(2D); rank r holds chunk r then chunk 2D-1-r (local row order), i.e.
- * local row t has global position r*c + t for t < c and (2D-1-r)*c + (t-c)
- * otherwise.  GQA: q-head i reads kv-head floor(i*Hkv/Hq).  Shard j is head
+ * Token partitions (r007.github.io "Распределенное обучение", section
+ * "Параллелизм по контексту: Ring Attention против Ulysses", item 1, names
+ * zigzag and striped partitions as the ways to balance causal tiles):
+ *   zigzag (default, the one the TSP article uses): the sequence of S
+ *     positions is cut into 2D chunks of c = S/(2D); rank r holds chunk r then
+ *     chunk 2D-1-r (local row order), i.e. local row t has global position
+ *     r*c + t for t < c and (2D-1-r)*c + (t-c) otherwise;
+ *   striped: local row t of rank r has global position t*D + r (position g
+ *     lives on rank g mod D at row g div D).  GQA: q-head i reads kv-head floor(i*Hkv/Hq).  Shard j is head
  * group j: q-heads [j*Hq/D, (j+1)*Hq/D), kv-heads [j*Hkv/D, (j+1)*Hkv/D), and
  * MLP rows/columns [j*F/D, (j+1)*F/D).  The MLP ring at step s uses shard
  * (r - s) mod D.
@@ -61,13 +66,19 @@ extern "C" {
  *   n_q_heads  Hq, n_kv_heads Hkv:  Hq % D == 0, Hkv % D == 0, Hq % Hkv == 0
  *   head_dim   dh in {64, 128}
  *   ffn        F, F % 64 == 0 and (F/D) % 8 == 0
+ *   partition  TSP_PARTITION_ZIGZAG (0) or TSP_PARTITION_STRIPED (1); a
+ *              zero-initialised struct means zigzag
  * Derived: T = S/D local rows per sequence, c = S/(2D), M = B*T, F_s = F/D,
- *   kmax = (2D - r)*c (one past the largest position rank r attends to),
+ *   kmax = one past the largest position rank r attends to: (2D - r)*c for
+ *   zigzag, (T - 1)*D + r + 1 for striped;
  *   kmax_pad = kmax rounded up to a multiple of 64.
  */
 typedef struct {
   int32_t batch, seq, degree, rank, hidden, n_q_heads, n_kv_heads, head_dim, ffn;
+  int32_t partition;
 } tsp_dims_t;
+
+typedef enum { TSP_PARTITION_ZIGZAG = 0, TSP_PARTITION_STRIPED = 1 } tsp_partition;
 
 typedef enum {
   TSP_OK = 0,
@@ -86,10 +97,11 @@ typedef enum {
   TSP_FN_KV_GATHERED = 5 /* size of the kv_gathered buffer */
 } tsp_fn;
 
-/* Zigzag maps of the partition described above (TSP article, "How to Fold a
- * Book": K/V are reordered with a zigzag partition that balances causal work
- * across ranks; r007.github.io "Распределенное обучение", section
- * "Параллелизм по контексту: Ring Attention против Ulysses", item 1).
+/* Maps of the partition dims->partition selects, as described above (TSP
+ * article, "How to Fold a Book": K/V are reordered with a zigzag partition
+ * that balances causal work across ranks; r007.github.io "Распределенное
+ * обучение", section "Параллелизм по контексту: Ring Attention против
+ * Ulysses", item 1, for zigzag and striped partitions).
  *   local_to_global  int32 [T]: global position of rank dims->rank's row t.
  *   global_to_slot   int32 [S] or NULL: for each global position g, the slot
  *                    rank*T + t that holds it in a rank-major all-gather.
@@ -101,8 +113,8 @@ int tsp_zigzag_index(const tsp_dims_t* dims, int32_t* local_to_global,
  * to Fold a Book": each rank applies the broadcast W_Q/W_K/W_V of shard j to
  * its own tokens).  Computes X_src * W_qkv,j^T for every shard j with bf16
  * matrix cores and float32 accumulation, rounding results to f16.
- *   src_rank     rank whose tokens x_shard holds (its zigzag rows)
- *   x_shard      bf16 [B][T][h], local zigzag row order of src_rank
+ *   src_rank     rank whose tokens x_shard holds (its partition rows)
+ *   x_shard      bf16 [B][T][h], local row order of src_rank
  *   w_qkv        bf16 [D][(Hq/D + 2*Hkv/D)*dh][h]: shard j's rows are its
  *                Hq/D q-heads, then its Hkv/D k-heads, then its v-heads,
  *                dh rows each, in nn.Linear [out][in] order
@@ -117,8 +129,8 @@ int tsp_qkv_proj(const tsp_dims_t* dims, int32_t src_rank, const uint16_t* x_sha
                  const uint16_t* w_qkv, uint16_t* q_out, uint16_t* kv_gathered,
                  hipStream_t stream);
 
-/* Zigzag reorder of the gathered K/V into natural sequence order (TSP
- * article, "How to Fold a Book").  Bit-exact 16-bit copy of every key
+/* Reorder of the gathered K/V into natural sequence order through the
+ * partition's position -> slot map (TSP article, "How to Fold a Book").  Bit-exact 16-bit copy of every key
  * position g < kmax; the positions [kmax, kmax_pad) are zero-filled.
  *   kv_gathered  f16, layout of tsp_qkv_proj, all D_src slots filled
  *   kv_natural   f16, TSP_FN_KV_NATURAL bytes:
@@ -131,9 +143,10 @@ int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered,
 
 /* Attention half of the layer on rank dims->rank:
  *     out = x + sum_j O_j W_O,j^T,
- * O_j = causal attention of the rank's zigzag queries (q-heads of shard j)
- * over the K/V of shard j in natural sequence order (TSP article, "How to
- * Fold a Book"; the attention kernel applies the zigzag position -> slot map
+ * O_j = causal attention of the rank's queries (q-heads of shard j) at their
+ * partition positions over the K/V of shard j in natural sequence order (TSP
+ * article, "How to Fold a Book"; the attention kernel applies the partition's
+ * position -> slot map
  * while it loads K/V tiles from kv_gathered, so no reordered copy is made;
  * the head split with row-split output projection is exact:
  * bowenzhou.top "张量并行", section "机制：行切与列切").

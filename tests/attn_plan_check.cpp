@@ -1,11 +1,13 @@
 // Host check of the attention work plan (folded_tensor_sequence_amd/csrc/
 // attn_plan.h, the code the attention and merge kernels run): for many rank
-// shapes, both row-block sizes and both pairings, every (row block, sequence
-// x q-head, key tile) is computed by exactly one work unit, every row of the
-// rank's two zigzag chunks lies in exactly one block, split pieces get
-// distinct workspace slots, and the merge kernel finds each split block with
-// the same first piece the attention units used.  Prints "ok <cases>" or the
-// first failure.
+// shapes, both token partitions, both row-block sizes and both pairings,
+// every (row block, sequence x q-head, key tile) is computed by exactly one
+// work unit, every local row lies in exactly one block at the position the
+// partition gives it (written out here on its own), each block's key tiles
+// end with the tile of its last row's position, split pieces get distinct
+// workspace slots, and the merge kernel finds each split block with the same
+// first piece the attention units used.  Prints "ok <cases>" or the first
+// failure.
 #include <cstdio>
 #include <vector>
 
@@ -13,28 +15,43 @@
 
 using namespace tsp;
 
-static int fail(const char* what, int B, int S, int D, int r, int Hq, int rbr, long long target, int pair) {
-  std::printf("FAIL %s: B=%d S=%d D=%d r=%d Hq=%d rb=%d target=%lld pair=%d\n", what, B, S, D, r, Hq, rbr, target,
-              pair);
+static int fail(const char* what, int B, int S, int D, int r, int part, int Hq, int rbr, long long target,
+                int pair) {
+  std::printf("FAIL %s: B=%d S=%d D=%d r=%d part=%d Hq=%d rb=%d target=%lld pair=%d\n", what, B, S, D, r, part, Hq,
+              rbr, target, pair);
   return 1;
 }
 
-static int check(int B, int S, int D, int r, int Hq, int rbr, long long slots, long long target, int pair_req) {
+// Global position of local row t: zigzag (chunks r and 2D-1-r of length c)
+// or striped (t D + r).
+static int position(int c, int D, int r, int part, int t) {
+  if (part == 1) return t * D + r;
+  return t < c ? r * c + t : (2 * D - 1 - r) * c + (t - c);
+}
+
+static int check(int B, int S, int D, int r, int part, int Hq, int rbr, long long slots, long long target,
+                 int pair_req) {
   const int c = S / (2 * D);
-  const PlanKey k = plan_key(c, D, r, B, Hq, rbr, slots, target, pair_req);
+  const PlanKey k = plan_key(c, D, r, part, B, Hq, rbr, slots, target, pair_req);
   const PlanCounts n = plan_counts(k);
   const int per_bh = B * Hq;
   const int nb = 2 * k.nrb;
-#define FAIL(what) return fail(what, B, S, D, r, Hq, rbr, target, pair_req)
-  // rows: each of the 2c local rows in exactly one block
+#define FAIL(what) return fail(what, B, S, D, r, part, Hq, rbr, target, pair_req)
+  // rows: each of the 2c local rows in exactly one block, at its position
   std::vector<int> row_seen(2 * c, 0);
   int max_nkt = 0;
   for (int bi = 0; bi < nb; ++bi) {
-    const BlockGeo g = block_rows(c, D, r, rbr, k.nrb, bi);
-    for (int t = g.t0; t < g.t0 + rbr && t < g.row_end; ++t) ++row_seen[t];
+    const BlockGeo g = block_rows(c, D, r, part, rbr, k.nrb, bi);
+    int last = -1;
+    for (int t = g.t0; t < g.t0 + rbr && t < g.row_end; ++t) {
+      ++row_seen[t];
+      const int pos = g.gstart + (t - g.row_begin) * g.pstride;
+      if (pos != position(c, D, r, part, t)) FAIL("row position");
+      if (pos <= last) FAIL("positions not increasing");
+      last = pos;
+    }
     if (g.nkt > max_nkt) max_nkt = g.nkt;
-    // the key range covers the block's last row (position gstart + offset)
-    const int last = (g.t0 + rbr - 1 < g.row_end ? g.t0 + rbr - 1 : g.row_end - 1) - g.row_begin + g.gstart;
+    // the key tiles end with the tile holding the block's last position
     if (g.nkt * 64 <= last || (g.nkt - 1) * 64 > last) FAIL("key range");
   }
   for (int t = 0; t < 2 * c; ++t)
@@ -52,12 +69,12 @@ static int check(int B, int S, int D, int r, int Hq, int rbr, long long slots, l
       if (first_piece[p.bi] != p.piece_base) FAIL("piece base");
     }
     const int nparts = k.pair && p.piece == p.g.ns - 1 ? 2 : 1;
-    for (int part = 0; part < nparts; ++part) {
-      const int bi = part == 0 ? p.bi : nb - 1 - p.bi;
-      const BlockGeo g = part == 0 ? p.g : block_rows(c, D, r, rbr, k.nrb, bi);
-      const bool split = part == 0 && g.ns > 1;
-      const int kb = part == 0 ? p.piece * g.tper : 0;
-      const int ke = part == 0 ? (kb + g.tper < g.nkt ? kb + g.tper : g.nkt) : g.nkt;
+    for (int ipart = 0; ipart < nparts; ++ipart) {
+      const int bi = ipart == 0 ? p.bi : nb - 1 - p.bi;
+      const BlockGeo g = ipart == 0 ? p.g : block_rows(c, D, r, part, rbr, k.nrb, bi);
+      const bool split = ipart == 0 && g.ns > 1;
+      const int kb = ipart == 0 ? p.piece * g.tper : 0;
+      const int ke = ipart == 0 ? (kb + g.tper < g.nkt ? kb + g.tper : g.nkt) : g.nkt;
       if (kb >= ke) FAIL("empty piece");
       for (int kt = kb; kt < ke; ++kt) ++cover[((size_t)bi * per_bh + p.bh) * max_nkt + kt];
       if (split) {
@@ -68,7 +85,7 @@ static int check(int B, int S, int D, int r, int Hq, int rbr, long long slots, l
     }
   }
   for (int bi = 0; bi < nb; ++bi) {
-    const int nkt = block_rows(c, D, r, rbr, k.nrb, bi).nkt;
+    const int nkt = block_rows(c, D, r, part, rbr, k.nrb, bi).nkt;
     for (int bh = 0; bh < per_bh; ++bh)
       for (int kt = 0; kt < max_nkt; ++kt)
         if (cover[((size_t)bi * per_bh + bh) * max_nkt + kt] != (kt < nkt ? 1 : 0)) FAIL("tile coverage");
@@ -96,20 +113,22 @@ int main() {
   std::vector<Case> cases = {{1, 256, 2, 4},     {1, 512, 4, 16},    {2, 384, 2, 16},   {1, 256, 4, 8},
                              {1, 128, 1, 2},     {1, 16, 8, 8},      {1, 96, 2, 4},     {1, 1024, 2, 8},
                              {2, 320, 2, 8},     {1, 4096, 2, 2},    {2, 2048, 2, 4},   {1, 8192, 8, 32},
-                             {2, 16384, 8, 32},  {1, 32768, 8, 64},  {1, 131072, 8, 32}};
+                             {2, 16384, 8, 32},  {1, 32768, 8, 64},  {1, 131072, 8, 32}, {1, 384, 3, 6},
+                             {1, 600, 5, 5},     {2, 768, 6, 12},    {1, 4480, 7, 7}};
   for (int D = 1; D <= 8; D *= 2)
     for (int c = 1; c <= 1200; c = c * 3 + 7)
       for (int Hq = 1; Hq <= 16; Hq *= 4) cases.push_back({1 + (c & 1), 2 * D * c, D, Hq});
   int checked = 0;
   for (const Case& cs : cases)
     for (int r = 0; r < cs.D; ++r)
-      for (int rbr : {128, 256})
-        for (long long target : {512LL, 256LL, 97LL, 2000LL})
-          for (int pair = 0; pair < 2; ++pair) {
-            const long long slots = rbr == 128 ? 512 : 256;
-            if (check(cs.B, cs.S, cs.D, r, cs.Hq, rbr, slots, target, pair)) return 1;
-            ++checked;
-          }
+      for (int part = 0; part < 2; ++part)
+        for (int rbr : {128, 256})
+          for (long long target : {512LL, 256LL, 97LL, 2000LL})
+            for (int pair = 0; pair < 2; ++pair) {
+              const long long slots = rbr == 128 ? 512 : 256;
+              if (check(cs.B, cs.S, cs.D, r, part, cs.Hq, rbr, slots, target, pair)) return 1;
+              ++checked;
+            }
   std::printf("ok %d\n", checked);
   return 0;
 }

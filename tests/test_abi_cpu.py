@@ -71,6 +71,8 @@ MISALIGNED = ctypes.c_void_p(0x10008)
     (dict(ffn=64, degree=16, n_q_heads=16, n_kv_heads=16), B.TSP_ERR_INVALID_ARG, "ffn"),  # F/D = 4
     (dict(ffn=128, degree=3, seq=258, n_q_heads=6, n_kv_heads=3), B.TSP_ERR_INVALID_ARG, "ffn"),
     (dict(head_dim=96), B.TSP_ERR_UNSUPPORTED, "head_dim"),
+    (dict(partition=2), B.TSP_ERR_INVALID_ARG, "partition"),
+    (dict(partition=-1), B.TSP_ERR_INVALID_ARG, "partition"),
 ])
 def test_invalid_dims_rejected(lib, kw, code, frag):
     d = _dims(**kw)
@@ -172,3 +174,25 @@ def test_workspace_sizes_match_layout(lib, name):
     assert mlp - fixed_mlp <= scratch          # one scratch region sized for both
     assert layer == fixed_attn + up(M * d.hidden * 4) + fixed_mlp + scratch
     assert all(x % 256 == 0 for x in (attn, mlp, layer))
+
+
+# The natural-order K/V buffer covers keys [0, kmax): one past the largest
+# position any of the rank's rows attends to, which the oracle's partition
+# maps give independently (zigzag (2D - r) c, striped (T - 1) D + r + 1).
+@pytest.mark.parametrize("partition", [0, 1], ids=["zigzag", "striped"])
+@pytest.mark.parametrize("S,D,r", [(256, 2, 0), (256, 2, 1), (384, 3, 2), (8192, 8, 0), (8192, 8, 7), (16, 8, 5)])
+def test_kv_natural_size_follows_the_partition(lib, partition, S, D, r):
+    from oracle import tsp_oracle as orc
+    d = _dims(seq=S, degree=D, rank=r, n_q_heads=2 * D, n_kv_heads=D, ffn=64 * D, partition=partition)
+    kmax = int(orc.local_to_global(S, D, r, partition).max()) + 1
+    kpad = -(-kmax // 64) * 64
+    want = 2 * D * 1 * kpad * 64 * 2   # K and V, Hkv heads, B = 1, dh = 64, 2 bytes
+    assert lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_KV_NATURAL) == want
+
+
+def test_dims_struct_carries_the_partition():
+    names = [f[0] for f in B.TspDims._fields_]
+    assert names[-1] == "partition" and len(names) == 10
+    d = synth.Dims(1, 256, 2, 0, 256, 4, 4, 64, 768, partition=1)
+    assert B.dims_struct(d).partition == 1
+    assert B.dims_struct(synth.Dims(1, 256, 2, 0, 256, 4, 4, 64, 768)).partition == 0

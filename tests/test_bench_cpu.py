@@ -6,14 +6,17 @@ import synth
 from oracle import tsp_oracle as orc
 
 
+@pytest.mark.parametrize("partition", [0, 1], ids=["zigzag", "striped"])
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
-def test_closed_form_flops_match_the_oracle_count(name):
+def test_closed_form_flops_match_the_oracle_count(name, partition):
     # bench.py counts causal pairs with a closed form; the oracle sums over the
-    # rank's actual zigzag positions
-    d = synth.WORKLOADS[name].dims
+    # rank's actual positions under the partition
+    import dataclasses
+    d = dataclasses.replace(synth.WORKLOADS[name].dims, partition=partition)
     mine, ref = bench.layer_flops(d), orc.algorithmic_flops(d)
     for k in ref:
         assert mine[k] == ref[k], k
+    assert bench.rank_kmax(d) == int(orc.local_to_global(d.seq, d.degree, d.rank, partition).max()) + 1
 
 
 def test_pair_count_is_rank_independent():

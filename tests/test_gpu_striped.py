@@ -1,0 +1,189 @@
+"""GPU parity of the striped token partition (through the C ABI) against the
+float64 oracle.
+
+Striped: position g of each sequence lives on rank g mod D at local row
+g div D.  The Q/K/V and MLP GEMMs are row-local and do not see the partition;
+what changes is the index map, the K/V reorder, and the attention kernel's
+query positions, key ranges and K/V row addresses.  Integer work must match
+bit for bit; float outputs meet max-abs <= 2e-2 and relative Frobenius
+<= 5e-3 against the oracle.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from folded_tensor_sequence_amd import binding as B
+from folded_tensor_sequence_amd.harness import RankProblem
+from oracle import tsp_oracle as orc
+
+from gpu_util import SWEEP, assert_close, dims_of, errors, inputs_for, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+STRIPED = orc.STRIPED
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _striped(shape):
+    return tuple(shape[:9]) + (STRIPED,)
+
+
+# Small shapes.  The attention kernel addresses K/V tiles per tile when D
+# divides 64 and S is a multiple of 64 (every shape here but the D = 3, 5 and
+# S = 16 ones, which take the per-key path); degree 1 makes striped the
+# identity order.
+SHAPES = {
+    "mha_d2_r1": _striped(SWEEP["mha_d2_r1"]),
+    "gqa4_dh128_d4_r2": _striped(SWEEP["gqa4_dh128_d4_r2"]),
+    "gqa8_b2_c96": _striped(SWEEP["gqa8_b2_c96"]),
+    "d1": _striped(SWEEP["d1"]),
+    "c1_d8_r5": _striped(SWEEP["c1_d8_r5"]),
+    "split_keys_dh128": _striped(SWEEP["split_keys_dh128"]),
+    "split_keys_d8_r5": _striped(SWEEP["split_keys_d8_r5"]),
+    "d3_r2_per_key": (1, 384, 3, 2, 128, 6, 3, 64, 384, STRIPED),
+    "d5_r4_b2_per_key": (2, 640, 5, 4, 128, 10, 5, 128, 640, STRIPED),
+}
+
+
+@pytest.mark.parametrize("S,D", [(16, 2), (96, 3), (256, 8), (640, 5), (8192, 8)])
+def test_striped_index_bitexact(S, D):
+    slot_ref = orc.global_to_slot(S, D, STRIPED)
+    for r in range(D):
+        _case(f"striped index S={S} D={D} r={r}")
+        d = synth.Dims(1, S, D, r, 64, D, D, 64, 64 * D, STRIPED)
+        l2g = torch.full((S // D,), -7, dtype=torch.int32, device="cuda")
+        g2s = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+        B.tsp_zigzag_index(d, l2g, g2s)
+        torch.cuda.synchronize()
+        assert np.array_equal(l2g.cpu().numpy(), orc.local_to_global(S, D, r, STRIPED))
+        assert np.array_equal(g2s.cpu().numpy(), slot_ref)
+
+
+@pytest.mark.parametrize("name", ["mha_d2_r1", "gqa8_b2_c96", "d3_r2_per_key", "d5_r4_b2_per_key",
+                                  "split_keys_d8_r5"])
+def test_striped_kv_reorder_bitexact(name):
+    d = dims_of(SHAPES[name])
+    _case(f"striped kv_reorder {name} {d}")
+    Bn, S, D, r, dh = d.batch, d.seq, d.degree, d.rank, d.head_dim
+    T = S // D
+    hkv_s = d.n_kv_heads // D
+    kmax = int(orc.local_to_global(S, D, r, STRIPED).max()) + 1
+    kpad = -(-kmax // 64) * 64
+    rng = np.random.default_rng(7)
+    n = B.tsp_workspace_bytes(d, B.TSP_FN_KV_GATHERED) // 2
+    gathered = rng.integers(-32768, 32767, size=n, dtype=np.int16)
+    nat = torch.full((B.tsp_workspace_bytes(d, B.TSP_FN_KV_NATURAL) // 2,), 0x5A5A, dtype=torch.int16,
+                     device="cuda")
+    assert nat.numel() == 2 * D * hkv_s * Bn * kpad * dh
+    B.tsp_kv_reorder(d, torch.from_numpy(gathered).cuda(), nat)
+    torch.cuda.synchronize()
+    got = nat.cpu().numpy()
+    g6 = gathered.reshape(D, D, 2, Bn, T, hkv_s, dh)        # [j][src][kv][b][t][hk][d]
+    slot = orc.global_to_slot(S, D, STRIPED)[:kmax]
+    src, t = slot // T, slot % T
+    k_exp = np.zeros((D, hkv_s, Bn, kpad, dh), np.int16)
+    v_exp = np.zeros((D, hkv_s, Bn, dh, kpad), np.int16)
+    for j in range(D):
+        for b in range(Bn):
+            k_exp[j, :, b, :kmax] = g6[j, src, 0, b, t].transpose(1, 0, 2)
+            v_exp[j, :, b, :, :kmax] = g6[j, src, 1, b, t].transpose(1, 2, 0)
+    half = got.size // 2
+    assert np.array_equal(got[:half], k_exp.reshape(-1))
+    assert np.array_equal(got[half:], v_exp.reshape(-1))
+
+
+def _attn_check(name, sigma=0.02, seed=101, check_h=True):
+    shape = SHAPES[name]
+    d = dims_of(shape)
+    inp = inputs_for(shape, sigma, seed)
+    prob = RankProblem.build(d, inp)
+    T = d.seq // d.degree
+    out = torch.empty((d.batch, T, d.hidden), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN), dtype=torch.uint8, device="cuda")
+    B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, out, ws)
+    torch.cuda.synchronize()
+    ref = orc.layer_rank_rows(inp, d)
+    got = out.cpu().numpy()
+    if check_h:
+        assert_close(got, ref["h"], what="h = x + attn")
+    branch = got.astype(np.float64) - ref["x"]
+    ma, rf = errors(branch, ref["attn"])
+    ma_rel = ma / float(np.abs(ref["attn"]).max())
+    print(f"  attn branch max_abs/max={ma_rel:.3e} rel_frob={rf:.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert ma_rel <= 2e-2 and rf <= 5e-3
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_striped_attn_fwd(name):
+    _case(f"striped attn_fwd {name}")
+    _attn_check(name)
+
+
+# The plan variants: no pairing of the two halves' blocks, and the 8-wave
+# block shape, on shapes whose blocks are cut into key pieces.
+@pytest.mark.parametrize("name", ["split_keys_dh128", "split_keys_d8_r5", "d5_r4_b2_per_key"])
+@pytest.mark.parametrize("variant", [{"TSP_ATTN_PAIR": "0"}, {"TSP_ATTN_SHAPE": "8x3"}], ids=["unpaired", "8x3"])
+def test_striped_attn_fwd_plan_variants(name, variant, monkeypatch):
+    for k, v in variant.items():
+        monkeypatch.setenv(k, v)
+    _case(f"striped attn_fwd {name} {variant}")
+    _attn_check(name)
+
+
+# Sharp softmax (weights 12.5x the usual scale, logit spread ~16): the
+# running maximum moves often.  The branch is then large, so it is checked
+# relative to its own size only.
+@pytest.mark.parametrize("name", ["gqa4_dh128_d4_r2", "split_keys_d8_r5"])
+def test_striped_attn_fwd_sharp_softmax(name):
+    _case(f"striped attn_fwd {name} sharp softmax")
+    _attn_check(name, sigma=0.25, seed=103, check_h=False)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_striped_layer_fwd(name):
+    shape = SHAPES[name]
+    d = dims_of(shape)
+    _case(f"striped layer_fwd {name}")
+    inp = inputs_for(shape, 0.02, 101)
+    prob = RankProblem.build(d, inp)
+    y = prob.layer().clone()
+    torch.cuda.synchronize()
+    ref = orc.layer_rank_rows(inp, d)
+    assert_close(y.cpu().numpy(), ref["y"], what="y")
+    y2 = prob.layer()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+# The Llama-7B-like 8K layer (rank 0 of D = 8) with the striped partition, in
+# the benchmark's launch configuration: sampled rows against the oracle.
+@pytest.mark.parametrize("rank", [0, 7])
+def test_striped_layer_fwd_full_size_sampled(rank):
+    wl = synth.WORKLOADS["llama7b_s8k_d8"]
+    d = dataclasses.replace(wl.dims, rank=rank, partition=STRIPED)
+    _case(f"striped layer_fwd full {wl.name} rank={rank}")
+    inp = synth.make_inputs(d, wl.sigma, wl.seed)
+    prob = RankProblem.build(d, inp)
+    y = prob.layer()
+    torch.cuda.synchronize()
+    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
+    rows = sample_rows(T, c, n_extra=4, seed=wl.seed)
+    yg = y.cpu().numpy()
+    del prob
+    torch.cuda.empty_cache()
+    ref = orc.rank_rows_forward(inp, d, 0, rows)
+    assert_close(yg[0, rows], ref["y"], what=f"y rows={rows.tolist()}")
