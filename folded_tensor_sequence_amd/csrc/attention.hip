@@ -17,8 +17,9 @@
 // kt_max tiles of 64 keys is cut into pieces along the keys (each piece keeps
 // its own max / sum / unnormalised output, merged afterwards in piece order,
 // so results are deterministic).  Units are ordered heaviest block first;
-// when blocks are cut, each earlier-half block runs inside the last key piece
-// of a later-half partner, so the units weigh about the same (block_geo).
+// when blocks are cut, each later-half block and its earlier-half partner
+// share units: their combined key range is cut into equal pieces
+// (block_geo), so the units weigh about the same.
 //
 // Per 64-key tile:
 //   S^T = K Q^T   (32x32x16 MFMA, K from LDS as the first operand, the wave's
@@ -180,13 +181,11 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
   const int per_bh = s.B * s.Hq;
   const PlanKey pk{s.c, s.D, s.r, s.part, RBR, a.nrb, a.kt_max, a.pair};
   const UnitPos up = unit_of(pk, per_bh, blockIdx.x);
-  BlockGeo g = up.g;
   const int piece = up.piece, bh = up.bh, piece_base = up.piece_base;
   const int b = bh / s.Hq, qh = bh - b * s.Hq;
-  // paired plan: the last piece of a later-chunk block also runs its
-  // earlier-chunk partner block (whole, final output)
-  const int heavy_bi = up.bi;
-  const int nparts = a.pair && piece == g.ns - 1 ? 2 : 1;
+  // paired plan: the unit's piece of the pair's combined key range may also
+  // (or only) cover tiles of the earlier-half partner block
+  const PieceSplit psp = piece_split(pk, up.g, up.bi);
 
   const int G = qh / (s.Hq / s.Hkv);
   const int jsh = G / s.Hkv_s, hk = G - jsh * s.Hkv_s;
@@ -227,12 +226,13 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
     loff[i] = (uint32_t)(((q < K_INS ? 0 : v_step) + row_off + lcol[i]) * 2);
   }
 
-  for (int part = 0; part < nparts; ++part) {
-    if (part == 1) g = block_rows(s.c, s.D, s.r, s.part, RBR, a.nrb, 2 * a.nrb - 1 - heavy_bi);
-    // split: this piece's partial state goes to the workspace for the merge
-    const bool split = part == 0 && g.ns > 1;
-    const int kt_begin = part == 0 ? piece * g.tper : 0;
-    const int kt_end = part == 0 ? (kt_begin + g.tper < g.nkt ? kt_begin + g.tper : g.nkt) : g.nkt;
+  for (int part = 0; part < (a.pair ? 2 : 1); ++part) {
+    // split: this piece's partial state goes to workspace slot piece_base +
+    // slot for the merge
+    BlockGeo g;
+    int kt_begin, kt_end, slot;
+    bool split;
+    if (!unit_part(pk, up.g, up.bi, psp, piece, part, g, kt_begin, kt_end, split, slot)) continue;
     const int wt0 = g.t0 + wave * 32;
     const bool wave_active = wt0 < g.row_end;
     int t_lane = wt0 + lrow;
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
           *reinterpret_cast<u32x2*>(orow + d) = pk;
         }
     } else {
-      const int64_t pidx = (int64_t)(piece_base + piece) * per_bh + bh;
+      const int64_t pidx = (int64_t)(piece_base + slot) * per_bh + bh;
       const int r = t_lane - g.t0;
       float* po = a.part_o + (pidx * RBR + r) * DH;
 #pragma unroll
@@ -502,13 +502,13 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   const int t = g.t0 + r;
   if (t >= g.row_end) return;
   float mmax = -INFINITY;
-  for (int p = 0; p < g.ns; ++p) {
+  for (int p = 0; p < mp.npieces; ++p) {
     const int64_t pidx = (int64_t)(mp.piece_base + p) * per_bh + bh;
     mmax = fmaxf(mmax, a.part_ml[(pidx * 2 + 0) * a.rb + r]);
   }
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int p = 0; p < g.ns; ++p) {
+  for (int p = 0; p < mp.npieces; ++p) {
     const int64_t pidx = (int64_t)(mp.piece_base + p) * per_bh + bh;
     const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * a.rb + r] - mmax);
     l += w * a.part_ml[(pidx * 2 + 1) * a.rb + r];
@@ -558,10 +558,15 @@ static long long plan_makespan(const PlanKey& k, int per_bh, long long slots) {
   long long end = 0;
   for (int bi = 0; bi < 2 * k.nrb; ++bi) {
     const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    const PieceSplit sp = piece_split(k, g, bi);
     for (int p = 0; p < g.ns; ++p) {
-      const int kb = p * g.tper, ke = kb + g.tper < g.nkt ? kb + g.tper : g.nkt;
-      int w = ke - kb + kUnitCost;
-      if (k.pair && p == g.ns - 1) w += block_rows(k.c, k.D, k.r, k.part, k.rbr, k.nrb, 2 * k.nrb - 1 - bi).nkt;
+      int w = kUnitCost;
+      for (int which = 0; which < 2; ++which) {
+        BlockGeo pg;
+        int kb, ke, slot;
+        bool split;
+        if (unit_part(k, g, bi, sp, p, which, pg, kb, ke, split, slot)) w += ke - kb;
+      }
       for (int bh = 0; bh < per_bh; ++bh) {
         const long long t = q.top() + w;
         q.pop();

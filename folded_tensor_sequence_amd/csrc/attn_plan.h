@@ -56,11 +56,13 @@ TSP_HD inline BlockGeo block_rows(int c, int D, int r, int part, int rbr, int nr
 }
 
 // Pieces along the keys.  Unpaired: every block is cut into pieces of at
-// most kt_max tiles.  Paired: the later-chunk block bi (heavy: its keys reach
-// back over both chunks) and the earlier-chunk block 2 nrb - 1 - bi (light)
-// share their work units: the heavy block's key range is cut so that its
-// last piece plus the whole light block weigh about as much as each other
-// piece, and the unit of that last piece then runs the light block too.
+// most kt_max tiles.  Paired: the later-half block bi (heavy) and the
+// earlier-half block 2 nrb - 1 - bi (light) share their work units: their key
+// ranges, the heavy block's tiles followed by the light block's, form one
+// combined range cut into ns pieces of tper tiles, so every unit of the pair
+// weighs the same.  A piece may end in the heavy block, start in the light
+// one, or straddle the two; either block is split (partial states merged
+// afterwards) when more than one piece touches it.  Light blocks get ns = 0.
 TSP_HD inline BlockGeo block_geo(int c, int D, int r, int part, int rbr, int nrb, int kt_max, int pair, int bi) {
   BlockGeo g = block_rows(c, D, r, part, rbr, nrb, bi);
   if (!pair) {
@@ -70,13 +72,8 @@ TSP_HD inline BlockGeo block_geo(int c, int D, int r, int part, int rbr, int nrb
     g.ns = 0;
   } else {
     const int tot = g.nkt + block_rows(c, D, r, part, rbr, nrb, 2 * nrb - 1 - bi).nkt;
-    int ns = (tot + kt_max - 1) / kt_max, tper = (tot + ns - 1) / ns;
-    while (ns > 1 && (ns - 1) * tper >= g.nkt) {  // the last piece keeps at least one heavy tile
-      --ns;
-      tper = (tot + ns - 1) / ns;
-    }
-    g.ns = ns;
-    g.tper = tper;
+    g.ns = (tot + kt_max - 1) / kt_max;
+    g.tper = (tot + g.ns - 1) / g.ns;
   }
   return g;
 }
@@ -86,9 +83,79 @@ struct PlanKey {
   int c, D, r, part, rbr, nrb, kt_max, pair;
 };
 
+// How the pieces of block bi (geometry g from block_geo) fall on the blocks
+// it computes: nh pieces touch the block itself; paired, the light partner
+// has nkt_l tiles and is touched by nl pieces, the first of them piece p0.
+// A block is split when more than one piece touches it; its partial states
+// then take one workspace slot per piece.
+struct PieceSplit {
+  int nh, nkt_l, p0, nl;
+  int slots;  // workspace slots the block (and its light partner) use
+};
+
+TSP_HD inline PieceSplit piece_split(const PlanKey& k, const BlockGeo& g, int bi) {
+  PieceSplit q;
+  q.nkt_l = 0;
+  q.p0 = 0;
+  q.nl = 0;
+  if (g.ns == 0) {
+    q.nh = 0;
+    q.slots = 0;
+    return q;
+  }
+  if (!k.pair) {
+    q.nh = g.ns;
+    q.slots = g.ns > 1 ? g.ns : 0;
+    return q;
+  }
+  q.nkt_l = block_rows(k.c, k.D, k.r, k.part, k.rbr, k.nrb, 2 * k.nrb - 1 - bi).nkt;
+  q.nh = (g.nkt + g.tper - 1) / g.tper;
+  q.p0 = g.nkt / g.tper;
+  q.nl = g.ns - q.p0;
+  q.slots = (q.nh > 1 ? q.nh : 0) + (q.nl > 1 ? q.nl : 0);
+  return q;
+}
+
+// Part `which` of unit piece `piece` of block bi: 0 = the block's own key
+// tiles, 1 = the light partner's (paired plans).  Fills the block computed
+// (geometry pg), its key tiles [kb, ke), whether its state is partial
+// (split) and, if so, its workspace slot relative to the pair's first slot.
+// Returns false when the part is empty.
+TSP_HD inline bool unit_part(const PlanKey& k, const BlockGeo& g, int bi, const PieceSplit& q, int piece,
+                             int which, BlockGeo& pg, int& kb, int& ke, bool& split, int& slot) {
+  if (!k.pair) {
+    if (which != 0) return false;
+    pg = g;
+    kb = piece * g.tper;
+    ke = kb + g.tper < g.nkt ? kb + g.tper : g.nkt;
+    split = g.ns > 1;
+    slot = piece;
+    return kb < ke;
+  }
+  const int tot = g.nkt + q.nkt_l;
+  const int c0 = piece * g.tper;
+  const int c1 = c0 + g.tper < tot ? c0 + g.tper : tot;
+  if (which == 0) {
+    if (c0 >= g.nkt) return false;
+    pg = g;
+    kb = c0;
+    ke = c1 < g.nkt ? c1 : g.nkt;
+    split = q.nh > 1;
+    slot = piece;
+    return kb < ke;
+  }
+  if (c1 <= g.nkt) return false;
+  pg = block_rows(k.c, k.D, k.r, k.part, k.rbr, k.nrb, 2 * k.nrb - 1 - bi);
+  kb = (c0 > g.nkt ? c0 : g.nkt) - g.nkt;
+  ke = c1 - g.nkt;
+  split = q.nl > 1;
+  slot = (q.nh > 1 ? q.nh : 0) + (piece - q.p0);
+  return kb < ke;
+}
+
 // Work unit u of the attention kernel: block bi, key piece `piece` of
-// (sequence, q-head) pair bh; piece_base = pieces of the split blocks listed
-// before bi (the index of the block's first piece in the workspace).
+// (sequence, q-head) pair bh; piece_base = workspace slots taken by the
+// blocks listed before bi (the index of the block's first slot).
 struct UnitPos {
   BlockGeo g;
   int bi, piece, bh, piece_base;
@@ -103,7 +170,7 @@ TSP_HD inline UnitPos unit_of(const PlanKey& k, int per_bh, int u) {
     const int n = p.g.ns * per_bh;
     if (u < n || p.bi + 1 >= 2 * k.nrb) break;
     u -= n;
-    if (p.g.ns > 1) p.piece_base += p.g.ns;
+    p.piece_base += piece_split(k, p.g, p.bi).slots;
     ++p.bi;
     p.g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, p.bi);
   }
@@ -112,38 +179,44 @@ TSP_HD inline UnitPos unit_of(const PlanKey& k, int per_bh, int u) {
   return p;
 }
 
-// The split block (ns > 1) holding merge item `item` when every split block
-// holds items_per_block items: its geometry, index, first piece and the item
-// within it; bi = -1 past the last one.
+// The split block holding merge item `item` when every split block holds
+// items_per_block items, in workspace slot order: its geometry, index, first
+// slot, number of pieces and the item within it; bi = -1 past the last one.
 struct MergePos {
   BlockGeo g;
-  int bi, piece_base;
+  int bi, piece_base, npieces;
   long long item;
 };
 
 TSP_HD inline MergePos merge_block_of(const PlanKey& k, long long items_per_block, long long item) {
   MergePos m;
-  m.piece_base = 0;
+  int base = 0;
   for (int bi = 0; bi < 2 * k.nrb; ++bi) {
     const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
-    if (g.ns <= 1) continue;
-    if (item >= items_per_block) {
-      item -= items_per_block;
-      m.piece_base += g.ns;
-      continue;
+    const PieceSplit q = piece_split(k, g, bi);
+    for (int which = 0; which < 2; ++which) {
+      const int n = which == 0 ? q.nh : q.nl;
+      if (n <= 1) continue;
+      if (item >= items_per_block) {
+        item -= items_per_block;
+        base += n;
+        continue;
+      }
+      m.g = which == 0 ? g : block_rows(k.c, k.D, k.r, k.part, k.rbr, k.nrb, 2 * k.nrb - 1 - bi);
+      m.bi = which == 0 ? bi : 2 * k.nrb - 1 - bi;
+      m.piece_base = base;
+      m.npieces = n;
+      m.item = item;
+      return m;
     }
-    m.g = g;
-    m.bi = bi;
-    m.item = item;
-    return m;
   }
   m.bi = -1;
   m.item = item;
   return m;
 }
 
-// Whole-plan counts: work units per (sequence, q-head) pair, pieces of the
-// split blocks, rows of the split blocks.
+// Whole-plan counts: work units per (sequence, q-head) pair, workspace slots
+// of the split blocks, rows of the split blocks.
 struct PlanCounts {
   long long units_per_bh;
   int pieces, split_rows;
@@ -153,11 +226,10 @@ TSP_HD inline PlanCounts plan_counts(const PlanKey& k) {
   PlanCounts n{0, 0, 0};
   for (int bi = 0; bi < 2 * k.nrb; ++bi) {
     const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    const PieceSplit q = piece_split(k, g, bi);
     n.units_per_bh += g.ns;
-    if (g.ns > 1) {
-      n.pieces += g.ns;
-      n.split_rows += k.rbr;
-    }
+    n.pieces += q.slots;
+    n.split_rows += (q.nh > 1 ? k.rbr : 0) + (q.nl > 1 ? k.rbr : 0);
   }
   return n;
 }

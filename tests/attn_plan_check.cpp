@@ -4,10 +4,12 @@
 // every (row block, sequence x q-head, key tile) is computed by exactly one
 // work unit, every local row lies in exactly one block at the position the
 // partition gives it (written out here on its own), each block's key tiles
-// end with the tile of its last row's position, split pieces get distinct
-// workspace slots, and the merge kernel finds each split block with the same
-// first piece the attention units used.  Prints "ok <cases>" or the first
-// failure.
+// end with the tile of its last row's position, no unit is empty, a block is
+// either computed whole by one unit or split into pieces with distinct
+// consecutive workspace slots, and the merge kernel finds every split block
+// with the first slot and piece count the attention units used.  Prints
+// "ok <cases>" or the first failure.
+#include <algorithm>
 #include <cstdio>
 #include <vector>
 
@@ -56,33 +58,47 @@ static int check(int B, int S, int D, int r, int part, int Hq, int rbr, long lon
   }
   for (int t = 0; t < 2 * c; ++t)
     if (row_seen[t] != 1) FAIL("rows");
-  // units: every (block, bh, key tile) exactly once
+  // units: every (block, bh, key tile) exactly once; each split block's
+  // partial states in consecutive workspace slots, one per piece
   std::vector<int> cover((size_t)nb * per_bh * max_nkt, 0);
   std::vector<int> slot_used((size_t)(n.pieces > 0 ? n.pieces : 1) * per_bh, 0);
-  std::vector<int> first_piece(nb, -1);
+  std::vector<int> first_slot(nb, 1 << 30), last_slot(nb, -1), pieces_of(nb, 0), whole(nb, 0);
   const long long units = n.units_per_bh * per_bh;
   for (long long u = 0; u < units; ++u) {
     const UnitPos p = unit_of(k, per_bh, (int)u);
     if (p.piece < 0 || p.piece >= p.g.ns || p.bh < 0 || p.bh >= per_bh) FAIL("unit decode");
-    if (p.g.ns > 1) {
-      if (first_piece[p.bi] < 0) first_piece[p.bi] = p.piece_base;
-      if (first_piece[p.bi] != p.piece_base) FAIL("piece base");
-    }
-    const int nparts = k.pair && p.piece == p.g.ns - 1 ? 2 : 1;
-    for (int ipart = 0; ipart < nparts; ++ipart) {
-      const int bi = ipart == 0 ? p.bi : nb - 1 - p.bi;
-      const BlockGeo g = ipart == 0 ? p.g : block_rows(c, D, r, part, rbr, k.nrb, bi);
-      const bool split = ipart == 0 && g.ns > 1;
-      const int kb = ipart == 0 ? p.piece * g.tper : 0;
-      const int ke = ipart == 0 ? (kb + g.tper < g.nkt ? kb + g.tper : g.nkt) : g.nkt;
-      if (kb >= ke) FAIL("empty piece");
+    const PieceSplit q = piece_split(k, p.g, p.bi);
+    int nonempty = 0;
+    for (int which = 0; which < 2; ++which) {
+      BlockGeo g;
+      int kb, ke, slot;
+      bool split;
+      if (!unit_part(k, p.g, p.bi, q, p.piece, which, g, kb, ke, split, slot)) continue;
+      ++nonempty;
+      const int bi = which == 0 ? p.bi : nb - 1 - p.bi;
+      if (g.t0 != block_rows(c, D, r, part, rbr, k.nrb, bi).t0) FAIL("part block");
+      if (kb < 0 || ke > g.nkt) FAIL("part range");
       for (int kt = kb; kt < ke; ++kt) ++cover[((size_t)bi * per_bh + p.bh) * max_nkt + kt];
       if (split) {
-        const long long slot = (long long)(p.piece_base + p.piece) * per_bh + p.bh;
-        if (slot < 0 || slot >= (long long)n.pieces * per_bh) FAIL("piece slot range");
-        ++slot_used[slot];
+        const long long s = (long long)(p.piece_base + slot) * per_bh + p.bh;
+        if (s < 0 || s >= (long long)n.pieces * per_bh) FAIL("piece slot range");
+        ++slot_used[s];
+        if (p.bh == 0) {
+          first_slot[bi] = std::min(first_slot[bi], p.piece_base + slot);
+          last_slot[bi] = std::max(last_slot[bi], p.piece_base + slot);
+          ++pieces_of[bi];
+        }
+      } else {
+        if (kb != 0 || ke != g.nkt) FAIL("whole block not whole");
+        if (p.bh == 0) ++whole[bi];
       }
     }
+    if (nonempty == 0) FAIL("empty unit");
+  }
+  for (int bi = 0; bi < nb; ++bi) {
+    if (whole[bi] + (pieces_of[bi] > 0 ? 1 : 0) != 1) FAIL("block both whole and split");
+    if (pieces_of[bi] == 1) FAIL("split block with one piece");
+    if (pieces_of[bi] > 1 && last_slot[bi] - first_slot[bi] + 1 != pieces_of[bi]) FAIL("slots not consecutive");
   }
   for (int bi = 0; bi < nb; ++bi) {
     const int nkt = block_rows(c, D, r, part, rbr, k.nrb, bi).nkt;
@@ -95,11 +111,17 @@ static int check(int B, int S, int D, int r, int part, int Hq, int rbr, long lon
   // merge: work groups of 256 items, 32 items (4 head-dim columns each) per row
   const long long ipb = (long long)per_bh * rbr * 32;
   const long long total = (long long)n.split_rows * per_bh * 32;
+  std::vector<int> merged(nb, 0);
   for (long long item = 0; item < total; item += 256) {
     const MergePos m = merge_block_of(k, ipb, item);
-    if (m.bi < 0 || m.g.ns <= 1 || m.piece_base != first_piece[m.bi]) FAIL("merge block");
+    if (m.bi < 0 || m.bi >= nb || pieces_of[m.bi] < 2) FAIL("merge block");
+    if (m.piece_base != first_slot[m.bi] || m.npieces != pieces_of[m.bi]) FAIL("merge pieces");
+    if (m.g.t0 != block_rows(c, D, r, part, rbr, k.nrb, m.bi).t0) FAIL("merge rows");
     if (m.item < 0 || m.item + 256 > ipb) FAIL("merge item");
+    if (m.item == 0) ++merged[m.bi];
   }
+  for (int bi = 0; bi < nb; ++bi)
+    if (merged[bi] != (pieces_of[bi] > 1 ? 1 : 0)) FAIL("merge misses a split block");
   if (merge_block_of(k, ipb, total).bi != -1) FAIL("merge end");
 #undef FAIL
   return 0;
