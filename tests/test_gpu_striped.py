@@ -169,11 +169,14 @@ def test_striped_layer_fwd(name):
     assert torch.equal(y, y2)
 
 
-# The Llama-7B-like 8K layer (rank 0 of D = 8) with the striped partition, in
-# the benchmark's launch configuration: sampled rows against the oracle.
-@pytest.mark.parametrize("rank", [0, 7])
-def test_striped_layer_fwd_full_size_sampled(rank):
-    wl = synth.WORKLOADS["llama7b_s8k_d8"]
+# Full-size layers with the striped partition, in the benchmark's launch
+# configuration: the Llama-7B-like 8K layer on the first and last ranks
+# (attention blocks cut into key pieces and paired) and the GQA 16K layer
+# (B = 2, rank 3); sampled rows against the oracle.
+@pytest.mark.parametrize("name,rank", [("llama7b_s8k_d8", 0), ("llama7b_s8k_d8", 7),
+                                       ("llama3_8b_gqa_s16k_d8", 3)])
+def test_striped_layer_fwd_full_size_sampled(name, rank):
+    wl = synth.WORKLOADS[name]
     d = dataclasses.replace(wl.dims, rank=rank, partition=STRIPED)
     _case(f"striped layer_fwd full {wl.name} rank={rank}")
     inp = synth.make_inputs(d, wl.sigma, wl.seed)
@@ -185,5 +188,6 @@ def test_striped_layer_fwd_full_size_sampled(rank):
     yg = y.cpu().numpy()
     del prob
     torch.cuda.empty_cache()
-    ref = orc.rank_rows_forward(inp, d, 0, rows)
-    assert_close(yg[0, rows], ref["y"], what=f"y rows={rows.tolist()}")
+    for b in range(d.batch):
+        ref = orc.rank_rows_forward(inp, d, b, rows)
+        assert_close(yg[b, rows], ref["y"], what=f"y b={b} rows={rows.tolist()}")
