@@ -926,7 +926,8 @@ static int env_choice(const char* name, int* nsplit) {
 }
 
 // Single-weight GEMM configurations:
-//   0: staged, 256x192 tile, 8 waves (4x2)   -- Q/K/V projection
+//   0: staged, 256x192 tile, 8 waves (4x2)   -- Q/K/V projection; output and
+//      down projections without split-K when it takes fewer rounds
 //   1: staged, 256x128 tile, 4 waves (2x2)
 //   2: staged, 256x192 tile, 4 waves (2x2)
 //   3: direct-load ring, 256x256 tile, 8 waves, K step 32, 5 stages
@@ -966,6 +967,15 @@ static hipError_t launch_single(const GemmArgs& a, const char* name, int max_spl
     nsplit = env_split;
   }
   if (nsplit < 1 || nsplit > max_split || a.partial == nullptr) nsplit = 1;
+  if (EPI != EPI_QKV && env_cfg < 0 && nsplit == 1) {
+    // Unsplit output/down projection (large M): 256x192 tiles when their
+    // work-group rounds on 256 CUs, at 1.3x the time of a 256x128 tile (1.5x
+    // the products, fewer LDS operand reads per product), finish sooner.
+    const long long mt = (a.M + 255) / 256;
+    const long long r192 = (mt * ((a.N + 191) / 192) + 255) / 256;
+    const long long r128 = (mt * ((a.N + 127) / 128) + 255) / 256;
+    if (13 * r192 < 10 * r128) cfg = 0;
+  }
   return launch_cfg<F16, CONVB, EPI>(a, cfg, nsplit, st);
 }
 
