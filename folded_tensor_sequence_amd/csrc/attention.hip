@@ -527,16 +527,19 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 
 // ---- host-side plan (shared with workspace sizing) -----------------------
 // Kernel shape: waves per block (32 rows each) and depth of the K/V ring.
-// The default, 4 waves and 2 stages, fits two blocks per CU; 8 waves and 3
-// stages (one block per CU, each K/V tile shared by 256 query rows) is the
-// alternative.  Tuning override (no effect unless set):
+// 4 waves and 2 stages fit two blocks per CU; 8 waves and 3 stages run one
+// block per CU, each K/V tile shared by 256 query rows (half the K/V
+// traffic).  The second pays off only when blocks loop over long key ranges
+// (measured: 3% faster at 128K context with ~1100 key tiles per block, 2-5%
+// slower at 130-260), so it is taken when the rank's 128-row blocks average
+// at least 512 key tiles.  Tuning override (no effect unless set):
 // TSP_ATTN_SHAPE=<waves>x<stages>, 4x2 or 8x3.
 struct AttnShape {
   int nwv, nst;
 };
 static const AttnShape kShapes[] = {{4, 2}, {8, 3}};
 
-static AttnShape attn_shape() {
+static AttnShape attn_shape(const Shape& s) {
   if (const char* ev = getenv("TSP_ATTN_SHAPE")) {
     for (const AttnShape& k : kShapes) {
       char name[8];
@@ -544,7 +547,10 @@ static AttnShape attn_shape() {
       if (strcmp(ev, name) == 0) return k;
     }
   }
-  return kShapes[0];
+  const int rbr = 32 * kShapes[0].nwv, nrb = (s.c + rbr - 1) / rbr;
+  long long tiles = 0;
+  for (int bi = 0; bi < 2 * nrb; ++bi) tiles += block_rows(s.c, s.D, s.r, s.part, rbr, nrb, bi).nkt;
+  return tiles >= 512LL * 2 * nrb ? kShapes[1] : kShapes[0];
 }
 
 // Estimated finishing time of a plan, in key tiles: units are handed out in
@@ -629,7 +635,7 @@ AttnPlan attn_plan(const Shape& s) {
     char pair_env, pieces_env[16];
     AttnPlan p;
   } last;
-  const AttnShape k = attn_shape();
+  const AttnShape k = attn_shape(s);
   const char* pe = getenv("TSP_ATTN_PAIR");
   const char* ne = getenv("TSP_ATTN_PIECES");
   char pieces[16] = {0};
