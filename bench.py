@@ -83,6 +83,29 @@ def kernel_work(d):
     }, f["total"]
 
 
+def device_peak():
+    """bf16 dense matrix-core peak recomputed from the agent's own compute-unit
+    count and maximum engine clock as rocminfo reports them (4096 bf16 FLOP per
+    clock per CU on gfx950), or None if rocminfo is unavailable.  Run before
+    the GPU is initialised in this process."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in out.split("Agent ")[1:]:
+        if "gfx950" not in agent or "GPU" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return {"compute_units": cus, "max_clock_mhz": clk,
+                    "bf16_tflops": round(cus * clk * 1e6 * 4096 / 1e12, 1)}
+    return None
+
+
 def source_digest(paths):
     import hashlib
     h = hashlib.sha256()
@@ -176,6 +199,8 @@ def main():
               "multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
+    peak_dev = device_peak()
+
     import torch
 
     import synth
@@ -219,14 +244,15 @@ def main():
 
     # timed region: K steps; the dominant kernel is bracketed by HIP events
     B.tsp_profile_kernel(dominant, args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         prob.layer()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
+    total_ms = ev[0].elapsed_time(ev[-1])
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     n_dom, dom_ms = B.tsp_profile_result()
     B.tsp_profile_kernel(None)
     ms_per_step = total_ms / args.steps
@@ -258,6 +284,8 @@ def main():
                    "head_dim": d.head_dim, "ffn": d.ffn, "rank_tokens": M, "partition": args.partition},
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
         "pct_of_bf16_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 5), "min": round(step_ms[0], 5)},
+        "device_peak": peak_dev,
         "gflop_per_step": round(total_flop / 1e9, 2),
         "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": runit, "frac": round(achieved / peak, 4), "traffic": None,

@@ -55,3 +55,23 @@ def test_more_than_one_gpu_is_refused():
     assert "--gpus must be 1" in out.stderr
     assert out.stdout == ""
 
+
+
+def test_device_peak_from_rocminfo_text(monkeypatch):
+    # the peak is recomputed from the GPU agent's own CU count and clock; the
+    # CPU agent (no gfx950) is skipped
+    import subprocess
+    text = ("Agent 1\n  Name:  AMD EPYC\n  Device Type:  CPU\n  Compute Unit:  128\n"
+            "  Max Clock Freq. (MHz):  3700\n"
+            "Agent 2\n  Name:  gfx950\n  Device Type:  GPU\n  Compute Unit:  256\n"
+            "  Max Clock Freq. (MHz):  2400\n")
+
+    class Out:
+        stdout = text
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: Out())
+    assert bench.device_peak() == {"compute_units": 256, "max_clock_mhz": 2400, "bf16_tflops": 2516.6}
+
+    def missing(*a, **k):
+        raise FileNotFoundError("rocminfo")
+    monkeypatch.setattr(subprocess, "run", missing)
+    assert bench.device_peak() is None
