@@ -132,6 +132,67 @@ def recorded_traffic(workload, kernel):
     return rec["traffic_bytes_per_launch"]
 
 
+def host_info():
+    """CPU model and the host threads this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cores": len(os.sched_getaffinity(0))}
+
+
+def versions():
+    """Versions of what produced the numbers: torch / HIP, ROCm, and a digest
+    of the library's sources."""
+    import platform
+
+    import torch
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    srcs = sorted(os.path.join("folded_tensor_sequence_amd", "csrc", n)
+                  for n in os.listdir(os.path.join(ROOT, "folded_tensor_sequence_amd", "csrc")))
+    return {"torch": torch.__version__, "hip": torch.version.hip, "rocm": rocm,
+            "python": platform.python_version(), "libtsp_sources_sha256": source_digest(srcs)[:16]}
+
+
+def oracle_parity(d, inp, y_host, max_rows: int, seed: int):
+    """The timed step's output against the float64 oracle: every row of
+    sequence 0 when the rank has at most max_rows rows, else the first and
+    last row of every 128-row block of both halves plus seeded others."""
+    import numpy as np
+
+    from oracle import tsp_oracle as orc
+
+    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
+    if T <= max_rows:
+        rows, what = np.arange(T), f"all {T} rows of sequence 0"
+    else:
+        rng = np.random.default_rng(seed)
+        pick = set(rng.choice(T, size=16, replace=False).tolist())
+        for h0, h1 in ((0, c), (c, T)):
+            for b0 in range(h0, h1, 128):
+                pick.update((b0, min(b0 + 128, h1) - 1))
+        rows = np.array(sorted(pick))
+        what = (f"{len(rows)} of the {T} rows of sequence 0: first and last row of every 128-row block "
+                f"plus 16 seeded")
+    ref = orc.rank_rows_forward(inp, d, 0, rows)["y"]
+    got = np.asarray(y_host[0, rows], dtype=np.float64)
+    diff = got - ref
+    max_abs = float(np.abs(diff).max())
+    rel = float(np.linalg.norm(diff) / np.linalg.norm(ref))
+    return {"max_abs": max_abs, "rel_frob": rel, "rows": what,
+            "bar": {"max_abs": 2e-2, "rel_frob": 5e-3}, "within_bar": max_abs <= 2e-2 and rel <= 5e-3}
+
+
 def cpu_baseline(d, inp, target_s: float, max_rows: int):
     """Times the oracle (float64 numpy, host cores) on a sample of the rank's rows:
     own Q/K/V projection, attention over the full causal prefix, output
@@ -173,7 +234,7 @@ def cpu_baseline(d, inp, target_s: float, max_rows: int):
         dt = run(rows)
     fl = orc.algorithmic_flops(d, rows_per_seq=rows)["total"]
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "tokens_per_s": len(rows) / dt, "seconds": dt,
+            "cpu_model": host_info()["cpu_model"], "tokens_per_s": len(rows) / dt, "seconds": dt,
             "sample": f"{len(rows)} of the rank's {T} rows (seeded, half per half of its rows) of "
                       f"sequence 0, float64 numpy/OpenBLAS on {cores} host threads; K/V of all "
                       f"{kmax} keys precomputed before timing"}
@@ -255,6 +316,7 @@ def main():
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     n_dom, dom_ms = B.tsp_profile_result()
     B.tsp_profile_kernel(None)
+    y_host = prob.y.cpu().numpy()           # the output of the last timed step
     ms_per_step = total_ms / args.steps
     tflops = total_flop / (ms_per_step * 1e-3) / 1e12
     M = d.batch * d.seq // d.degree
@@ -292,14 +354,18 @@ def main():
                      "avg_launch_ms": round(dom_avg_s * 1e3, 5), "launches": n_dom,
                      "algorithmic_per_launch": amount},
         "kernels_ms": {k: round(v, 5) for k, v in kms.items()},
+        "seeds": {"inputs": wl.seed, "cpu_sample": 1234},
+        "host": host_info(),
+        "versions": versions(),
+        "parity": None,
     }
     # standalone zigzag K/V reorder (not part of the layer step): HBM-bound copy
     nat = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_KV_NATURAL) // 2, dtype=torch.int16, device="cuda")
     for _ in range(3):
-        B.tsp_kv_reorder(d, prob.kv_gathered, nat)
+        B.tsp_kv_reorder(d, prob.kv_gathered, nat, 0)
     B.tsp_profile_kernel("reorder", args.steps)
     for _ in range(args.steps):
-        B.tsp_kv_reorder(d, prob.kv_gathered, nat)
+        B.tsp_kv_reorder(d, prob.kv_gathered, nat, 0)
     n_re, re_ms = B.tsp_profile_result()
     B.tsp_profile_kernel(None)
     torch.cuda.synchronize()
@@ -324,6 +390,8 @@ def main():
         del prob
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(d, inp, args.cpu_seconds, max_rows=d.seq // d.degree)
+        print("[bench] checking the timed output against the oracle", file=sys.stderr, flush=True)
+        out["parity"] = oracle_parity(d, inp, y_host, max_rows=2048, seed=wl.seed)
     print(json.dumps(out), flush=True)
 
 

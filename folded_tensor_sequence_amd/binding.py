@@ -4,6 +4,12 @@ Every computation happens in the HIP kernels behind the C ABI; this module
 turns torch tensors into device pointers and the current HIP stream into a
 ``hipStream_t``.  If the library is not built it raises -- there is no CPU
 fallback.
+
+Before a pointer is handed over, each wrapper checks that the tensor lives on
+a GPU, is contiguous, has an element type of the width the ABI expects, and
+holds at least the bytes the ABI layout implies for these dims; a mismatch
+raises ``ValueError`` and nothing reaches the library.  16-bit tensors may be
+``int16`` / ``uint16`` bit patterns or the matching float type.
 """
 from __future__ import annotations
 
@@ -20,6 +26,22 @@ TSP_ERR_INVALID_ARG = -1
 TSP_ERR_UNSUPPORTED = -2
 TSP_ERR_WORKSPACE = -3
 TSP_ERR_HIP = -4
+TSP_ERR_NULL_POINTER = -5
+TSP_ERR_MISALIGNED = -6
+TSP_ERR_BATCH = -10
+TSP_ERR_DEGREE = -11
+TSP_ERR_RANK = -12
+TSP_ERR_SEQ = -13
+TSP_ERR_HEADS = -14
+TSP_ERR_GQA = -15
+TSP_ERR_HIDDEN = -16
+TSP_ERR_FFN = -17
+TSP_ERR_PARTITION = -18
+TSP_ERR_DTYPE = -19
+TSP_ERR_KMAX = -20
+TSP_ERR_SCRATCH = -21
+
+TSP_BF16, TSP_F16, TSP_F32 = 0, 1, 2
 
 TSP_FN_ATTN = 1
 TSP_FN_MLP = 2
@@ -29,9 +51,12 @@ TSP_FN_KV_GATHERED = 5
 
 KERNELS = {"qkv": 1, "reorder": 2, "attn": 3, "oproj": 4, "gateup": 5, "down": 6}
 
+TUNE = {"gemm_qkv": 0, "gemm_oproj": 1, "gemm_gateup": 2, "gemm_down": 3, "split_oproj": 4,
+        "split_down": 5, "attn_shape": 6, "attn_pair": 7, "attn_pieces": 8}
+
 EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd",
             "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",
-            "tsp_profile_kernel", "tsp_profile_result")
+            "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning")
 
 
 class TspDims(ctypes.Structure):
@@ -63,9 +88,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "tsp_zigzag_index": [dp, vp, vp, vp],
         "tsp_qkv_proj": [dp, i32, vp, vp, vp, vp, vp],
-        "tsp_kv_reorder": [dp, vp, vp, vp],
-        "tsp_attn_fwd": [dp, vp, vp, vp, vp, vp, vp, sz, vp],
-        "tsp_mlp_ring_fwd": [dp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_kv_reorder": [dp, vp, vp, i32, vp],
+        "tsp_attn_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_mlp_ring_fwd": [dp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_layer_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
@@ -78,6 +103,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tsp_profile_kernel.restype = ctypes.c_int
     lib.tsp_profile_result.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)]
     lib.tsp_profile_result.restype = ctypes.c_int
+    lib.tsp_set_tuning.argtypes = [i32, i32]
+    lib.tsp_set_tuning.restype = ctypes.c_int
     lib.tsp_last_error.argtypes = []
     lib.tsp_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -92,14 +119,65 @@ def dims_struct(dims) -> TspDims:
                    getattr(dims, "partition", 0))
 
 
-def _p(t):
+# --------------------------------------------------------------------------- #
+# Argument checks (host side, before any pointer reaches the library)
+# --------------------------------------------------------------------------- #
+_KINDS = {
+    "bf16": (torch.int16, torch.uint16, torch.bfloat16),
+    "f16": (torch.int16, torch.uint16, torch.float16),
+    "f32": (torch.float32,),
+    "i32": (torch.int32,),
+    "bytes": None,  # any element type (workspace)
+}
+
+
+def _tensor(t, name: str, kind: str, nbytes: int | None, optional: bool = False):
+    """Device pointer of ``t`` after checking device, layout, type and size."""
     if t is None:
-        return None
-    if isinstance(t, int):
-        return ctypes.c_void_p(t)
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor (got {type(t).__name__})")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
     if not t.is_contiguous():
-        raise ValueError("tensor arguments must be contiguous")
+        raise ValueError(f"{name} must be contiguous")
+    allowed = _KINDS[kind]
+    if allowed is not None and t.dtype not in allowed:
+        raise ValueError(f"{name} must be {kind} ({', '.join(str(a) for a in allowed)}), got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if nbytes is not None and have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the ABI layout needs {nbytes}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+class _Sizes:
+    """Byte sizes of the ABI layouts for one dims (include/tsp.h)."""
+
+    def __init__(self, dims):
+        d = dims
+        self.T = d.seq // d.degree
+        self.M = d.batch * self.T
+        self.rows = self.M * d.hidden                         # [B][T][h]
+        self.x16 = 2 * self.rows
+        self.f32 = 4 * self.rows
+        self.w_qkv = 2 * (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim * d.hidden
+        self.w_o = 2 * d.hidden * d.n_q_heads * d.head_dim
+        self.w_ffn = 2 * d.ffn * d.hidden
+        self.q = 2 * self.M * d.n_q_heads * d.head_dim
+        self.l2g = 4 * self.T
+        self.g2s = 4 * d.seq
+        self.dims = d
+
+    def kv_natural(self, kmax):
+        d = self.dims
+        if kmax == 0:
+            c = d.seq // (2 * d.degree)
+            kmax = ((self.T - 1) * d.degree + d.rank + 1 if getattr(d, "partition", 0) == 1
+                    else (2 * d.degree - d.rank) * c)
+        kpad = -(-kmax // 64) * 64
+        return 4 * d.n_kv_heads * d.batch * kpad * d.head_dim
 
 
 def _s(stream):
@@ -125,38 +203,101 @@ def tsp_workspace_bytes(dims, fn: int) -> int:
     return n
 
 
+def _ws(dims, ws, fn):
+    return _tensor(ws, "ws", "bytes", tsp_workspace_bytes(dims, fn)), _nbytes(ws)
+
+
 def tsp_zigzag_index(dims, local_to_global, global_to_slot=None, stream=None):
+    z = _Sizes(dims)
     d = dims_struct(dims)
-    _check(load().tsp_zigzag_index(ctypes.byref(d), _p(local_to_global), _p(global_to_slot), _s(stream)))
+    _check(load().tsp_zigzag_index(ctypes.byref(d), _tensor(local_to_global, "local_to_global", "i32", z.l2g),
+                                   _tensor(global_to_slot, "global_to_slot", "i32", z.g2s, optional=True),
+                                   _s(stream)))
 
 
 def tsp_qkv_proj(dims, src_rank, x_shard, w_qkv, q_out, kv_gathered, stream=None):
+    z = _Sizes(dims)
     d = dims_struct(dims)
-    _check(load().tsp_qkv_proj(ctypes.byref(d), int(src_rank), _p(x_shard), _p(w_qkv), _p(q_out),
-                               _p(kv_gathered), _s(stream)))
+    _check(load().tsp_qkv_proj(ctypes.byref(d), int(src_rank), _tensor(x_shard, "x_shard", "bf16", z.x16),
+                               _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv),
+                               _tensor(q_out, "q_out", "f16", z.q, optional=True),
+                               _tensor(kv_gathered, "kv_gathered", "f16",
+                                       tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+                               _s(stream)))
 
 
-def tsp_kv_reorder(dims, kv_gathered, kv_natural, stream=None):
+def tsp_kv_reorder(dims, kv_gathered, kv_natural, kmax: int = 0, stream=None):
+    z = _Sizes(dims)
     d = dims_struct(dims)
-    _check(load().tsp_kv_reorder(ctypes.byref(d), _p(kv_gathered), _p(kv_natural), _s(stream)))
+    kmax = int(kmax)
+    nat_bytes = z.kv_natural(kmax) if 0 <= kmax <= d.seq else None  # else the library says why
+    _check(load().tsp_kv_reorder(ctypes.byref(d),
+                                 _tensor(kv_gathered, "kv_gathered", "f16",
+                                         tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+                                 _tensor(kv_natural, "kv_natural", "f16", nat_bytes), kmax, _s(stream)))
 
 
-def tsp_attn_fwd(dims, x_local, w_qkv, w_o, kv_gathered, out, ws, stream=None):
+def tsp_attn_fwd(dims, x_local, w_qkv, w_o, kv_gathered, out, ws, residual=None, stream=None):
+    """out = residual + attention branch (residual None: the branch alone)."""
+    z = _Sizes(dims)
     d = dims_struct(dims)
-    _check(load().tsp_attn_fwd(ctypes.byref(d), _p(x_local), _p(w_qkv), _p(w_o), _p(kv_gathered),
-                               _p(out), _p(ws), _nbytes(ws), _s(stream)))
+    wsp, wsn = _ws(dims, ws, TSP_FN_ATTN)
+    _check(load().tsp_attn_fwd(ctypes.byref(d), _tensor(x_local, "x_local", "bf16", z.x16),
+                               _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv), _tensor(w_o, "w_o", "bf16", z.w_o),
+                               _tensor(kv_gathered, "kv_gathered", "f16",
+                                       tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+                               _tensor(residual, "residual", "f32", z.f32, optional=True),
+                               _tensor(out, "out", "f32", z.f32), wsp, wsn, _s(stream)))
 
 
-def tsp_mlp_ring_fwd(dims, x, w_gate, w_up, w_down, y, ws, stream=None):
+_XDTYPE = {torch.bfloat16: TSP_BF16, torch.float16: TSP_F16, torch.float32: TSP_F32}
+
+
+def tsp_mlp_ring_fwd(dims, x, w_gate, w_up, w_down, y, ws, residual=None, x_dtype=None, stream=None):
+    """y = residual + MLP ring over x (residual None: the MLP branch alone).
+
+    x_dtype: TSP_BF16 / TSP_F16 / TSP_F32; None takes it from x's torch dtype
+    (bfloat16, float16 or float32; 16-bit integer bit patterns need x_dtype)."""
+    z = _Sizes(dims)
     d = dims_struct(dims)
-    _check(load().tsp_mlp_ring_fwd(ctypes.byref(d), _p(x), _p(w_gate), _p(w_up), _p(w_down), _p(y),
-                                   _p(ws), _nbytes(ws), _s(stream)))
+    if x_dtype is None:
+        if not isinstance(x, torch.Tensor) or x.dtype not in _XDTYPE:
+            raise ValueError("x_dtype is required unless x is bfloat16, float16 or float32")
+        x_dtype = _XDTYPE[x.dtype]
+    kind = {TSP_BF16: "bf16", TSP_F16: "f16", TSP_F32: "f32"}.get(int(x_dtype))
+    if kind is None:
+        raise ValueError(f"x_dtype {x_dtype} unknown")
+    wsp, wsn = _ws(dims, ws, TSP_FN_MLP)
+    _check(load().tsp_mlp_ring_fwd(ctypes.byref(d), _tensor(x, "x", kind, z.f32 if kind == "f32" else z.x16),
+                                   int(x_dtype), _tensor(w_gate, "w_gate", "bf16", z.w_ffn),
+                                   _tensor(w_up, "w_up", "bf16", z.w_ffn), _tensor(w_down, "w_down", "bf16", z.w_ffn),
+                                   _tensor(residual, "residual", "f32", z.f32, optional=True),
+                                   _tensor(y, "y", "f32", z.f32), wsp, wsn, _s(stream)))
 
 
 def tsp_layer_fwd(dims, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, ws, stream=None):
+    z = _Sizes(dims)
     d = dims_struct(dims)
-    _check(load().tsp_layer_fwd(ctypes.byref(d), _p(x_local), _p(w_qkv), _p(w_o), _p(w_gate), _p(w_up),
-                                _p(w_down), _p(kv_gathered), _p(y), _p(ws), _nbytes(ws), _s(stream)))
+    wsp, wsn = _ws(dims, ws, TSP_FN_LAYER)
+    _check(load().tsp_layer_fwd(ctypes.byref(d), _tensor(x_local, "x_local", "bf16", z.x16),
+                                _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv), _tensor(w_o, "w_o", "bf16", z.w_o),
+                                _tensor(w_gate, "w_gate", "bf16", z.w_ffn), _tensor(w_up, "w_up", "bf16", z.w_ffn),
+                                _tensor(w_down, "w_down", "bf16", z.w_ffn),
+                                _tensor(kv_gathered, "kv_gathered", "f16",
+                                        tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+                                _tensor(y, "y", "f32", z.f32), wsp, wsn, _s(stream)))
+
+
+def tsp_set_tuning(knob, value: int | None):
+    """Kernel-choice override for tests and tuning: knob name (see TUNE) or id;
+    value None or < 0 restores the default dispatch."""
+    kid = TUNE[knob] if isinstance(knob, str) else int(knob)
+    _check(load().tsp_set_tuning(kid, -1 if value is None else int(value)))
+
+
+def reset_tuning():
+    for kid in TUNE.values():
+        load().tsp_set_tuning(kid, -1)
 
 
 def tsp_profile_kernel(kernel, max_launches: int = 1):

@@ -532,21 +532,18 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 // traffic).  The second pays off only when blocks loop over long key ranges
 // (measured: 3% faster at 128K context with ~1100 key tiles per block, 2-5%
 // slower at 130-260), so it is taken when the rank's 128-row blocks average
-// at least 512 key tiles.  Tuning override (no effect unless set):
-// TSP_ATTN_SHAPE=<waves>x<stages>, 4x2 or 8x3.
+// at least 512 key tiles.  Override (tsp_set_tuning, TSP_TUNE_ATTN_SHAPE):
+// 4 or 8 waves.
 struct AttnShape {
   int nwv, nst;
 };
 static const AttnShape kShapes[] = {{4, 2}, {8, 3}};
+enum { KNOB_ATTN_SHAPE = 6, KNOB_ATTN_PAIR = 7, KNOB_ATTN_PIECES = 8 };
 
 static AttnShape attn_shape(const Shape& s) {
-  if (const char* ev = getenv("TSP_ATTN_SHAPE")) {
-    for (const AttnShape& k : kShapes) {
-      char name[8];
-      snprintf(name, sizeof name, "%dx%d", k.nwv, k.nst);
-      if (strcmp(ev, name) == 0) return k;
-    }
-  }
+  const int over = tune_get(KNOB_ATTN_SHAPE);
+  for (const AttnShape& k : kShapes)
+    if (over == k.nwv) return k;
   const int rbr = 32 * kShapes[0].nwv, nrb = (s.c + rbr - 1) / rbr;
   long long tiles = 0;
   for (int bi = 0; bi < 2 * nrb; ++bi) tiles += block_rows(s.c, s.D, s.r, s.part, rbr, nrb, bi).nkt;
@@ -589,8 +586,8 @@ static long long plan_makespan(const PlanKey& k, int per_bh, long long slots) {
 // work groups) key tiles, and the earlier half's blocks ride with the later
 // half's (paired) unless the makespan estimate says that separate units
 // finish sooner (when both halves see long key ranges: zigzag on the middle
-// and last ranks, striped).  Tuning overrides, no effect unless set:
-// TSP_ATTN_PIECES=<target number of work units>, TSP_ATTN_PAIR=0 or 1.
+// and last ranks, striped).  Overrides (tsp_set_tuning): TSP_TUNE_ATTN_PIECES
+// = target number of work units, TSP_TUNE_ATTN_PAIR = 0 or 1.
 static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   AttnPlan p;
   p.nwv = k.nwv;
@@ -598,13 +595,11 @@ static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   p.rb = 32 * k.nwv;
   const long long slots = k.nwv == 4 && k.nst == 2 ? 512 : 256;  // resident blocks on 256 CUs
   long long target = slots;
-  if (const char* ev = getenv("TSP_ATTN_PIECES")) {
-    if (atoi(ev) > 0) target = atoi(ev);
-  }
+  if (tune_get(KNOB_ATTN_PIECES) > 0) target = tune_get(KNOB_ATTN_PIECES);
   if (pair < 0) {
-    const char* ev = getenv("TSP_ATTN_PAIR");
-    if (ev != nullptr && (ev[0] == '0' || ev[0] == '1')) {
-      pair = ev[0] - '0';
+    const int over = tune_get(KNOB_ATTN_PAIR);
+    if (over == 0 || over == 1) {
+      pair = over;
     } else {
       const PlanKey kp = plan_key(s.c, s.D, s.r, s.part, s.B, s.Hq, p.rb, slots, target, 1);
       pair = 1;
@@ -625,34 +620,10 @@ static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
   return p;
 }
 
-// The plan of the last shape asked for is kept, so that the makespan
-// estimate runs once per shape rather than on every launch.
-AttnPlan attn_plan(const Shape& s) {
-  static thread_local struct {
-    bool valid = false;
-    Shape s;
-    int nwv, nst;
-    char pair_env, pieces_env[16];
-    AttnPlan p;
-  } last;
-  const AttnShape k = attn_shape(s);
-  const char* pe = getenv("TSP_ATTN_PAIR");
-  const char* ne = getenv("TSP_ATTN_PIECES");
-  char pieces[16] = {0};
-  if (ne != nullptr) strncpy(pieces, ne, sizeof pieces - 1);
-  const char pair_env = pe != nullptr ? pe[0] : 0;
-  if (last.valid && memcmp(&last.s, &s, sizeof s) == 0 && last.nwv == k.nwv && last.nst == k.nst &&
-      last.pair_env == pair_env && memcmp(last.pieces_env, pieces, sizeof pieces) == 0)
-    return last.p;
-  last.p = plan_for(s, -1, k);
-  last.s = s;
-  last.nwv = k.nwv;
-  last.nst = k.nst;
-  last.pair_env = pair_env;
-  memcpy(last.pieces_env, pieces, sizeof pieces);
-  last.valid = true;
-  return last.p;
-}
+// The plan is recomputed on every launch (no state is kept between calls);
+// its cost is a few thousand integer steps at most, and only shapes whose
+// blocks are split along the keys estimate the makespan at all.
+AttnPlan attn_plan(const Shape& s) { return plan_for(s, -1, attn_shape(s)); }
 
 // Enough for every plan, so that a workspace sized once serves them all.
 size_t attn_partial_bytes(const Shape& s) {

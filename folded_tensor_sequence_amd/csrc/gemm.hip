@@ -16,8 +16,6 @@
 // block run on the same XCD (blocks are dealt round-robin to the 8 XCDs) and
 // hit its L2.  Details of the pipeline are at the kernel below.
 #include <stdio.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include <type_traits>
 
@@ -90,14 +88,21 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
       *reinterpret_cast<u32x2*>(a.out16 + off) = pk;
     }
   } else if constexpr (EPI == EPI_RESID_F32) {
+    // float32 residual, or none (the branch alone) when resid is null
     const int64_t off = (int64_t)m * a.N + n;
-    f32x4 r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
-    f32x4 o;
-    o[0] = r[0] + v[0];
-    o[1] = r[1] + v[1];
-    o[2] = r[2] + v[2];
-    o[3] = r[3] + v[3];
+    f32x4 o{v[0], v[1], v[2], v[3]};
+    if (a.resid != nullptr) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
+      o[0] = r[0] + v[0];
+      o[1] = r[1] + v[1];
+      o[2] = r[2] + v[2];
+      o[3] = r[3] + v[3];
+    }
     *reinterpret_cast<f32x4*>(a.out + off) = o;
+    if (a.out16 != nullptr) {
+      u32x2 pk{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(a.out16 + off) = pk;
+    }
   } else if constexpr (EPI == EPI_PARTIAL) {
     // v2 carries the split index in its first element's bits (see caller)
     (void)v2;
@@ -913,17 +918,11 @@ static hipError_t launch_staged(const GemmArgs& a, int nsplit, hipStream_t st) {
   return launch_staged_seg<BM, BN, NB, WGM, NW, false, F16, CONVB, EPI, NSTG, SPLIT>(a, nsplit, st);
 }
 
-// Tuning override (no effect unless set): TSP_GEMM_<NAME>=<config>[:<nsplit>].
-static int env_choice(const char* name, int* nsplit) {
-  char key[64];
-  snprintf(key, sizeof(key), "TSP_GEMM_%s", name);
-  const char* v = getenv(key);
-  if (v == nullptr || *v == 0) return -1;
-  int cfg = atoi(v);
-  const char* c = strchr(v, ':');
-  if (c != nullptr && nsplit != nullptr) *nsplit = atoi(c + 1);
-  return cfg;
-}
+// Overrides set through tsp_set_tuning (for tests and tuning): a GEMM
+// configuration index and, for the output and down projections, a split-K
+// factor.  -1: the default dispatch.
+enum { KNOB_GEMM_QKV = 0, KNOB_GEMM_OPROJ = 1, KNOB_GEMM_GATEUP = 2, KNOB_GEMM_DOWN = 3,
+       KNOB_SPLIT_OPROJ = 4, KNOB_SPLIT_DOWN = 5 };
 
 // Single-weight GEMM configurations:
 //   0: staged, 256x192 tile, 8 waves (4x2)   -- Q/K/V projection; output and
@@ -956,18 +955,16 @@ static hipError_t launch_cfg(const GemmArgs& a, int cfg, int nsplit, hipStream_t
 }
 
 template <bool F16, bool CONVB, int EPI>
-static hipError_t launch_single(const GemmArgs& a, const char* name, int max_split, hipStream_t st) {
+static hipError_t launch_single(const GemmArgs& a, int knob_cfg, int knob_split, int max_split, hipStream_t st) {
   // Q/K/V: 256x192 tiles; output/down (M x h): 256x128 tiles, split along K
   // as planned by gemm_split_plan so that tiles x splits covers the CUs
   int cfg = EPI == EPI_QKV ? 0 : 6, nsplit = EPI == EPI_QKV ? 1 : max_split;
-  int env_split = nsplit;
-  const int env_cfg = env_choice(name, &env_split);
-  if (env_cfg >= 0) {
-    cfg = env_cfg;
-    nsplit = env_split;
-  }
+  const int over_cfg = tune_get(knob_cfg);
+  if (over_cfg >= 0) cfg = over_cfg;
+  if (knob_split >= 0 && tune_get(knob_split) >= 1) nsplit = tune_get(knob_split);
+  // the workspace holds partials for at most the planned factor
   if (nsplit < 1 || nsplit > max_split || a.partial == nullptr) nsplit = 1;
-  if (EPI != EPI_QKV && env_cfg < 0 && nsplit == 1) {
+  if (EPI != EPI_QKV && over_cfg < 0 && nsplit == 1) {
     // Unsplit output/down projection (large M): 256x192 tiles when their
     // work-group rounds on 256 CUs, at 1.3x the time of a 256x128 tile (1.5x
     // the products, fewer LDS operand reads per product), finish sooner.
@@ -1002,12 +999,12 @@ hipError_t launch_qkv_gemm(const Shape& s, int src_rank, const uint16_t* x, cons
   a.q = q;
   a.kv = kv_gathered;
   a.src_rank = src_rank;
-  return launch_single<false, false, EPI_QKV>(a, "QKV", 1, st);
+  return launch_single<false, false, EPI_QKV>(a, KNOB_GEMM_QKV, -1, 1, st);
 }
 
 hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* w_o,
-                             const uint16_t* x_resid, float* out, uint16_t* out16, float* partial,
-                             hipStream_t st) {
+                             const uint16_t* x_resid, const float* resid_f32, float* out, uint16_t* out16,
+                             float* partial, hipStream_t st) {
   GemmArgs a = base_args(s);
   const int seg = s.Hq_s * s.dh;
   a.A = o;
@@ -1023,15 +1020,19 @@ hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* 
   a.nseg = s.D;
   a.out = out;
   a.out16 = out16;
-  a.resid = x_resid;
   a.partial = partial;
-  return launch_single<true, true, EPI_RESID_BF16X>(a, "OPROJ", gemm_split_plan(s), st);
+  if (x_resid != nullptr) {
+    a.resid = x_resid;
+    return launch_single<true, true, EPI_RESID_BF16X>(a, KNOB_GEMM_OPROJ, KNOB_SPLIT_OPROJ, gemm_split_plan(s), st);
+  }
+  a.resid = resid_f32;
+  return launch_single<true, true, EPI_RESID_F32>(a, KNOB_GEMM_OPROJ, KNOB_SPLIT_OPROJ, gemm_split_plan(s), st);
 }
 
-hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_t* w_g,
+hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g,
                               const uint16_t* w_u, uint16_t* act, hipStream_t st) {
   GemmArgs a = base_args(s);
-  a.A = h16;
+  a.A = x;
   a.lda = s.h;
   a.B0 = w_g;
   a.B1 = w_u;
@@ -1046,7 +1047,14 @@ hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_
   //   2: direct-load ring, 128x128 (x2), 4 waves, K step 64, 3 stages
   //   3: staged, 256x96 (x2) tile, 8 waves (8x1);  4: as 3 with two register sets
   //   5: staged, 256x96 (x2) tile, 8 waves (4x2) with one weight per wave column
-  int cfg = env_choice("GATEUP", nullptr);
+  // bf16 input: both operands bf16 as given (bf16 matrix cores), the
+  // default tile only
+  if (x_bf16) {
+    hipError_t e = launch_staged<256, 96, 2, 4, 8, false, false, EPI_SWIGLU, 1, true>(a, 1, st);
+    if (e != hipErrorNotSupported) return e;
+    return launch_tile<128, 128, 2, 2, 4, 64, 3, false, false, EPI_SWIGLU, 1>(a, 1, st);
+  }
+  int cfg = tune_get(KNOB_GEMM_GATEUP);
   if (cfg < 0) cfg = 5;
   hipError_t e = hipErrorNotSupported;
   if (cfg == 0) e = launch_staged<128, 192, 2, 4, 8, true, true, EPI_SWIGLU>(a, 1, st);
@@ -1076,7 +1084,7 @@ hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t*
   a.out = y;
   a.resid = resid;
   a.partial = partial;
-  return launch_single<true, true, EPI_RESID_F32>(a, "DOWN", gemm_split_plan(s), st);
+  return launch_single<true, true, EPI_RESID_F32>(a, KNOB_GEMM_DOWN, KNOB_SPLIT_DOWN, gemm_split_plan(s), st);
 }
 
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n4) {

@@ -9,6 +9,10 @@
 
 namespace tsp {
 
+// Kernel-choice override set through tsp_set_tuning (knob = tsp_tune_knob);
+// -1 when none is set.
+int tune_get(int knob);
+
 hipError_t launch_zigzag_index(const Shape& s, int32_t* l2g, int32_t* g2s, hipStream_t st);
 hipError_t launch_kv_reorder(const Shape& s, const uint16_t* gathered, uint16_t* knat,
                              uint16_t* vnat, hipStream_t st);
@@ -32,17 +36,19 @@ inline int gemm_split_plan(const Shape& s) {
   return p > kMaxSplit ? kMaxSplit : p;
 }
 
-// out = x(bf16) + O * W_o^T over the D shards' K-segments; also an f16 copy
-// of out when out16 != nullptr.
+// out = resid + O * W_o^T over the D shards' K-segments, where resid is
+// x_resid (bf16) when given, else resid_f32 (float32), else nothing; also an
+// f16 copy of out when out16 != nullptr.
 hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* w_o,
-                             const uint16_t* x_resid, float* out, uint16_t* out16, float* partial,
-                             hipStream_t st);
+                             const uint16_t* x_resid, const float* resid_f32, float* out, uint16_t* out16,
+                             float* partial, hipStream_t st);
 
-// act = silu(h16 Wg^T) * (h16 Wu^T) (f16 matrix cores, weights bf16->f16).
-hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* h16, const uint16_t* w_g,
+// act = silu(x Wg^T) * (x Wu^T): x f16 with f16 matrix cores (weights
+// bf16 -> f16), or x bf16 (x_bf16) with bf16 matrix cores on the weights as given.
+hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g,
                               const uint16_t* w_u, uint16_t* act, hipStream_t st);
 
-// y = resid + sum over ring steps of act_j W_d,j^T.
+// y = resid + sum over ring steps of act_j W_d,j^T (resid may be nullptr).
 hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t* w_d,
                             const float* resid, float* y, float* partial, hipStream_t st);
 

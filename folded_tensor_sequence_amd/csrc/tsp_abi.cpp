@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -34,30 +35,26 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 
 // Validates dims and fills the derived shape.  Returns TSP_OK or an error code.
 int make_shape(const tsp_dims_t* d, tsp::Shape* s) {
-  if (d == nullptr) return fail(TSP_ERR_INVALID_ARG, "dims is NULL");
-  if (d->batch < 1) return fail(TSP_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
-  if (d->degree < 1) return fail(TSP_ERR_INVALID_ARG, "degree must be >= 1 (got %d)", d->degree);
+  if (d == nullptr) return fail(TSP_ERR_NULL_POINTER, "dims is NULL");
+  if (d->batch < 1) return fail(TSP_ERR_BATCH, "batch must be >= 1 (got %d)", d->batch);
+  if (d->degree < 1) return fail(TSP_ERR_DEGREE, "degree must be >= 1 (got %d)", d->degree);
   if (d->rank < 0 || d->rank >= d->degree)
-    return fail(TSP_ERR_INVALID_ARG, "rank %d not in [0, degree=%d)", d->rank, d->degree);
+    return fail(TSP_ERR_RANK, "rank %d not in [0, degree=%d)", d->rank, d->degree);
   if (d->seq < 2 * d->degree || d->seq % (2 * d->degree) != 0)
-    return fail(TSP_ERR_INVALID_ARG, "seq %d must be a positive multiple of 2*degree=%d", d->seq,
-                2 * d->degree);
-  if (d->n_q_heads < 1 || d->n_kv_heads < 1)
-    return fail(TSP_ERR_INVALID_ARG, "head counts must be >= 1");
+    return fail(TSP_ERR_SEQ, "seq %d must be a positive multiple of 2*degree=%d", d->seq, 2 * d->degree);
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1) return fail(TSP_ERR_HEADS, "head counts must be >= 1");
   if (d->n_q_heads % d->degree != 0 || d->n_kv_heads % d->degree != 0)
-    return fail(TSP_ERR_INVALID_ARG, "n_q_heads %d and n_kv_heads %d must be multiples of degree %d",
-                d->n_q_heads, d->n_kv_heads, d->degree);
+    return fail(TSP_ERR_HEADS, "n_q_heads %d and n_kv_heads %d must be multiples of degree %d", d->n_q_heads,
+                d->n_kv_heads, d->degree);
   if (d->n_q_heads % d->n_kv_heads != 0)
-    return fail(TSP_ERR_INVALID_ARG, "n_q_heads %d must be a multiple of n_kv_heads %d",
-                d->n_q_heads, d->n_kv_heads);
+    return fail(TSP_ERR_GQA, "n_q_heads %d must be a multiple of n_kv_heads %d", d->n_q_heads, d->n_kv_heads);
   if (d->hidden < 64 || d->hidden % 64 != 0)
-    return fail(TSP_ERR_INVALID_ARG, "hidden %d must be a positive multiple of 64", d->hidden);
+    return fail(TSP_ERR_HIDDEN, "hidden %d must be a positive multiple of 64", d->hidden);
   if (d->ffn < 64 || d->ffn % 64 != 0 || (d->ffn / d->degree) * d->degree != d->ffn ||
       (d->ffn / d->degree) % 8 != 0)
-    return fail(TSP_ERR_INVALID_ARG,
-                "ffn %d must be a positive multiple of 64 with ffn/degree a multiple of 8", d->ffn);
+    return fail(TSP_ERR_FFN, "ffn %d must be a positive multiple of 64 with ffn/degree a multiple of 8", d->ffn);
   if (d->partition != TSP_PARTITION_ZIGZAG && d->partition != TSP_PARTITION_STRIPED)
-    return fail(TSP_ERR_INVALID_ARG, "partition %d unknown (0 zigzag, 1 striped)", d->partition);
+    return fail(TSP_ERR_PARTITION, "partition %d unknown (0 zigzag, 1 striped)", d->partition);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(TSP_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if ((int64_t)d->seq > kMaxDim || (int64_t)d->batch * d->seq / d->degree > kMaxDim ||
@@ -89,15 +86,18 @@ int make_shape(const tsp_dims_t* d, tsp::Shape* s) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int need_ptr(const void* p, const char* name) {
-  if (p == nullptr) return fail(TSP_ERR_INVALID_ARG, "%s is NULL", name);
-  if (!aligned16(p)) return fail(TSP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  if (p == nullptr) return fail(TSP_ERR_NULL_POINTER, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TSP_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
   return TSP_OK;
 }
 
 int opt_ptr(const void* p, const char* name) {
-  if (p != nullptr && !aligned16(p)) return fail(TSP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  if (p != nullptr && !aligned16(p)) return fail(TSP_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
   return TSP_OK;
 }
+
+// Process-wide kernel-choice overrides (tsp_set_tuning); -1 = default.
+std::atomic<int> g_tune[TSP_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
 
 constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -217,21 +217,25 @@ int check_device(const char* where) {
     if (_e != hipSuccess) return hip_fail(_e, where); \
   } while (0)
 
+// out = resid + attention branch; resid is x_resid (bf16, the layer's own
+// input), else resid_f32, else nothing.
 int run_attention(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* w_qkv,
-                  const uint16_t* w_o, uint16_t* kv_gathered, float* out, uint16_t* out16,
-                  const AttnWs& w, hipStream_t st) {
+                  const uint16_t* w_o, uint16_t* kv_gathered, const uint16_t* x_resid, const float* resid_f32,
+                  float* out, uint16_t* out16, const AttnWs& w, hipStream_t st) {
   TSP_KLAUNCH(TSP_K_QKV, st, tsp::launch_qkv_gemm(s, s.r, x_local, w_qkv, w.q, kv_gathered, st),
               "qkv projection");
   TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, st),
               "flash attention");
-  TSP_KLAUNCH(TSP_K_OPROJ, st, tsp::launch_oproj_gemm(s, w.o, w_o, x_local, out, out16, w.partial, st),
+  TSP_KLAUNCH(TSP_K_OPROJ, st,
+              tsp::launch_oproj_gemm(s, w.o, w_o, x_resid, resid_f32, out, out16, w.partial, st),
               "output projection");
   return TSP_OK;
 }
 
-int run_mlp(const tsp::Shape& s, const uint16_t* h16, const float* resid, const uint16_t* w_gate,
+int run_mlp(const tsp::Shape& s, const uint16_t* x16, bool x_bf16, const float* resid, const uint16_t* w_gate,
             const uint16_t* w_up, const uint16_t* w_down, float* y, const MlpWs& w, hipStream_t st) {
-  TSP_KLAUNCH(TSP_K_GATEUP, st, tsp::launch_gateup_gemm(s, h16, w_gate, w_up, w.act, st), "mlp gate/up");
+  TSP_KLAUNCH(TSP_K_GATEUP, st, tsp::launch_gateup_gemm(s, x16, x_bf16, w_gate, w_up, w.act, st),
+              "mlp gate/up");
   TSP_KLAUNCH(TSP_K_DOWN, st, tsp::launch_down_gemm(s, w.act, w_down, resid, y, w.partial, st),
               "mlp down ring");
   return TSP_OK;
@@ -239,9 +243,21 @@ int run_mlp(const tsp::Shape& s, const uint16_t* h16, const float* resid, const 
 
 }  // namespace
 
+namespace tsp {
+int tune_get(int knob) {
+  return knob >= 0 && knob < TSP_TUNE_COUNT ? g_tune[knob].load(std::memory_order_relaxed) : -1;
+}
+}  // namespace tsp
+
 extern "C" {
 
 const char* tsp_last_error(void) { return g_last_error.c_str(); }
+
+int tsp_set_tuning(int32_t knob, int32_t value) {
+  if (knob < 0 || knob >= TSP_TUNE_COUNT) return fail(TSP_ERR_INVALID_ARG, "unknown tuning knob %d", knob);
+  g_tune[knob].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+  return TSP_OK;
+}
 
 int tsp_profile_kernel(int32_t kernel_id, int32_t max_launches) {
   if (kernel_id < TSP_K_NONE || kernel_id >= TSP_K_COUNT)
@@ -268,7 +284,7 @@ int tsp_profile_kernel(int32_t kernel_id, int32_t max_launches) {
 
 int tsp_profile_result(int32_t* launches, float* total_ms) {
   if (launches == nullptr || total_ms == nullptr)
-    return fail(TSP_ERR_INVALID_ARG, "launches and total_ms must not be NULL");
+    return fail(TSP_ERR_NULL_POINTER, "launches and total_ms must not be NULL");
   float sum = 0.0f;
   for (int i = 0; i < g_prof.used; ++i) {
     hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
@@ -301,7 +317,7 @@ int tsp_zigzag_index(const tsp_dims_t* dims, int32_t* local_to_global, int32_t* 
                      hipStream_t stream) {
   tsp::Shape s;
   TSP_TRY(make_shape(dims, &s));
-  if (local_to_global == nullptr) return fail(TSP_ERR_INVALID_ARG, "local_to_global is NULL");
+  if (local_to_global == nullptr) return fail(TSP_ERR_NULL_POINTER, "local_to_global is NULL");
   TSP_TRY(check_device("tsp_zigzag_index"));
   TSP_LAUNCH(tsp::launch_zigzag_index(s, local_to_global, global_to_slot, stream), "zigzag index");
   return TSP_OK;
@@ -312,7 +328,7 @@ int tsp_qkv_proj(const tsp_dims_t* dims, int32_t src_rank, const uint16_t* x_sha
   tsp::Shape s;
   TSP_TRY(make_shape(dims, &s));
   if (src_rank < 0 || src_rank >= s.D)
-    return fail(TSP_ERR_INVALID_ARG, "src_rank %d not in [0, %d)", src_rank, s.D);
+    return fail(TSP_ERR_RANK, "src_rank %d not in [0, %d)", src_rank, s.D);
   TSP_TRY(need_ptr(x_shard, "x_shard"));
   TSP_TRY(need_ptr(w_qkv, "w_qkv"));
   TSP_TRY(opt_ptr(q_out, "q_out"));
@@ -324,13 +340,18 @@ int tsp_qkv_proj(const tsp_dims_t* dims, int32_t src_rank, const uint16_t* x_sha
   return TSP_OK;
 }
 
-int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered, uint16_t* kv_natural,
+int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered, uint16_t* kv_natural, int32_t kmax,
                    hipStream_t stream) {
   tsp::Shape s;
   TSP_TRY(make_shape(dims, &s));
+  if (kmax < 0 || kmax > s.S) return fail(TSP_ERR_KMAX, "kmax %d not in [0, seq=%d]", kmax, s.S);
   TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
   TSP_TRY(need_ptr(kv_natural, "kv_natural"));
   TSP_TRY(check_device("tsp_kv_reorder"));
+  if (kmax > 0) {
+    s.kmax = kmax;
+    s.kmax_pad = (kmax + 63) / 64 * 64;
+  }
   uint16_t* vnat = kv_natural + bytes_knat(s) / 2;
   TSP_KLAUNCH(TSP_K_REORDER, stream, tsp::launch_kv_reorder(s, kv_gathered, kv_natural, vnat, stream),
               "kv reorder");
@@ -338,14 +359,15 @@ int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered, uint16_t
 }
 
 int tsp_attn_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
-                 const uint16_t* w_o, uint16_t* kv_gathered, float* out, void* ws, size_t ws_bytes,
-                 hipStream_t stream) {
+                 const uint16_t* w_o, uint16_t* kv_gathered, const float* residual, float* out, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
   tsp::Shape s;
   TSP_TRY(make_shape(dims, &s));
   TSP_TRY(need_ptr(x_local, "x_local"));
   TSP_TRY(need_ptr(w_qkv, "w_qkv"));
   TSP_TRY(need_ptr(w_o, "w_o"));
   TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(opt_ptr(residual, "residual"));
   TSP_TRY(need_ptr(out, "out"));
   TSP_TRY(need_ptr(ws, "ws"));
   if (ws_bytes < ws_attn(s))
@@ -353,18 +375,21 @@ int tsp_attn_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t
   TSP_TRY(check_device("tsp_attn_fwd"));
   AttnWs w;
   w.partial = partial_or_null(s, carve_attn(s, static_cast<char*>(ws), &w));
-  return run_attention(s, x_local, w_qkv, w_o, kv_gathered, out, nullptr, w, stream);
+  return run_attention(s, x_local, w_qkv, w_o, kv_gathered, nullptr, residual, out, nullptr, w, stream);
 }
 
-int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const float* x, const uint16_t* w_gate,
-                     const uint16_t* w_up, const uint16_t* w_down, float* y, void* ws,
+int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const uint16_t* w_gate,
+                     const uint16_t* w_up, const uint16_t* w_down, const float* residual, float* y, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
   tsp::Shape s;
   TSP_TRY(make_shape(dims, &s));
+  if (x_dtype != TSP_BF16 && x_dtype != TSP_F16 && x_dtype != TSP_F32)
+    return fail(TSP_ERR_DTYPE, "x_dtype %d unknown (0 bf16, 1 f16, 2 f32)", x_dtype);
   TSP_TRY(need_ptr(x, "x"));
   TSP_TRY(need_ptr(w_gate, "w_gate"));
   TSP_TRY(need_ptr(w_up, "w_up"));
   TSP_TRY(need_ptr(w_down, "w_down"));
+  TSP_TRY(opt_ptr(residual, "residual"));
   TSP_TRY(need_ptr(y, "y"));
   TSP_TRY(need_ptr(ws, "ws"));
   if (ws_bytes < ws_mlp(s))
@@ -372,8 +397,13 @@ int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const float* x, const uint16_t* w_g
   TSP_TRY(check_device("tsp_mlp_ring_fwd"));
   MlpWs w;
   w.partial = partial_or_null(s, carve_mlp(s, static_cast<char*>(ws), &w));
-  TSP_LAUNCH(tsp::launch_f32_to_f16(x, w.h16, (int64_t)s.M * s.h, stream), "mlp input rounding");
-  return run_mlp(s, w.h16, x, w_gate, w_up, w_down, y, w, stream);
+  const uint16_t* x16 = static_cast<const uint16_t*>(x);
+  if (x_dtype == TSP_F32) {
+    TSP_LAUNCH(tsp::launch_f32_to_f16(static_cast<const float*>(x), w.h16, (int64_t)s.M * s.h, stream),
+               "mlp input rounding");
+    x16 = w.h16;
+  }
+  return run_mlp(s, x16, x_dtype == TSP_BF16, residual, w_gate, w_up, w_down, y, w, stream);
 }
 
 int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
@@ -401,8 +431,8 @@ int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_
   p += up(bytes_h32(s));
   p = carve_mlp(s, p, &mw);
   aw.partial = mw.partial = partial_or_null(s, p);
-  TSP_TRY(run_attention(s, x_local, w_qkv, w_o, kv_gathered, h32, mw.h16, aw, stream));
-  return run_mlp(s, mw.h16, h32, w_gate, w_up, w_down, y, mw, stream);
+  TSP_TRY(run_attention(s, x_local, w_qkv, w_o, kv_gathered, x_local, nullptr, h32, mw.h16, aw, stream));
+  return run_mlp(s, mw.h16, false, h32, w_gate, w_up, w_down, y, mw, stream);
 }
 
 }  // extern "C"

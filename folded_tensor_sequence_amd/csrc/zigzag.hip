@@ -85,14 +85,17 @@ __global__ __launch_bounds__(8 * (DH / 8)) void kv_reorder_kernel(
   const int64_t row_elems = (int64_t)s.Hkv_s * DH;
 
   // Source rows of the thread's 8 keys.  Zigzag with c % 8 == 0: the 8 keys
-  // sit in one chunk at consecutive local rows (one address, fixed stride);
-  // otherwise each key's rank and row are computed on their own.
+  // sit in one chunk at consecutive local rows (one address, fixed stride),
+  // and all of them are copied when the group lies below kmax (a kmax that
+  // is not a multiple of 8 ends inside a group: that group takes the per-key
+  // path, which zero-fills the keys past kmax); otherwise each key's rank
+  // and row are computed on their own.
   const int g0 = tile * 64 + kc * 8;
   const uint16_t* col = gathered + (int64_t)hk * DH + dc * 8;
   const int64_t src_base = (((int64_t)j * s.D * 2 + kv) * s.B + b) * s.T;  // row of (src 0, t 0)
   const int64_t src_step = (int64_t)2 * s.B * s.T;                          // rows per src rank
   u32x4 v[8];
-  if (s.part == 0 && s.c % 8 == 0) {
+  if (s.part == 0 && s.c % 8 == 0 && (g0 + 8 <= s.kmax || g0 >= s.kmax)) {
     if (g0 < s.kmax) {
       const int q = g0 / s.c, i = g0 - q * s.c;
       const int src = q < s.D ? q : 2 * s.D - 1 - q;

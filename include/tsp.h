@@ -80,13 +80,32 @@ typedef struct {
 
 typedef enum { TSP_PARTITION_ZIGZAG = 0, TSP_PARTITION_STRIPED = 1 } tsp_partition;
 
+/* Return codes.  Every validation failure has a code of its own; the text
+ * from tsp_last_error() names the argument and the rule it broke. */
 typedef enum {
   TSP_OK = 0,
-  TSP_ERR_INVALID_ARG = -1, /* shape rule broken, NULL or misaligned pointer */
-  TSP_ERR_UNSUPPORTED = -2, /* valid TSP shape the library does not handle */
-  TSP_ERR_WORKSPACE = -3,   /* ws too small (see tsp_workspace_bytes) */
-  TSP_ERR_HIP = -4          /* HIP runtime error (no device, launch failure) */
+  TSP_ERR_INVALID_ARG = -1,  /* argument outside its documented set (selector, src_rank, ...) */
+  TSP_ERR_UNSUPPORTED = -2,  /* valid TSP shape the library does not handle (head_dim, index range) */
+  TSP_ERR_WORKSPACE = -3,    /* ws too small (see tsp_workspace_bytes) */
+  TSP_ERR_HIP = -4,          /* HIP runtime error (no device, launch failure) */
+  TSP_ERR_NULL_POINTER = -5, /* a required pointer (or dims) is NULL */
+  TSP_ERR_MISALIGNED = -6,   /* a tensor pointer is not 16-byte aligned */
+  TSP_ERR_BATCH = -10,       /* batch < 1 */
+  TSP_ERR_DEGREE = -11,      /* degree < 1 */
+  TSP_ERR_RANK = -12,        /* rank (or src_rank) not in [0, degree) */
+  TSP_ERR_SEQ = -13,         /* seq not a positive multiple of 2*degree */
+  TSP_ERR_HEADS = -14,       /* a head count < 1 or not a multiple of degree */
+  TSP_ERR_GQA = -15,         /* n_q_heads not a multiple of n_kv_heads */
+  TSP_ERR_HIDDEN = -16,      /* hidden not a positive multiple of 64 */
+  TSP_ERR_FFN = -17,         /* ffn not a positive multiple of 64, or ffn/degree not a multiple of 8 */
+  TSP_ERR_PARTITION = -18,   /* unknown token partition */
+  TSP_ERR_DTYPE = -19,       /* unknown tsp_dtype */
+  TSP_ERR_KMAX = -20,        /* kmax outside [0, seq] */
+  TSP_ERR_SCRATCH = -21      /* problem larger than the library's fixed scratch array */
 } tsp_status;
+
+/* Element types of tensors whose type the caller chooses. */
+typedef enum { TSP_BF16 = 0, TSP_F16 = 1, TSP_F32 = 2 } tsp_dtype;
 
 /* Selectors for tsp_workspace_bytes. */
 typedef enum {
@@ -130,51 +149,64 @@ int tsp_qkv_proj(const tsp_dims_t* dims, int32_t src_rank, const uint16_t* x_sha
                  hipStream_t stream);
 
 /* Reorder of the gathered K/V into natural sequence order through the
- * partition's position -> slot map (TSP article, "How to Fold a Book").  Bit-exact 16-bit copy of every key
- * position g < kmax; the positions [kmax, kmax_pad) are zero-filled.
+ * partition's position -> slot map (TSP article, "How to Fold a Book": the
+ * all-gathered K and V are reordered with the zigzag partition before
+ * attention).  Bit-exact 16-bit copy of every key position g < kmax; the
+ * positions [kmax, kmax_pad) are zero-filled.
  *   kv_gathered  f16, layout of tsp_qkv_proj, all D_src slots filled
- *   kv_natural   f16, TSP_FN_KV_NATURAL bytes:
+ *   kmax         number of leading positions to reorder: 0 means the rank's
+ *                own kmax (above); otherwise 1 <= kmax <= seq (else
+ *                TSP_ERR_KMAX).  kmax_pad = kmax rounded up to 64.
+ *   kv_natural   f16, 4*Hkv*B*kmax_pad*dh bytes (TSP_FN_KV_NATURAL gives it
+ *                for kmax = 0):
  *                K part  [Hkv][B][kmax_pad][dh]   (key-major rows)
  *                V part  [Hkv][B][dh][kmax_pad]   (transposed: dh-major)
  *                the V part starts right after the K part; the kv-head
  *                index is the global one, j*Hkv/D + (head within shard j). */
 int tsp_kv_reorder(const tsp_dims_t* dims, const uint16_t* kv_gathered,
-                   uint16_t* kv_natural, hipStream_t stream);
+                   uint16_t* kv_natural, int32_t kmax, hipStream_t stream);
 
 /* Attention half of the layer on rank dims->rank:
- *     out = x + sum_j O_j W_O,j^T,
+ *     out = residual + sum_j O_j W_O,j^T     (residual NULL: out = the sum),
  * O_j = causal attention of the rank's queries (q-heads of shard j) at their
  * partition positions over the K/V of shard j in natural sequence order (TSP
- * article, "How to Fold a Book"; the attention kernel applies the partition's
- * position -> slot map
- * while it loads K/V tiles from kv_gathered, so no reordered copy is made;
- * the head split with row-split output projection is exact:
- * bowenzhou.top "张量并行", section "机制：行切与列切").
+ * article, "How to Fold a Book": every rank projects its tokens with the
+ * broadcast W_Q/W_K/W_V/W_O of shard j, K/V are all-gathered and put in
+ * sequence order, then attention; the head split with a row-split output
+ * projection sums exactly: bowenzhou.top "张量并行", section "机制：行切与列切").
+ * The attention kernel applies the partition's position -> slot map while it
+ * loads K/V tiles from kv_gathered, so no reordered copy is made.
  *   x_local      bf16 [B][T][h]
  *   w_qkv        bf16, layout of tsp_qkv_proj;  w_o bf16 [D][h][Hq/D*dh]
  *                (shard j = W_o columns of its q-heads)
  *   kv_gathered  in: the other ranks' slots; out: this rank's slots
- *   out          float32 [B][T][h]
+ *   residual     float32 [B][T][h] or NULL (the attention branch alone)
+ *   out          float32 [B][T][h]; may alias residual
  *   ws           device workspace of >= tsp_workspace_bytes(dims, TSP_FN_ATTN)
  * Precision: Q/K/V, softmax probabilities and O are f16 with float32
  * accumulation and float32 online softmax; W_o is read as bf16 and rounded
  * to f16 for the matrix cores. */
 int tsp_attn_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
-                 const uint16_t* w_o, uint16_t* kv_gathered, float* out, void* ws,
-                 size_t ws_bytes, hipStream_t stream);
+                 const uint16_t* w_o, uint16_t* kv_gathered, const float* residual, float* out,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Gated-MLP weight ring on rank dims->rank (TSP article, "How to Fold a
  * Book": gate/up/down shards travel around a ring, partial outputs are
  * accumulated locally, no all-reduce; the column/row split sums exactly,
  * bowenzhou.top "张量并行", section "机制：行切与列切"):
- *     y = x + sum_{s=0}^{D-1} (silu(x Wg_j^T) * (x Wu_j^T)) Wd_j^T,  j = (r - s) mod D
- *   x        float32 [B][T][h] (rounded to f16 for the matrix cores)
+ *     y = residual + sum_{s=0}^{D-1} (silu(x Wg_j^T) * (x Wu_j^T)) Wd_j^T,  j = (r - s) mod D
+ * (residual NULL: y = the sum alone).
+ *   x        [B][T][h] of type x_dtype: TSP_BF16 (bf16 matrix cores on x as
+ *            given), TSP_F16, or TSP_F32 (rounded to f16 for the matrix
+ *            cores; values must lie in the f16 range)
  *   w_gate, w_up  bf16 [D][F/D][h] (= [F][h]);  w_down bf16 [D][h][F/D]
- *   y        float32 [B][T][h]; may alias x
+ *   residual float32 [B][T][h] or NULL
+ *   y        float32 [B][T][h]; may alias residual or x
  *   ws       >= tsp_workspace_bytes(dims, TSP_FN_MLP) bytes */
-int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const float* x, const uint16_t* w_gate,
-                     const uint16_t* w_up, const uint16_t* w_down, float* y, void* ws,
-                     size_t ws_bytes, hipStream_t stream);
+int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype,
+                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                     const float* residual, float* y, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* Whole layer on rank dims->rank: h = x + Attn(x), y = h + MLP(h), with the
  * argument layouts of tsp_attn_fwd and tsp_mlp_ring_fwd.  h stays float32;
@@ -215,6 +247,30 @@ int tsp_profile_kernel(int32_t kernel_id, int32_t max_launches);
  * of bracketed launches and their summed duration in milliseconds; the
  * profile stays armed for the same kernel with its counters reset. */
 int tsp_profile_result(int32_t* launches, float* total_ms);
+
+/* Kernel-choice overrides, for tests and tuning only.  The default dispatch
+ * depends on the shape alone; an override set here replaces one decision for
+ * every later launch in the process until it is reset (value < 0).  Not
+ * synchronised with launches in flight on other threads.
+ *   TSP_TUNE_GEMM_*    GEMM configuration index (see the GEMM source)
+ *   TSP_TUNE_SPLIT_*   split-K factor 1..4 of the output / down projection
+ *   TSP_TUNE_ATTN_SHAPE  4: 4 waves x 2 K/V stages, 8: 8 waves x 3 stages
+ *   TSP_TUNE_ATTN_PAIR   0 or 1: pair the two halves' row blocks or not
+ *   TSP_TUNE_ATTN_PIECES target number of attention work units (> 0) */
+typedef enum {
+  TSP_TUNE_GEMM_QKV = 0,
+  TSP_TUNE_GEMM_OPROJ = 1,
+  TSP_TUNE_GEMM_GATEUP = 2,
+  TSP_TUNE_GEMM_DOWN = 3,
+  TSP_TUNE_SPLIT_OPROJ = 4,
+  TSP_TUNE_SPLIT_DOWN = 5,
+  TSP_TUNE_ATTN_SHAPE = 6,
+  TSP_TUNE_ATTN_PAIR = 7,
+  TSP_TUNE_ATTN_PIECES = 8,
+  TSP_TUNE_COUNT = 9
+} tsp_tune_knob;
+
+int tsp_set_tuning(int32_t knob, int32_t value);
 
 /* Thread-local text describing the last non-zero return on this thread. */
 const char* tsp_last_error(void);

@@ -72,3 +72,34 @@ def f16_bits_to_f64(t):
 
 def dev():
     return torch.device("cuda:0")
+
+
+def block_edge_rows(T, c, rb=128, seed=0, n_extra=4):
+    """The first and last row of every rb-row block of both halves of the
+    rank's rows (each attention row block, with its split and paired key
+    pieces, is then compared at least twice), plus sample_rows'."""
+    rows = set(sample_rows(T, c, n_extra=n_extra, seed=seed).tolist())
+    for half0, half1 in ((0, c), (c, T)):
+        for b0 in range(half0, half1, rb):
+            rows.add(b0)
+            rows.add(min(b0 + rb, half1) - 1)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+class tuning:
+    """Context manager: kernel-choice overrides through tsp_set_tuning, reset
+    to the default dispatch on exit."""
+
+    def __init__(self, **knobs):
+        self.knobs = knobs
+
+    def __enter__(self):
+        from folded_tensor_sequence_amd import binding as B
+        for k, v in self.knobs.items():
+            B.tsp_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        from folded_tensor_sequence_amd import binding as B
+        B.reset_tuning()
+        return False

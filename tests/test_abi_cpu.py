@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd",
               "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",
-              "tsp_profile_kernel", "tsp_profile_result"):
+              "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning"):
         assert n in names
     assert set(names) == set(B.EXPORTED)
 
@@ -58,21 +58,22 @@ MISALIGNED = ctypes.c_void_p(0x10008)
 
 
 @pytest.mark.parametrize("kw,code,frag", [
-    (dict(batch=0), B.TSP_ERR_INVALID_ARG, "batch"),
-    (dict(degree=0), B.TSP_ERR_INVALID_ARG, "degree"),
-    (dict(rank=2), B.TSP_ERR_INVALID_ARG, "rank"),
-    (dict(rank=-1), B.TSP_ERR_INVALID_ARG, "rank"),
-    (dict(seq=250), B.TSP_ERR_INVALID_ARG, "seq"),
-    (dict(seq=2), B.TSP_ERR_INVALID_ARG, "seq"),
-    (dict(n_q_heads=3), B.TSP_ERR_INVALID_ARG, "multiples of degree"),
-    (dict(n_kv_heads=6, n_q_heads=4), B.TSP_ERR_INVALID_ARG, "multiple of n_kv_heads"),
-    (dict(hidden=200), B.TSP_ERR_INVALID_ARG, "hidden"),
-    (dict(ffn=100), B.TSP_ERR_INVALID_ARG, "ffn"),
-    (dict(ffn=64, degree=16, n_q_heads=16, n_kv_heads=16), B.TSP_ERR_INVALID_ARG, "ffn"),  # F/D = 4
-    (dict(ffn=128, degree=3, seq=258, n_q_heads=6, n_kv_heads=3), B.TSP_ERR_INVALID_ARG, "ffn"),
+    (dict(batch=0), B.TSP_ERR_BATCH, "batch"),
+    (dict(degree=0), B.TSP_ERR_DEGREE, "degree"),
+    (dict(rank=2), B.TSP_ERR_RANK, "rank"),
+    (dict(rank=-1), B.TSP_ERR_RANK, "rank"),
+    (dict(seq=250), B.TSP_ERR_SEQ, "seq"),
+    (dict(seq=2), B.TSP_ERR_SEQ, "seq"),
+    (dict(n_q_heads=3), B.TSP_ERR_HEADS, "multiples of degree"),
+    (dict(n_q_heads=0), B.TSP_ERR_HEADS, "head counts"),
+    (dict(n_kv_heads=6, n_q_heads=4), B.TSP_ERR_GQA, "multiple of n_kv_heads"),
+    (dict(hidden=200), B.TSP_ERR_HIDDEN, "hidden"),
+    (dict(ffn=100), B.TSP_ERR_FFN, "ffn"),
+    (dict(ffn=64, degree=16, n_q_heads=16, n_kv_heads=16), B.TSP_ERR_FFN, "ffn"),  # F/D = 4
+    (dict(ffn=128, degree=3, seq=258, n_q_heads=6, n_kv_heads=3), B.TSP_ERR_FFN, "ffn"),
     (dict(head_dim=96), B.TSP_ERR_UNSUPPORTED, "head_dim"),
-    (dict(partition=2), B.TSP_ERR_INVALID_ARG, "partition"),
-    (dict(partition=-1), B.TSP_ERR_INVALID_ARG, "partition"),
+    (dict(partition=2), B.TSP_ERR_PARTITION, "partition"),
+    (dict(partition=-1), B.TSP_ERR_PARTITION, "partition"),
 ])
 def test_invalid_dims_rejected(lib, kw, code, frag):
     d = _dims(**kw)
@@ -90,30 +91,49 @@ def test_valid_edge_dims_accepted(lib):
 
 
 def test_null_dims(lib):
-    assert lib.tsp_zigzag_index(None, FAKE, None, None) == B.TSP_ERR_INVALID_ARG
+    assert lib.tsp_zigzag_index(None, FAKE, None, None) == B.TSP_ERR_NULL_POINTER
     assert "dims" in lib.tsp_last_error().decode()
+
+
+def test_error_codes_are_distinct():
+    codes = {k: v for k, v in vars(B).items() if k.startswith("TSP_ERR_")}
+    assert len(set(codes.values())) == len(codes)
+    # the header declares the same set with the same values
+    text = open(HEADER).read()
+    declared = dict((n, int(v)) for n, v in re.findall(r"\b(TSP_ERR_\w+)\s*=\s*(-?\d+)", text))
+    assert declared == codes
 
 
 def test_null_and_misaligned_pointers(lib):
     d = _dims()
     big = 1 << 40
     rc = lib.tsp_layer_fwd(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
-    assert rc == B.TSP_ERR_INVALID_ARG and "x_local is NULL" in lib.tsp_last_error().decode()
+    assert rc == B.TSP_ERR_NULL_POINTER and "x_local is NULL" in lib.tsp_last_error().decode()
     rc = lib.tsp_layer_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE,
                            big, None)
-    assert rc == B.TSP_ERR_INVALID_ARG and "w_down is not 16-byte aligned" in lib.tsp_last_error().decode()
-    rc = lib.tsp_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None)
-    assert rc == B.TSP_ERR_INVALID_ARG and "out is NULL" in lib.tsp_last_error().decode()
-    rc = lib.tsp_mlp_ring_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, big, None)
-    assert rc == B.TSP_ERR_INVALID_ARG and "ws is NULL" in lib.tsp_last_error().decode()
+    assert rc == B.TSP_ERR_MISALIGNED and "w_down is not 16-byte aligned" in lib.tsp_last_error().decode()
+    rc = lib.tsp_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, big, None)
+    assert rc == B.TSP_ERR_NULL_POINTER and "out is NULL" in lib.tsp_last_error().decode()
+    rc = lib.tsp_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, big, None)
+    assert rc == B.TSP_ERR_MISALIGNED and "residual" in lib.tsp_last_error().decode()
+    rc = lib.tsp_mlp_ring_fwd(ctypes.byref(d), FAKE, B.TSP_F32, FAKE, FAKE, FAKE, None, FAKE, None, big, None)
+    assert rc == B.TSP_ERR_NULL_POINTER and "ws is NULL" in lib.tsp_last_error().decode()
+    rc = lib.tsp_mlp_ring_fwd(ctypes.byref(d), FAKE, B.TSP_F32, FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, big, None)
+    assert rc == B.TSP_ERR_MISALIGNED and "residual" in lib.tsp_last_error().decode()
+    for bad in (3, -1):
+        rc = lib.tsp_mlp_ring_fwd(ctypes.byref(d), FAKE, bad, FAKE, FAKE, FAKE, None, FAKE, FAKE, big, None)
+        assert rc == B.TSP_ERR_DTYPE and "x_dtype" in lib.tsp_last_error().decode()
     rc = lib.tsp_qkv_proj(ctypes.byref(d), 2, FAKE, FAKE, None, FAKE, None)
-    assert rc == B.TSP_ERR_INVALID_ARG and "src_rank" in lib.tsp_last_error().decode()
+    assert rc == B.TSP_ERR_RANK and "src_rank" in lib.tsp_last_error().decode()
     rc = lib.tsp_qkv_proj(ctypes.byref(d), 1, FAKE, FAKE, MISALIGNED, FAKE, None)
-    assert rc == B.TSP_ERR_INVALID_ARG and "q_out" in lib.tsp_last_error().decode()
-    rc = lib.tsp_kv_reorder(ctypes.byref(d), FAKE, None, None)
-    assert rc == B.TSP_ERR_INVALID_ARG
+    assert rc == B.TSP_ERR_MISALIGNED and "q_out" in lib.tsp_last_error().decode()
+    rc = lib.tsp_kv_reorder(ctypes.byref(d), FAKE, None, 0, None)
+    assert rc == B.TSP_ERR_NULL_POINTER
+    for bad in (-1, 257):
+        rc = lib.tsp_kv_reorder(ctypes.byref(d), FAKE, FAKE, bad, None)
+        assert rc == B.TSP_ERR_KMAX and "kmax" in lib.tsp_last_error().decode()
     rc = lib.tsp_zigzag_index(ctypes.byref(d), None, None, None)
-    assert rc == B.TSP_ERR_INVALID_ARG
+    assert rc == B.TSP_ERR_NULL_POINTER
 
 
 def test_workspace_too_small(lib):
@@ -123,18 +143,29 @@ def test_workspace_too_small(lib):
                            need - 1, None)
     assert rc == B.TSP_ERR_WORKSPACE
     need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_ATTN)
-    assert lib.tsp_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+    assert lib.tsp_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, None) == \
         B.TSP_ERR_WORKSPACE
     need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_MLP)
-    assert lib.tsp_mlp_ring_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
-        B.TSP_ERR_WORKSPACE
+    assert lib.tsp_mlp_ring_fwd(ctypes.byref(d), FAKE, B.TSP_BF16, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1,
+                                None) == B.TSP_ERR_WORKSPACE
     assert lib.tsp_workspace_bytes(ctypes.byref(d), 99) == 0
+
+
+def test_tuning_knobs(lib):
+    assert lib.tsp_set_tuning(B.TUNE["attn_pair"], 0) == B.TSP_OK
+    assert lib.tsp_set_tuning(B.TUNE["attn_pair"], -1) == B.TSP_OK
+    assert lib.tsp_set_tuning(99, 1) == B.TSP_ERR_INVALID_ARG
+    assert lib.tsp_set_tuning(-1, 1) == B.TSP_ERR_INVALID_ARG
+    # the header's knob list matches the binding's
+    text = open(HEADER).read()
+    declared = dict((n, int(v)) for n, v in re.findall(r"\bTSP_TUNE_(\w+)\s*=\s*(\d+)", text))
+    assert {k.lower(): v for k, v in declared.items() if k != "COUNT"} == B.TUNE
 
 
 def test_profile_arguments(lib):
     assert lib.tsp_profile_kernel(99, 1) == B.TSP_ERR_INVALID_ARG
     assert lib.tsp_profile_kernel(0, 0) == B.TSP_OK          # disarm is always fine
-    assert lib.tsp_profile_result(None, None) == B.TSP_ERR_INVALID_ARG
+    assert lib.tsp_profile_result(None, None) == B.TSP_ERR_NULL_POINTER
 
 
 def test_no_device_gives_hip_error(lib):
@@ -196,3 +227,74 @@ def test_dims_struct_carries_the_partition():
     d = synth.Dims(1, 256, 2, 0, 256, 4, 4, 64, 768, partition=1)
     assert B.dims_struct(d).partition == 1
     assert B.dims_struct(synth.Dims(1, 256, 2, 0, 256, 4, 4, 64, 768)).partition == 0
+
+
+# --------------------------------------------------------------------------- #
+# The binding rejects tensors that do not fit the ABI before calling the library
+# --------------------------------------------------------------------------- #
+def _tiny():
+    return synth.WORKLOADS["tiny_d2"].dims
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    d = _tiny()
+    T = d.seq // d.degree
+    x = torch.zeros((d.batch, T, d.hidden), dtype=torch.int16)        # on the host
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.tsp_qkv_proj(d, 0, x, x, None, x)
+    l2g = torch.zeros(T, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.tsp_zigzag_index(d, l2g)
+
+
+class _FakeCuda:
+    """Stands in for a GPU tensor on a machine without one (only the fields the
+    binding's checks read); its pointer is never used because every case below
+    fails a check first."""
+
+    def __init__(self, n, dtype, contiguous=True):
+        import torch
+        self._t = torch.empty(n, dtype=dtype)
+        self.dtype = dtype
+        self._contig = contiguous
+        self.is_cuda = True
+        self.device = "cuda:0"
+
+    def is_contiguous(self):
+        return self._contig
+
+    def numel(self):
+        return self._t.numel()
+
+    def element_size(self):
+        return self._t.element_size()
+
+
+@pytest.mark.parametrize("case", ["dtype", "short", "noncontig", "notensor"])
+def test_binding_checks_dtype_size_layout(case, monkeypatch):
+    import torch
+    monkeypatch.setattr(torch, "Tensor", _FakeCuda)       # isinstance() accepts the fake
+    d = _tiny()
+    z = B._Sizes(d)
+    if case == "dtype":
+        t, msg = _FakeCuda(z.rows, torch.float32), "must be bf16"
+    elif case == "short":
+        t, msg = _FakeCuda(z.rows - 1, torch.int16), "bytes, the ABI layout needs"
+    elif case == "noncontig":
+        t, msg = _FakeCuda(z.rows, torch.int16, contiguous=False), "contiguous"
+    else:
+        t, msg = object(), "torch.Tensor"
+    with pytest.raises(ValueError, match=msg):
+        B._tensor(t, "x_local", "bf16", z.x16)
+
+
+def test_binding_sizes_follow_the_header():
+    d = synth.WORKLOADS["llama7b_s8k_d8"].dims
+    z = B._Sizes(d)
+    assert z.x16 == 1024 * 4096 * 2 and z.f32 == 1024 * 4096 * 4
+    assert z.w_qkv == 2 * 96 * 128 * 4096 and z.w_o == 2 * 4096 * 4096 and z.w_ffn == 2 * 11008 * 4096
+    assert z.q == 2 * 1024 * 32 * 128
+    # default kmax of rank 0 = (2D - r) c = 16 * 512; natural K and V, 32 heads
+    assert z.kv_natural(0) == 4 * 32 * 8192 * 128
+    assert z.kv_natural(100) == 4 * 32 * 128 * 128

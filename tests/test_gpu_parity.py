@@ -14,8 +14,8 @@ from folded_tensor_sequence_amd import binding as B
 from folded_tensor_sequence_amd.harness import RankProblem, pack_weights
 from oracle import tsp_oracle as orc
 
-from gpu_util import (MAX_ABS, REL_FROB, SWEEP, assert_close, dims_of, errors, f16_bits_to_f64, inputs_for,
-                      sample_rows)
+from gpu_util import (MAX_ABS, REL_FROB, SWEEP, assert_close, block_edge_rows, dims_of, errors, f16_bits_to_f64,
+                      inputs_for, tuning)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,19 +63,30 @@ REORDER_SHAPES = dict(SWEEP, tiny=synth.WORKLOADS["tiny_d2"].dims.astuple(),
 
 @pytest.mark.parametrize("name", list(REORDER_SHAPES))
 def test_kv_reorder_bitexact(name):
+    _check_kv_reorder(name, 0)
+
+
+# A caller-chosen kmax (0 = the rank's own): one key, a ragged tail, every key.
+@pytest.mark.parametrize("name", ["mha_d2_r1", "gqa8_b2_c96", "c24_generic_reorder", "split_keys_d8_r5"])
+@pytest.mark.parametrize("which", ["one", "ragged", "all"])
+def test_kv_reorder_explicit_kmax(name, which):
+    S = dims_of(REORDER_SHAPES[name]).seq
+    _check_kv_reorder(name, {"one": 1, "ragged": min(S, 65 + S // 3), "all": S}[which])
+
+
+def _check_kv_reorder(name, kmax_arg):
     d = dims_of(REORDER_SHAPES[name])
-    _case(f"kv_reorder {name} {d}")
+    _case(f"kv_reorder {name} kmax={kmax_arg} {d}")
     Bn, S, D, r, dh = d.batch, d.seq, d.degree, d.rank, d.head_dim
     T, c = S // D, S // (2 * D)
     hkv_s = d.n_kv_heads // D
-    kmax = (2 * D - r) * c
+    kmax = (2 * D - r) * c if kmax_arg == 0 else kmax_arg
     kpad = -(-kmax // 64) * 64
     rng = np.random.default_rng(5)
     n = B.tsp_workspace_bytes(d, B.TSP_FN_KV_GATHERED) // 2
     gathered = rng.integers(-32768, 32767, size=n, dtype=np.int16)
-    nat = torch.full((B.tsp_workspace_bytes(d, B.TSP_FN_KV_NATURAL) // 2,), 0x5A5A, dtype=torch.int16,
-                     device="cuda")
-    B.tsp_kv_reorder(d, torch.from_numpy(gathered).cuda(), nat)
+    nat = torch.full((2 * d.n_kv_heads * Bn * kpad * dh,), 0x5A5A, dtype=torch.int16, device="cuda")
+    B.tsp_kv_reorder(d, torch.from_numpy(gathered).cuda(), nat, kmax_arg)
     torch.cuda.synchronize()
     got = nat.cpu().numpy()
     g6 = gathered.reshape(D, D, 2, Bn, T, hkv_s, dh)        # [j][src][kv][b][t][hk][d]
@@ -139,45 +150,59 @@ def test_attn_fwd(name):
     _check_attn_fwd(name, f"attn_fwd {name}")
 
 
-# The attention work plan without pairing (the library's tuning variable): the
-# earlier zigzag chunk's row blocks get work units of their own instead of
-# running inside the last key piece of their later-chunk partner.
+# The attention work plan without pairing (a tuning override): the earlier
+# zigzag chunk's row blocks get work units of their own instead of running
+# inside the last key piece of their later-chunk partner.
 @pytest.mark.parametrize("name", ["split_keys_dh128", "split_keys_gqa_b2", "wide_tiles_dh128", "mha_d2_r1"])
-def test_attn_fwd_unpaired_plan(name, monkeypatch):
-    monkeypatch.setenv("TSP_ATTN_PAIR", "0")
-    _check_attn_fwd(name, f"attn_fwd {name} unpaired")
+def test_attn_fwd_unpaired_plan(name):
+    with tuning(attn_pair=0):
+        _check_attn_fwd(name, f"attn_fwd {name} unpaired")
 
 
-# The attention kernel's other shape (the library's tuning variable): 8 waves
-# (256 query rows) per block sharing each K/V tile, 3 tiles in the LDS ring;
-# head_dim 64 and 128, whole-tile and per-row K/V addressing (chunks that are
-# not multiples of 64 keys).
-@pytest.mark.parametrize("shape", ["8x3"])
+# The attention kernel's other shape (a tuning override): 8 waves (256 query
+# rows) per block sharing each K/V tile, 3 tiles in the LDS ring; head_dim 64
+# and 128, whole-tile and per-row K/V addressing (chunks that are not
+# multiples of 64 keys).
 @pytest.mark.parametrize("name", ["split_keys_dh128", "split_keys_gqa_b2", "gqa8_b2_c96", "c24_generic_reorder",
                                   "wide_tiles_dh128"])
-def test_attn_fwd_block_shapes(name, shape, monkeypatch):
-    monkeypatch.setenv("TSP_ATTN_SHAPE", shape)
-    _check_attn_fwd(name, f"attn_fwd {name} shape={shape}")
+def test_attn_fwd_block_shapes(name):
+    with tuning(attn_shape=8):
+        _check_attn_fwd(name, f"attn_fwd {name} shape=8x3")
 
 
 def _check_attn_fwd(name, case):
+    """out = residual + attention branch, three ways: residual = x (the
+    layer's h), no residual (the branch alone, against the oracle's O W_o^T),
+    and out written over its own residual buffer."""
     shape, sigma, seed = _shape(name)
     d = dims_of(shape)
     _case(case)
     inp = inputs_for(shape, sigma, seed)
     prob = RankProblem.build(d, inp)
     T = d.seq // d.degree
+    ref = orc.layer_rank_rows(inp, d)
+    x32 = torch.from_numpy(np.ascontiguousarray(ref["x"], dtype=np.float32)).cuda()
     out = torch.empty((d.batch, T, d.hidden), dtype=torch.float32, device="cuda")
     ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN), dtype=torch.uint8, device="cuda")
-    B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, out, ws)
+    B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, out, ws, residual=x32)
     torch.cuda.synchronize()
-    ref = orc.layer_rank_rows(inp, d)
     assert_close(out.cpu().numpy(), ref["h"], what="h = x + attn")
-    # the attention branch alone, relative to its own size
-    x = ref["x"]
-    _, rf = errors(out.cpu().numpy() - x, ref["attn"])
-    print(f"  attn branch rel_frob={rf:.3e}", flush=True)
-    assert rf <= 5e-3
+    # the attention branch alone (residual NULL), element by element: max-abs
+    # relative to the branch's own size, Frobenius relative
+    branch = torch.empty_like(out)
+    B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, branch, ws)
+    torch.cuda.synchronize()
+    ma, rf = errors(branch.cpu().numpy(), ref["attn"])
+    ma_rel = ma / float(np.abs(ref["attn"]).max())
+    print(f"  attn branch max_abs/max={ma_rel:.3e} rel_frob={rf:.3e}", flush=True)
+    assert np.all(np.isfinite(branch.cpu().numpy()))
+    assert ma_rel <= MAX_ABS and rf <= REL_FROB
+    # in place: out aliases the residual; same bits as the separate output
+    inplace = x32.clone()
+    B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, inplace, ws,
+                   residual=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(inplace, out)
 
 
 # Sharp softmax: weights 12.5x the usual scale make the logits' spread about
@@ -200,7 +225,7 @@ def test_attn_fwd_sharp_softmax(name):
     B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, out, ws)
     torch.cuda.synchronize()
     ref = orc.layer_rank_rows(inp, d)
-    branch = out.cpu().numpy().astype(np.float64) - ref["x"]
+    branch = out.cpu().numpy().astype(np.float64)
     ma, rf = errors(branch, ref["attn"])
     ma_rel = ma / float(np.abs(ref["attn"]).max())
     print(f"  attn branch max_abs/max={ma_rel:.3e} rel_frob={rf:.3e}", flush=True)
@@ -215,21 +240,60 @@ def test_mlp_ring_fwd(name):
     _case(f"mlp_ring_fwd {name}")
     inp = inputs_for(shape, sigma, seed)
     w = {k: v.cuda() for k, v in pack_weights(inp, d).items()}
-    T = d.seq // d.degree
     # MLP input: this rank's bf16 rows of X, handed over as float32
     l2g = orc.local_to_global(d.seq, d.degree, d.rank)
     x = np.ascontiguousarray(orc.bf16_bits_to_f64(inp["x"][:, l2g]), dtype=np.float32)
     xt = torch.from_numpy(x).cuda()
     y = torch.empty_like(xt)
     ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP), dtype=torch.uint8, device="cuda")
-    B.tsp_mlp_ring_fwd(d, xt, w["w_gate"], w["w_up"], w["w_down"], y, ws)
+    B.tsp_mlp_ring_fwd(d, xt, w["w_gate"], w["w_up"], w["w_down"], y, ws, residual=xt)
     torch.cuda.synchronize()
     ref = np.stack([orc.mlp_block(inp, x[b].astype(np.float64)) for b in range(d.batch)])
     assert_close(y.cpu().numpy(), ref, what="y = x + mlp")
-    # in place (y aliases x)
-    B.tsp_mlp_ring_fwd(d, xt, w["w_gate"], w["w_up"], w["w_down"], xt, ws)
+    # in place (y aliases x and the residual)
+    B.tsp_mlp_ring_fwd(d, xt, w["w_gate"], w["w_up"], w["w_down"], xt, ws, residual=xt)
     torch.cuda.synchronize()
     assert torch.equal(xt, y)
+
+
+# The MLP branch alone (residual NULL) for each input type: bf16 x feeds bf16
+# matrix cores as given, f16 x is used as given, float32 x is rounded to f16.
+# The reference is the oracle's gated MLP of exactly the values handed over;
+# max-abs relative to the branch's size, Frobenius relative.
+@pytest.mark.parametrize("name", ["tiny", "mha_d2_r1", "ffn_tail_d4_r3", "gqa8_b2_c96", "wide_tiles_dh128"])
+@pytest.mark.parametrize("xdt", ["bf16", "f16", "f32"])
+def test_mlp_ring_fwd_branch_dtypes(name, xdt):
+    shape, sigma, seed = _shape(name)
+    d = dims_of(shape)
+    _case(f"mlp_ring_fwd {name} x={xdt} residual=NULL")
+    inp = inputs_for(shape, sigma, seed)
+    w = {k: v.cuda() for k, v in pack_weights(inp, d).items()}
+    l2g = orc.local_to_global(d.seq, d.degree, d.rank)
+    bits = np.ascontiguousarray(inp["x"][:, l2g])
+    x64 = orc.bf16_bits_to_f64(bits)
+    if xdt == "bf16":
+        xt, xval = torch.from_numpy(bits.view(np.int16)).cuda(), x64
+        kw = {"x_dtype": B.TSP_BF16}
+    elif xdt == "f16":
+        h = (x64 * 1.25).astype(np.float16)                # not all bf16-representable
+        xt, xval = torch.from_numpy(h).cuda(), h.astype(np.float64)
+        kw = {}
+    else:
+        f = (x64 * 1.25).astype(np.float32)
+        xt, xval = torch.from_numpy(f).cuda(), f.astype(np.float64)
+        kw = {}
+    y = torch.empty((d.batch, d.seq // d.degree, d.hidden), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP), dtype=torch.uint8, device="cuda")
+    B.tsp_mlp_ring_fwd(d, xt, w["w_gate"], w["w_up"], w["w_down"], y, ws, **kw)
+    torch.cuda.synchronize()
+    wg, wu, wd = (orc.bf16_bits_to_f64(inp[n]) for n in ("w_g", "w_u", "w_d"))
+    ref = np.stack([orc.swiglu_mlp(xval[b], wg, wu, wd) for b in range(d.batch)])
+    got = y.cpu().numpy()
+    ma, rf = errors(got, ref)
+    ma_rel = ma / float(np.abs(ref).max())
+    print(f"  mlp branch max_abs/max={ma_rel:.3e} rel_frob={rf:.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert ma_rel <= MAX_ABS and rf <= REL_FROB
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -249,54 +313,57 @@ def test_layer_fwd(name):
     assert torch.equal(y, y2)
 
 
-# The alternative GEMM kernels: the direct-load ring kernel (the fallback when
-# operands need 64-bit offsets; its configuration is chosen here through the
-# library's tuning variables), the staged kernel with two register sets or
-# four waves, and split-K factors 2 and 3 for the output and down projections.
+# The alternative GEMM kernels, chosen through tuning overrides: the
+# direct-load ring kernel (the fallback when operands need 64-bit offsets),
+# the staged kernel with two register sets or four waves, and split-K
+# factors 2 and 3 for the output and down projections.
 ALT_GEMMS = {
-    "ring": {"TSP_GEMM_QKV": "3", "TSP_GEMM_OPROJ": "3:2", "TSP_GEMM_DOWN": "3:2", "TSP_GEMM_GATEUP": "2"},
-    "staged_two_sets": {"TSP_GEMM_OPROJ": "7:2", "TSP_GEMM_DOWN": "7:2", "TSP_GEMM_GATEUP": "4"},
-    "staged_4wave": {"TSP_GEMM_QKV": "2", "TSP_GEMM_OPROJ": "1:2", "TSP_GEMM_DOWN": "1:2", "TSP_GEMM_GATEUP": "1"},
+    "ring": dict(gemm_qkv=3, gemm_oproj=3, split_oproj=2, gemm_down=3, split_down=2, gemm_gateup=2),
+    "staged_two_sets": dict(gemm_oproj=7, split_oproj=2, gemm_down=7, split_down=2, gemm_gateup=4),
+    "staged_4wave": dict(gemm_qkv=2, gemm_oproj=1, split_oproj=2, gemm_down=1, split_down=2, gemm_gateup=1),
     # split-K factors other than the plan's (small shapes plan 4)
-    "split_k_2": {"TSP_GEMM_OPROJ": "6:2", "TSP_GEMM_DOWN": "6:2"},
-    "split_k_3": {"TSP_GEMM_OPROJ": "6:3", "TSP_GEMM_DOWN": "6:3"},
+    "split_k_2": dict(gemm_oproj=6, split_oproj=2, gemm_down=6, split_down=2),
+    "split_k_3": dict(gemm_oproj=6, split_oproj=3, gemm_down=6, split_down=3),
 }
 
 
 @pytest.mark.parametrize("name", ["mha_d2_r1", "ffn_tail_d4_r3", "gqa2_b2_dh128_c80"])
 @pytest.mark.parametrize("alt", list(ALT_GEMMS))
-def test_layer_fwd_alternative_gemms(name, alt, monkeypatch):
-    for k, v in ALT_GEMMS[alt].items():
-        monkeypatch.setenv(k, v)
+def test_layer_fwd_alternative_gemms(name, alt):
     shape, sigma, seed = _shape(name)
     d = dims_of(shape)
     _case(f"layer_fwd {name} gemms={alt}")
     inp = inputs_for(shape, sigma, seed)
-    prob = RankProblem.build(d, inp)
-    y = prob.layer().clone()
-    torch.cuda.synchronize()
+    with tuning(**ALT_GEMMS[alt]):
+        prob = RankProblem.build(d, inp)
+        y = prob.layer().clone()
+        torch.cuda.synchronize()
     ref = orc.layer_rank_rows(inp, d)
     assert_close(y.cpu().numpy(), ref["y"], what="y")
 
 
 # --------------------------------------------------------------------------- #
 # Full-size workloads in the benchmark's launch configuration: the whole
-# layer runs on the GPU, sampled rows are checked against the oracle.
+# layer runs on the GPU.  The 8K and GQA 16K layers are compared on every
+# row; the 70B-like and 128K layers on the first and last row of every
+# 128-row block (every attention row block, with its key pieces) plus the
+# chunk edges and a few seeded rows.
 # --------------------------------------------------------------------------- #
 FULL = ["llama7b_s8k_d8", "llama3_8b_gqa_s16k_d8", "wide70b_s32k_d8", "longctx_s128k_d8"]
+EVERY_ROW = {"llama7b_s8k_d8", "llama3_8b_gqa_s16k_d8"}
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_layer_fwd_full_size_sampled(name):
+def test_layer_fwd_full_size(name):
     wl = synth.WORKLOADS[name]
     d = wl.dims
-    _case(f"layer_fwd full {name}")
+    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
+    rows = np.arange(T) if name in EVERY_ROW else block_edge_rows(T, c, seed=wl.seed)
+    _case(f"layer_fwd full {name}: {len(rows)} of {T} rows per sequence")
     inp = synth.make_inputs(d, wl.sigma, wl.seed)
     prob = RankProblem.build(d, inp)
     y = prob.layer()
     torch.cuda.synchronize()
-    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
-    rows = sample_rows(T, c, n_extra=4, seed=wl.seed)
     yg = y.cpu().numpy()
     del prob
     torch.cuda.empty_cache()
@@ -305,4 +372,4 @@ def test_layer_fwd_full_size_sampled(name):
         # the max-abs bar is met except on the 70B-like layer, whose f16 storage
         # floor alone is 2.50e-2 (tests/test_rounding_floor.py); rel-Frobenius always
         max_abs = 3e-2 if name == "wide70b_s32k_d8" else 2e-2
-        assert_close(yg[b, rows], ref["y"], max_abs=max_abs, what=f"y b={b} rows={rows.tolist()}")
+        assert_close(yg[b, rows], ref["y"], max_abs=max_abs, what=f"y b={b} ({len(rows)} rows)")

@@ -19,7 +19,7 @@ from folded_tensor_sequence_amd import binding as B
 from folded_tensor_sequence_amd.harness import RankProblem
 from oracle import tsp_oracle as orc
 
-from gpu_util import SWEEP, assert_close, dims_of, errors, inputs_for, sample_rows
+from gpu_util import SWEEP, assert_close, dims_of, errors, inputs_for, tuning
 
 pytestmark = pytest.mark.gpu
 
@@ -111,15 +111,19 @@ def _attn_check(name, sigma=0.02, seed=101, check_h=True):
     inp = inputs_for(shape, sigma, seed)
     prob = RankProblem.build(d, inp)
     T = d.seq // d.degree
+    ref = orc.layer_rank_rows(inp, d)
     out = torch.empty((d.batch, T, d.hidden), dtype=torch.float32, device="cuda")
     ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN), dtype=torch.uint8, device="cuda")
+    if check_h:
+        x32 = torch.from_numpy(np.ascontiguousarray(ref["x"], dtype=np.float32)).cuda()
+        B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, out, ws, residual=x32)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref["h"], what="h = x + attn")
+    # the attention branch alone (no residual)
     B.tsp_attn_fwd(d, prob.x_local, prob.w["w_qkv"], prob.w["w_o"], prob.kv_gathered, out, ws)
     torch.cuda.synchronize()
-    ref = orc.layer_rank_rows(inp, d)
     got = out.cpu().numpy()
-    if check_h:
-        assert_close(got, ref["h"], what="h = x + attn")
-    branch = got.astype(np.float64) - ref["x"]
+    branch = got.astype(np.float64)
     ma, rf = errors(branch, ref["attn"])
     ma_rel = ma / float(np.abs(ref["attn"]).max())
     print(f"  attn branch max_abs/max={ma_rel:.3e} rel_frob={rf:.3e}", flush=True)
@@ -136,12 +140,11 @@ def test_striped_attn_fwd(name):
 # The plan variants: no pairing of the two halves' blocks, and the 8-wave
 # block shape, on shapes whose blocks are cut into key pieces.
 @pytest.mark.parametrize("name", ["split_keys_dh128", "split_keys_d8_r5", "d5_r4_b2_per_key"])
-@pytest.mark.parametrize("variant", [{"TSP_ATTN_PAIR": "0"}, {"TSP_ATTN_SHAPE": "8x3"}], ids=["unpaired", "8x3"])
-def test_striped_attn_fwd_plan_variants(name, variant, monkeypatch):
-    for k, v in variant.items():
-        monkeypatch.setenv(k, v)
+@pytest.mark.parametrize("variant", [{"attn_pair": 0}, {"attn_shape": 8}], ids=["unpaired", "8x3"])
+def test_striped_attn_fwd_plan_variants(name, variant):
     _case(f"striped attn_fwd {name} {variant}")
-    _attn_check(name)
+    with tuning(**variant):
+        _attn_check(name)
 
 
 # Sharp softmax (weights 12.5x the usual scale, logit spread ~16): the
@@ -172,22 +175,22 @@ def test_striped_layer_fwd(name):
 # Full-size layers with the striped partition, in the benchmark's launch
 # configuration: the Llama-7B-like 8K layer on the first and last ranks
 # (attention blocks cut into key pieces and paired) and the GQA 16K layer
-# (B = 2, rank 3); sampled rows against the oracle.
+# (B = 2, rank 3); every row of every sequence against the oracle.
 @pytest.mark.parametrize("name,rank", [("llama7b_s8k_d8", 0), ("llama7b_s8k_d8", 7),
                                        ("llama3_8b_gqa_s16k_d8", 3)])
-def test_striped_layer_fwd_full_size_sampled(name, rank):
+def test_striped_layer_fwd_full_size(name, rank):
     wl = synth.WORKLOADS[name]
     d = dataclasses.replace(wl.dims, rank=rank, partition=STRIPED)
-    _case(f"striped layer_fwd full {wl.name} rank={rank}")
+    T = d.seq // d.degree
+    _case(f"striped layer_fwd full {wl.name} rank={rank}: all {T} rows per sequence")
     inp = synth.make_inputs(d, wl.sigma, wl.seed)
     prob = RankProblem.build(d, inp)
     y = prob.layer()
     torch.cuda.synchronize()
-    T, c = d.seq // d.degree, d.seq // (2 * d.degree)
-    rows = sample_rows(T, c, n_extra=4, seed=wl.seed)
     yg = y.cpu().numpy()
     del prob
     torch.cuda.empty_cache()
+    rows = np.arange(T)
     for b in range(d.batch):
         ref = orc.rank_rows_forward(inp, d, b, rows)
-        assert_close(yg[b, rows], ref["y"], what=f"y b={b} rows={rows.tolist()}")
+        assert_close(yg[b], ref["y"], what=f"y b={b} (all {T} rows)")

@@ -38,3 +38,6 @@ def test_bench_prints_one_json_line(partition):
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert r["launches"] == 3
     assert set(j["kernels_ms"]) == {"qkv", "attn", "oproj", "gateup", "down"}
+    assert j["seeds"]["inputs"] == 2 and j["host"]["cores"] >= 1
+    assert j["versions"]["torch"] and len(j["versions"]["libtsp_sources_sha256"]) == 16
+    assert j["parity"] is None            # the oracle legs are off in this short run
