@@ -56,7 +56,10 @@ TUNE = {"gemm_qkv": 0, "gemm_oproj": 1, "gemm_gateup": 2, "gemm_down": 3, "split
 
 EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd",
             "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",
-            "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning")
+            "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning", "tsp_layer_fwd_noalloc")
+
+# Size of the library's fixed scratch array (TSP_SCRATCH_BYTES in include/tsp.h).
+TSP_SCRATCH_BYTES = 128 * 1024 * 1024
 
 
 class TspDims(ctypes.Structure):
@@ -92,6 +95,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tsp_attn_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_mlp_ring_fwd": [dp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_layer_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_layer_fwd_noalloc": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -286,6 +290,18 @@ def tsp_layer_fwd(dims, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, 
                                 _tensor(kv_gathered, "kv_gathered", "f16",
                                         tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
                                 _tensor(y, "y", "f32", z.f32), wsp, wsn, _s(stream)))
+
+
+def tsp_layer_fwd_noalloc(dims, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, stream=None):
+    """tsp_layer_fwd on the library's fixed scratch array (no workspace, no allocation)."""
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    _check(load().tsp_layer_fwd_noalloc(
+        ctypes.byref(d), _tensor(x_local, "x_local", "bf16", z.x16), _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv),
+        _tensor(w_o, "w_o", "bf16", z.w_o), _tensor(w_gate, "w_gate", "bf16", z.w_ffn),
+        _tensor(w_up, "w_up", "bf16", z.w_ffn), _tensor(w_down, "w_down", "bf16", z.w_ffn),
+        _tensor(kv_gathered, "kv_gathered", "f16", tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+        _tensor(y, "y", "f32", z.f32), _s(stream)))
 
 
 def tsp_set_tuning(knob, value: int | None):

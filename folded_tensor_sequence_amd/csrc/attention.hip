@@ -46,10 +46,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <functional>
-#include <queue>
+#include <algorithm>
 #include <type_traits>
-#include <vector>
 
 #include "attn_plan.h"
 #include "common.h"
@@ -556,8 +554,13 @@ static AttnShape attn_shape(const Shape& s) {
 // or the partial state, the merge).
 static long long plan_makespan(const PlanKey& k, int per_bh, long long slots) {
   constexpr int kUnitCost = 2;
-  std::priority_queue<long long, std::vector<long long>, std::greater<long long>> q;
-  for (long long i = 0; i < slots; ++i) q.push(0);
+  // min-heap of the resident work groups' finishing times (at most 512 of
+  // them: a fixed array, so planning allocates nothing)
+  constexpr int kMaxSlots = 512;
+  long long heap[kMaxSlots];
+  const int n = (int)(slots < kMaxSlots ? slots : kMaxSlots);
+  for (int i = 0; i < n; ++i) heap[i] = 0;
+  const auto later = [](long long x, long long y) { return x > y; };
   long long end = 0;
   for (int bi = 0; bi < 2 * k.nrb; ++bi) {
     const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
@@ -571,10 +574,10 @@ static long long plan_makespan(const PlanKey& k, int per_bh, long long slots) {
         if (unit_part(k, g, bi, sp, p, which, pg, kb, ke, split, slot)) w += ke - kb;
       }
       for (int bh = 0; bh < per_bh; ++bh) {
-        const long long t = q.top() + w;
-        q.pop();
-        q.push(t);
-        end = t > end ? t : end;
+        std::pop_heap(heap, heap + n, later);       // earliest-free work group to the back
+        heap[n - 1] += w;
+        end = heap[n - 1] > end ? heap[n - 1] : end;
+        std::push_heap(heap, heap + n, later);
       }
     }
   }

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -161,6 +162,37 @@ char* carve_mlp(const tsp::Shape& s, char* p, MlpWs* w) {
 
 float* partial_or_null(const tsp::Shape& s, char* p) {
   return bytes_partial(s) > 0 ? reinterpret_cast<float*>(p) : nullptr;
+}
+
+// ---- fixed scratch array (tsp_layer_fwd_noalloc) ---------------------------
+// The workspace of the entry point that allocates nothing.  Each GPU the
+// library runs on holds its own copy for the life of the process.  In host
+// code `scratch` is only a stand-in for the symbol: its device address comes
+// from hipGetSymbolAddress, looked up once per device and kept here.
+static __device__ __align__(256) unsigned char scratch[TSP_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "tsp_layer_fwd_noalloc");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TSP_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "tsp_layer_fwd_noalloc: scratch address");
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+      return fail(TSP_ERR_HIP, "tsp_layer_fwd_noalloc: scratch address %p unusable", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSP_OK;
 }
 
 // ---- live per-kernel timing (see tsp_profile_kernel) -----------------------
@@ -406,12 +438,11 @@ int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
   return run_mlp(s, x16, x_dtype == TSP_BF16, residual, w_gate, w_up, w_down, y, w, stream);
 }
 
-int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
-                  const uint16_t* w_o, const uint16_t* w_gate, const uint16_t* w_up,
-                  const uint16_t* w_down, uint16_t* kv_gathered, float* y, void* ws,
-                  size_t ws_bytes, hipStream_t stream) {
-  tsp::Shape s;
-  TSP_TRY(make_shape(dims, &s));
+// Checks of tsp_layer_fwd's arguments other than the workspace.
+int check_layer_args(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                     const uint16_t* w_o, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                     const uint16_t* kv_gathered, const float* y, tsp::Shape* s) {
+  TSP_TRY(make_shape(dims, s));
   TSP_TRY(need_ptr(x_local, "x_local"));
   TSP_TRY(need_ptr(w_qkv, "w_qkv"));
   TSP_TRY(need_ptr(w_o, "w_o"));
@@ -420,10 +451,12 @@ int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_
   TSP_TRY(need_ptr(w_down, "w_down"));
   TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
   TSP_TRY(need_ptr(y, "y"));
-  TSP_TRY(need_ptr(ws, "ws"));
-  if (ws_bytes < ws_layer(s))
-    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_layer(s));
-  TSP_TRY(check_device("tsp_layer_fwd"));
+  return TSP_OK;
+}
+
+int run_layer(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* w_qkv, const uint16_t* w_o,
+              const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, uint16_t* kv_gathered,
+              float* y, void* ws, hipStream_t stream) {
   AttnWs aw;
   MlpWs mw;
   char* p = carve_attn(s, static_cast<char*>(ws), &aw);
@@ -433,6 +466,32 @@ int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_
   aw.partial = mw.partial = partial_or_null(s, p);
   TSP_TRY(run_attention(s, x_local, w_qkv, w_o, kv_gathered, x_local, nullptr, h32, mw.h16, aw, stream));
   return run_mlp(s, mw.h16, false, h32, w_gate, w_up, w_down, y, mw, stream);
+}
+
+int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                  const uint16_t* w_o, const uint16_t* w_gate, const uint16_t* w_up,
+                  const uint16_t* w_down, uint16_t* kv_gathered, float* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(check_layer_args(dims, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, &s));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_layer(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_layer(s));
+  TSP_TRY(check_device("tsp_layer_fwd"));
+  return run_layer(s, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, ws, stream);
+}
+
+int tsp_layer_fwd_noalloc(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                          const uint16_t* w_o, const uint16_t* w_gate, const uint16_t* w_up,
+                          const uint16_t* w_down, uint16_t* kv_gathered, float* y, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(check_layer_args(dims, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, &s));
+  if (ws_layer(s) > (size_t)TSP_SCRATCH_BYTES)
+    return fail(TSP_ERR_SCRATCH, "layer needs %zu bytes of workspace, more than the %zu-byte scratch array",
+                ws_layer(s), (size_t)TSP_SCRATCH_BYTES);
+  void* ws = nullptr;
+  TSP_TRY(scratch_ptr(&ws));
+  return run_layer(s, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, ws, stream);
 }
 
 }  // extern "C"

@@ -218,6 +218,22 @@ int tsp_layer_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_
                   const uint16_t* w_down, uint16_t* kv_gathered, float* y, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 
+/* tsp_layer_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing: its workspace is
+ * a fixed array of TSP_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends.  Layers needing more workspace than that
+ * (tsp_workspace_bytes(dims, TSP_FN_LAYER) > TSP_SCRATCH_BYTES) return
+ * TSP_ERR_SCRATCH before anything is launched.  Nothing in the array has to
+ * start at zero (every piece is written before it is read).  Every call on
+ * one GPU uses the same array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  The first call
+ * on a device looks the array's device address up (no allocation). */
+#define TSP_SCRATCH_BYTES (128u * 1024u * 1024u)
+int tsp_layer_fwd_noalloc(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                          const uint16_t* w_o, const uint16_t* w_gate, const uint16_t* w_up,
+                          const uint16_t* w_down, uint16_t* kv_gathered, float* y, hipStream_t stream);
+
 /* Bytes of workspace (or of a buffer) named by fn for these dims; 0 if the
  * dims are invalid (tsp_last_error says why). */
 size_t tsp_workspace_bytes(const tsp_dims_t* dims, int32_t fn);

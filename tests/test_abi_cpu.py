@@ -298,3 +298,28 @@ def test_binding_sizes_follow_the_header():
     # default kmax of rank 0 = (2D - r) c = 16 * 512; natural K and V, 32 heads
     assert z.kv_natural(0) == 4 * 32 * 8192 * 128
     assert z.kv_natural(100) == 4 * 32 * 128 * 128
+
+
+def test_noalloc_rejects_layers_beyond_the_scratch_array(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define TSP_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m and int(m.group(1)) * 1024 * 1024 == B.TSP_SCRATCH_BYTES
+    big = B.dims_struct(synth.WORKLOADS["llama3_8b_gqa_s16k_d8"].dims)
+    assert lib.tsp_workspace_bytes(ctypes.byref(big), B.TSP_FN_LAYER) > B.TSP_SCRATCH_BYTES
+    rc = lib.tsp_layer_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == B.TSP_ERR_SCRATCH and "scratch array" in lib.tsp_last_error().decode()
+    # the headline layer fits
+    l7 = B.dims_struct(synth.WORKLOADS["llama7b_s8k_d8"].dims)
+    assert lib.tsp_workspace_bytes(ctypes.byref(l7), B.TSP_FN_LAYER) <= B.TSP_SCRATCH_BYTES
+    # argument checks come first
+    rc = lib.tsp_layer_fwd_noalloc(ctypes.byref(l7), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert rc == B.TSP_ERR_NULL_POINTER and "y is NULL" in lib.tsp_last_error().decode()
+
+
+def test_noalloc_without_device_gives_hip_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    d = _dims()
+    rc = lib.tsp_layer_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == B.TSP_ERR_HIP
