@@ -377,3 +377,71 @@ def test_algorithmic_flops_llama7b_8k():
     assert f["attn"] == 4 * 128 * 32 * (8192 * 8193 // 16)
     assert f["mlp"] == 2 * M * 3 * 11008 * h
     assert abs(f["total"] / 1e9 - 483.2) < 0.05
+
+
+# --------------------------------------------------------------------------- #
+# qkv_rows and mlp_block, the per-kernel references of the GPU tests
+# --------------------------------------------------------------------------- #
+def _tiny_gqa_inputs(seed=21, sigma=0.5):
+    # non-square everywhere: Hq != Hkv, dh != h, F != h, B = 2, D = 2
+    d = synth.Dims(2, 8, 2, 0, 8, 4, 2, 4, 12)
+    return d, synth.make_inputs(d, sigma, seed)
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_qkv_rows_matches_bruteforce_every_source_rank(rank):
+    """X W^T of every local row of rank `rank`, as a triple loop over the
+    positions the zigzag rule gives that rank written out by hand (chunks r
+    and 2D-1-r of c = 2 positions: rank 0 holds 0, 1, 6, 7; rank 1 holds 2, 3,
+    4, 5), so a wrong source rank, row order or weight fails."""
+    d, inp = _tiny_gqa_inputs()
+    d = dataclasses.replace(d, rank=rank)
+    positions = {0: [0, 1, 6, 7], 1: [2, 3, 4, 5]}[rank]
+    x = orc.bf16_bits_to_f64(inp["x"])
+    for b in range(d.batch):
+        got = orc.qkv_rows(inp, d, b, np.arange(4))
+        # also through the rank argument while dims says the other rank
+        other = dataclasses.replace(d, rank=1 - rank)
+        got2 = orc.qkv_rows(inp, other, b, np.arange(4), rank=rank)
+        for name in ("q", "k", "v"):
+            w = orc.bf16_bits_to_f64(inp["w_" + name])
+            want = np.zeros((4, w.shape[0]))
+            for t, g in enumerate(positions):
+                for o in range(w.shape[0]):
+                    acc = 0.0
+                    for k in range(d.hidden):
+                        acc += x[b, g, k] * w[o, k]
+                    want[t, o] = acc
+            np.testing.assert_allclose(got[name], want, rtol=1e-13, atol=1e-14)
+            np.testing.assert_array_equal(got2[name], got[name])
+    # the three projections are distinct (a swapped weight would show)
+    assert not np.allclose(got["k"], got["v"])
+
+
+def test_mlp_block_matches_bruteforce_and_torch():
+    """x + (silu(x Wg^T) * (x Wu^T)) Wd^T row by row in plain loops, and
+    through PyTorch's float64 silu and matmul; gate and up swapped, or the
+    residual dropped, fail (checked below)."""
+    d, inp = _tiny_gqa_inputs(seed=22)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, d.hidden))
+    wg, wu, wd = (orc.bf16_bits_to_f64(inp[n]) for n in ("w_g", "w_u", "w_d"))
+    got = orc.mlp_block(inp, x)
+    want = np.zeros_like(x)
+    for i in range(x.shape[0]):
+        a = []
+        for f in range(d.ffn):
+            g = sum(x[i, k] * wg[f, k] for k in range(d.hidden))
+            u = sum(x[i, k] * wu[f, k] for k in range(d.hidden))
+            a.append(g / (1.0 + math.exp(-g)) * u)
+        for o in range(d.hidden):
+            want[i, o] = x[i, o] + sum(a[f] * wd[o, f] for f in range(d.ffn))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    xt = torch.from_numpy(x)
+    ref = xt + (torch.nn.functional.silu(xt @ torch.from_numpy(wg).T) * (xt @ torch.from_numpy(wu).T)) \
+        @ torch.from_numpy(wd).T
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+    # the pins are sharp enough to see the plausible slips
+    swapped = x + (orc.silu(x @ wu.T) * (x @ wg.T)) @ wd.T
+    assert np.abs(swapped - want).max() > 1e-3
+    assert np.abs((got - x) - want).max() > 1e-1
