@@ -19,7 +19,8 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Dims", "Workload", "WORKLOADS", "workload", "f32_to_bf16_bits", "make_inputs", "make_custom"]
+__all__ = ["Dims", "Workload", "WORKLOADS", "workload", "f32_to_bf16_bits", "make_inputs", "make_custom",
+           "make_grad"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -127,3 +128,13 @@ def make_custom(batch, seq, degree, rank, hidden, n_q_heads, n_kv_heads, head_di
     dims = Dims(batch, seq, degree, rank, hidden, n_q_heads, n_kv_heads, head_dim, ffn)
     return dims, make_inputs(dims, sigma, seed)
 
+
+
+def make_grad(dims: Dims, seed: int, scale: float = 1.0) -> np.ndarray:
+    """Upstream gradient dY of the layer output, float32 [B][S][h] ~ N(0, scale^2),
+    from its own generator (seed + 7919, so it never repeats the input draw)."""
+    rng = np.random.default_rng(seed + 7919)
+    g = rng.standard_normal(size=(dims.batch, dims.seq, dims.hidden), dtype=np.float32)
+    if scale != 1.0:
+        g *= np.float32(scale)
+    return g
