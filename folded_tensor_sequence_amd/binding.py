@@ -48,6 +48,7 @@ TSP_FN_MLP = 2
 TSP_FN_LAYER = 3
 TSP_FN_KV_NATURAL = 4
 TSP_FN_KV_GATHERED = 5
+TSP_FN_MLP_BWD = 6
 
 KERNELS = {"qkv": 1, "reorder": 2, "attn": 3, "oproj": 4, "gateup": 5, "down": 6}
 
@@ -56,7 +57,8 @@ TUNE = {"gemm_qkv": 0, "gemm_oproj": 1, "gemm_gateup": 2, "gemm_down": 3, "split
 
 EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd",
             "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",
-            "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning", "tsp_layer_fwd_noalloc")
+            "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning", "tsp_layer_fwd_noalloc",
+            "tsp_mlp_ring_bwd")
 
 # Size of the library's fixed scratch array (TSP_SCRATCH_BYTES in include/tsp.h).
 TSP_SCRATCH_BYTES = 128 * 1024 * 1024
@@ -96,6 +98,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tsp_mlp_ring_fwd": [dp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_layer_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_layer_fwd_noalloc": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "tsp_mlp_ring_bwd": [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -277,6 +280,30 @@ def tsp_mlp_ring_fwd(dims, x, w_gate, w_up, w_down, y, ws, residual=None, x_dtyp
                                    _tensor(w_up, "w_up", "bf16", z.w_ffn), _tensor(w_down, "w_down", "bf16", z.w_ffn),
                                    _tensor(residual, "residual", "f32", z.f32, optional=True),
                                    _tensor(y, "y", "f32", z.f32), wsp, wsn, _s(stream)))
+
+
+def tsp_mlp_ring_bwd(dims, x, dy, w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down, ws, dx_residual=None,
+                     x_dtype=None, stream=None):
+    """Backward of the MLP ring: dx = dx_residual + dMLP/dx^T dy and this rank's
+    contributions to dW_gate, dW_up ([F][h]) and dW_down ([D][h][F/D])."""
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    if x_dtype is None:
+        if not isinstance(x, torch.Tensor) or x.dtype not in _XDTYPE:
+            raise ValueError("x_dtype is required unless x is bfloat16, float16 or float32")
+        x_dtype = _XDTYPE[x.dtype]
+    kind = {TSP_BF16: "bf16", TSP_F16: "f16", TSP_F32: "f32"}.get(int(x_dtype))
+    if kind is None:
+        raise ValueError(f"x_dtype {x_dtype} unknown")
+    wsp, wsn = _ws(dims, ws, TSP_FN_MLP_BWD)
+    fw = 2 * z.w_ffn      # float32 gradient of a [F][h] weight
+    _check(load().tsp_mlp_ring_bwd(
+        ctypes.byref(d), _tensor(x, "x", kind, z.f32 if kind == "f32" else z.x16), int(x_dtype),
+        _tensor(dy, "dy", "f32", z.f32), _tensor(w_gate, "w_gate", "bf16", z.w_ffn),
+        _tensor(w_up, "w_up", "bf16", z.w_ffn), _tensor(w_down, "w_down", "bf16", z.w_ffn),
+        _tensor(dx_residual, "dx_residual", "f32", z.f32, optional=True), _tensor(dx, "dx", "f32", z.f32),
+        _tensor(dw_gate, "dw_gate", "f32", fw), _tensor(dw_up, "dw_up", "f32", fw),
+        _tensor(dw_down, "dw_down", "f32", fw), wsp, wsn, _s(stream)))
 
 
 def tsp_layer_fwd(dims, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, ws, stream=None):

@@ -24,7 +24,9 @@
 
 namespace tsp {
 
-enum { EPI_QKV = 0, EPI_RESID_BF16X = 1, EPI_RESID_F32 = 2, EPI_SWIGLU = 3, EPI_PARTIAL = 4 };
+enum { EPI_QKV = 0, EPI_RESID_BF16X = 1, EPI_RESID_F32 = 2, EPI_SWIGLU = 3, EPI_PARTIAL = 4,
+       // backward of the gated MLP (see the launchers at the end)
+       EPI_SWIGLU_BWD = 5, EPI_DWD = 6, EPI_DWGU = 7 };
 
 struct GemmArgs {
   const uint16_t* A;
@@ -44,10 +46,22 @@ struct GemmArgs {
   // split-K: nsplit > 1 writes float32 partial sums to partial[split][M][N]
   int32_t nsplit;
   float* partial;
+  // backward epilogues: a second float32 output and a second bf16 output
+  float* out2;
+  uint16_t* aux16;
 };
 
 __device__ __forceinline__ float silu_f32(float z) {
   return z / (1.0f + __expf(-z));
+}
+
+// Two floats -> two packed bfloat16, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <int EPI>
@@ -106,6 +120,49 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
   } else if constexpr (EPI == EPI_PARTIAL) {
     // v2 carries the split index in its first element's bits (see caller)
     (void)v2;
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    // v = g = x Wg^T, v2 = u = x Wu^T for columns n..n+3 (F axis); resid =
+    // dA = dy Wd (float32 [M][F]).  With s = sigmoid(g): a = g s u,
+    // dU = dA g s, dG = dA u s (1 + g (1 - s)).  a goes to out16 (bf16
+    // [M][F]); dG and dU to aux16 (bf16 [M][D][2][F/D]: shard j's dG block,
+    // then its dU block, per row).  The four columns lie in one shard.
+    const Shape& s = a.s;
+    const int64_t off = (int64_t)m * a.N + n;
+    const f32x4 da = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
+    float av[4], dg[4], du[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float g = v[e], u = v2[e];
+      const float sg = 1.0f / (1.0f + __expf(-g));
+      const float gs = g * sg;
+      av[e] = gs * u;
+      du[e] = da[e] * gs;
+      dg[e] = da[e] * u * (sg + gs * (1.0f - sg));
+    }
+    u32x2 pa{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+    *reinterpret_cast<u32x2*>(a.out16 + off) = pa;
+    const int j = n / s.F_s, f = n - j * s.F_s;
+    uint16_t* gu = a.aux16 + (int64_t)m * 2 * s.F + (int64_t)j * 2 * s.F_s + f;
+    u32x2 pg{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+    u32x2 pu{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+    *reinterpret_cast<u32x2*>(gu) = pg;
+    *reinterpret_cast<u32x2*>(gu + s.F_s) = pu;
+  } else if constexpr (EPI == EPI_DWD) {
+    // C [h][F] (row = hidden index, column = F index) -> dW_down [D][h][F/D]
+    const Shape& s = a.s;
+    const int j = n / s.F_s, f = n - j * s.F_s;
+    f32x4 o{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(a.out + ((int64_t)j * s.h + m) * s.F_s + f) = o;
+  } else if constexpr (EPI == EPI_DWGU) {
+    // C [2F][h], rows in the [D][2][F/D] order of the dG|dU buffer ->
+    // dW_gate (out) or dW_up (out2), both [F][h]
+    const Shape& s = a.s;
+    const int j = m / (2 * s.F_s);
+    const int w = m - j * 2 * s.F_s;
+    const bool up = w >= s.F_s;
+    const int f = j * s.F_s + (up ? w - s.F_s : w);
+    f32x4 o{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>((up ? a.out2 : a.out) + (int64_t)f * a.N + n) = o;
   } else {  // EPI_SWIGLU: v = gate, v2 = up
     const int64_t off = (int64_t)m * a.N + n;
     u32x2 pk{pack_f16x2(silu_f32(v[0]) * v2[0], silu_f32(v[1]) * v2[1]),
@@ -1085,6 +1142,111 @@ hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t*
   a.resid = resid;
   a.partial = partial;
   return launch_single<true, true, EPI_RESID_F32>(a, KNOB_GEMM_DOWN, KNOB_SPLIT_DOWN, gemm_split_plan(s), st);
+}
+
+// --------------------------------------------------------------------------
+// Backward of the gated MLP (bf16 matrix cores on bf16 operands; gradients
+// keep bf16's float32 range).  Operand layouts (NT form, K-contiguous):
+//   dA   = dy16 [M][h] x WdT [F][h]                  -> float32 dA [M][F]
+//   g, u = x [M][h] x (Wg, Wu) [F][h], epilogue       -> a [M][F], dG|dU
+//   dx   = dGU [M][D][2][F/D] x WguT [h][D][2][F/D]   (K segments per shard,
+//          in ring order (r - s) mod D)  + dx_resid  -> float32 dx [M][h]
+//   dWd  = dyT [h][Mp] x aT [F][Mp]                   -> dW_down [D][h][F/D]
+//   dWgu = dGUT [2F][Mp] x xT [h][Mp]                 -> dW_gate, dW_up [F][h]
+// Mp = M rounded up to 64 (the transposed copies are zero beyond M).
+// --------------------------------------------------------------------------
+hipError_t launch_bwd_da(const Shape& s, const uint16_t* dy16, const uint16_t* wdT, float* da, hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = dy16;
+  a.lda = s.h;
+  a.B0 = a.B1 = wdT;
+  a.ldb = s.h;
+  a.M = s.M;
+  a.N = s.F;
+  a.K = s.h;
+  a.seg_len = s.h;
+  a.out = da;
+  a.resid = nullptr;
+  return launch_cfg<false, false, EPI_RESID_F32>(a, 0, 1, st);
+}
+
+hipError_t launch_bwd_gu(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g, const uint16_t* w_u,
+                         const float* da, uint16_t* act16, uint16_t* dgu, hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = x;
+  a.lda = s.h;
+  a.B0 = w_g;
+  a.B1 = w_u;
+  a.ldb = s.h;
+  a.M = s.M;
+  a.N = s.F;
+  a.K = s.h;
+  a.seg_len = s.h;
+  a.resid = da;
+  a.out16 = act16;
+  a.aux16 = dgu;
+  hipError_t e;
+  if (x_bf16) {
+    e = launch_staged<256, 96, 2, 4, 8, false, false, EPI_SWIGLU_BWD, 1, true>(a, 1, st);
+    if (e != hipErrorNotSupported) return e;
+    return launch_tile<128, 128, 2, 2, 4, 64, 3, false, false, EPI_SWIGLU_BWD, 1>(a, 1, st);
+  }
+  e = launch_staged<256, 96, 2, 4, 8, true, true, EPI_SWIGLU_BWD, 1, true>(a, 1, st);
+  if (e != hipErrorNotSupported) return e;
+  return launch_tile<128, 128, 2, 2, 4, 64, 3, true, true, EPI_SWIGLU_BWD, 1>(a, 1, st);
+}
+
+hipError_t launch_bwd_dx(const Shape& s, const uint16_t* dgu, const uint16_t* wguT, const float* dx_resid, float* dx,
+                         float* partial, hipStream_t st) {
+  GemmArgs a = base_args(s);
+  const int seg = 2 * s.F_s;
+  a.A = dgu;
+  a.lda = 2 * (int64_t)s.F;
+  a.a_seg_step = seg;
+  a.B0 = a.B1 = wguT;
+  a.ldb = 2 * (int64_t)s.F;
+  a.b_seg_step = seg;
+  a.M = s.M;
+  a.N = s.h;
+  a.K = 2 * s.F;
+  a.seg_len = seg;
+  a.nseg = s.D;
+  a.ring_rank = s.r;
+  a.out = dx;
+  a.resid = dx_resid;
+  a.partial = partial;
+  return launch_single<false, false, EPI_RESID_F32>(a, -1, -1, gemm_split_plan(s), st);
+}
+
+hipError_t launch_bwd_dwd(const Shape& s, int m_pad, const uint16_t* dyT, const uint16_t* aT, float* dw_down,
+                          hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = dyT;
+  a.lda = m_pad;
+  a.B0 = a.B1 = aT;
+  a.ldb = m_pad;
+  a.M = s.h;
+  a.N = s.F;
+  a.K = m_pad;
+  a.seg_len = m_pad;
+  a.out = dw_down;
+  return launch_cfg<false, false, EPI_DWD>(a, 0, 1, st);
+}
+
+hipError_t launch_bwd_dwgu(const Shape& s, int m_pad, const uint16_t* dguT, const uint16_t* xT, float* dw_gate,
+                           float* dw_up, hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = dguT;
+  a.lda = m_pad;
+  a.B0 = a.B1 = xT;
+  a.ldb = m_pad;
+  a.M = 2 * s.F;
+  a.N = s.h;
+  a.K = m_pad;
+  a.seg_len = m_pad;
+  a.out = dw_gate;
+  a.out2 = dw_up;
+  return launch_cfg<false, false, EPI_DWGU>(a, 0, 1, st);
 }
 
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n4) {

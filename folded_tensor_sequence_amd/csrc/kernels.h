@@ -55,6 +55,32 @@ hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t*
 // f32 -> f16 rounding copy (MLP input when it arrives as float32).
 hipError_t launch_f32_to_f16(const float* x, uint16_t* y, int64_t n, hipStream_t st);
 
+// ---- backward of the gated MLP ---------------------------------------------
+// Input element types of launch_transpose_bf16.
+enum { TR_BF16 = 0, TR_F16 = 1, TR_F32 = 2 };
+
+// out[b][c][r] = bf16(in[b][r][c]) for r < R, c < C, zero for R <= r < Rp
+// (Rp and C multiples of 8; rows 16-byte aligned; nothing past Rp written).
+hipError_t launch_transpose_bf16(int tin, const void* in, int64_t ld_in, int64_t in_bstride, uint16_t* out,
+                                 int64_t ld_out, int64_t out_bstride, int R, int C, int Rp, int batches,
+                                 hipStream_t st);
+hipError_t launch_f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t st);
+
+// dA = dy16 WdT^T (float32 [M][F]); WdT [F][h] bf16.
+hipError_t launch_bwd_da(const Shape& s, const uint16_t* dy16, const uint16_t* wdT, float* da, hipStream_t st);
+// g, u recomputed from x (f16, or bf16 when x_bf16); epilogue: act16 = a
+// (bf16 [M][F]), dgu = dG | dU per shard (bf16 [M][D][2][F/D]).
+hipError_t launch_bwd_gu(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g, const uint16_t* w_u,
+                         const float* da, uint16_t* act16, uint16_t* dgu, hipStream_t st);
+// dx = dx_resid + sum over ring steps of dGU_j WguT_j^T (dx_resid may be nullptr).
+hipError_t launch_bwd_dx(const Shape& s, const uint16_t* dgu, const uint16_t* wguT, const float* dx_resid, float* dx,
+                         float* partial, hipStream_t st);
+// dW_down [D][h][F/D] = dyT aT^T; dW_gate, dW_up [F][h] = dguT xT^T.
+hipError_t launch_bwd_dwd(const Shape& s, int m_pad, const uint16_t* dyT, const uint16_t* aT, float* dw_down,
+                          hipStream_t st);
+hipError_t launch_bwd_dwgu(const Shape& s, int m_pad, const uint16_t* dguT, const uint16_t* xT, float* dw_gate,
+                           float* dw_up, hipStream_t st);
+
 // Causal flash attention of the rank's queries over the all-gathered K/V
 // (read in zigzag order through the position -> slot map, no reordered copy).
 // Row blocks whose key range is long are cut into pieces along the keys

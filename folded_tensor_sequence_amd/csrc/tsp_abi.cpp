@@ -123,6 +123,37 @@ size_t bytes_partial(const tsp::Shape& s) {
   return gemm > attn ? gemm : attn;
 }
 
+// Backward of the MLP ring: M rows padded to 64 on the transposed copies.
+int mpad(const tsp::Shape& s) { return (s.M + 63) / 64 * 64; }
+
+struct MlpBwdWs {
+  uint16_t *x16, *xT, *dy16, *dyT, *wdT, *wguT, *act, *dgu, *actT, *dguT;
+  float *da, *partial;
+};
+
+// [x16 | xT | dy16 | dyT | wdT | wguT | da | act | dgu | actT | dguT | split-K partials]
+size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullptr) {
+  const size_t M = s.M, h = s.h, F = s.F, Mp = mpad(s);
+  const size_t sizes[] = {M * h * 2, h * Mp * 2, M * h * 2, h * Mp * 2, F * h * 2, h * 2 * F * 2,
+                          M * F * 4, M * F * 2, M * 2 * F * 2, F * Mp * 2, 2 * F * Mp * 2};
+  void** slots[] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (w != nullptr) {
+    void** ptrs[] = {(void**)&w->x16, (void**)&w->xT, (void**)&w->dy16, (void**)&w->dyT, (void**)&w->wdT,
+                     (void**)&w->wguT, (void**)&w->da, (void**)&w->act, (void**)&w->dgu, (void**)&w->actT,
+                     (void**)&w->dguT};
+    for (int i = 0; i < 11; ++i) slots[i] = ptrs[i];
+  }
+  size_t off = 0;
+  for (int i = 0; i < 11; ++i) {
+    if (slots[i] != nullptr) *slots[i] = base + off;
+    off += (sizes[i] + 255) / 256 * 256;
+  }
+  const int p = tsp::gemm_split_plan(s);
+  const size_t part = p > 1 ? (size_t)p * M * h * 4 : 0;
+  if (w != nullptr) w->partial = part > 0 ? reinterpret_cast<float*>(base + off) : nullptr;
+  return off + (part + 255) / 256 * 256;
+}
+
 struct AttnWs {
   uint16_t *q, *o;
   float* partial;
@@ -341,6 +372,7 @@ size_t tsp_workspace_bytes(const tsp_dims_t* dims, int32_t fn) {
     case TSP_FN_LAYER: return ws_layer(s);
     case TSP_FN_KV_NATURAL: return bytes_kvnat(s);
     case TSP_FN_KV_GATHERED: return bytes_gathered(s);
+    case TSP_FN_MLP_BWD: return ws_mlp_bwd(s);
     default: fail(TSP_ERR_INVALID_ARG, "unknown workspace selector %d", fn); return 0;
   }
 }
@@ -436,6 +468,69 @@ int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
     x16 = w.h16;
   }
   return run_mlp(s, x16, x_dtype == TSP_BF16, residual, w_gate, w_up, w_down, y, w, stream);
+}
+
+int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const float* dy,
+                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                     const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  if (x_dtype != TSP_BF16 && x_dtype != TSP_F16 && x_dtype != TSP_F32)
+    return fail(TSP_ERR_DTYPE, "x_dtype %d unknown (0 bf16, 1 f16, 2 f32)", x_dtype);
+  TSP_TRY(need_ptr(x, "x"));
+  TSP_TRY(need_ptr(dy, "dy"));
+  TSP_TRY(need_ptr(w_gate, "w_gate"));
+  TSP_TRY(need_ptr(w_up, "w_up"));
+  TSP_TRY(need_ptr(w_down, "w_down"));
+  TSP_TRY(opt_ptr(dx_residual, "dx_residual"));
+  TSP_TRY(need_ptr(dx, "dx"));
+  TSP_TRY(need_ptr(dw_gate, "dw_gate"));
+  TSP_TRY(need_ptr(dw_up, "dw_up"));
+  TSP_TRY(need_ptr(dw_down, "dw_down"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_mlp_bwd(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_mlp_bwd(s));
+  TSP_TRY(check_device("tsp_mlp_ring_bwd"));
+  MlpBwdWs w;
+  ws_mlp_bwd(s, &w, static_cast<char*>(ws));
+  const int Mp = mpad(s), h = s.h, F = s.F, Fs = s.F_s;
+  const int tin = x_dtype == TSP_BF16 ? tsp::TR_BF16 : x_dtype == TSP_F16 ? tsp::TR_F16 : tsp::TR_F32;
+  // recomputation input: x itself (bf16 or f16), or x rounded to f16
+  const uint16_t* xg = static_cast<const uint16_t*>(x);
+  if (x_dtype == TSP_F32) {
+    TSP_LAUNCH(tsp::launch_f32_to_f16(static_cast<const float*>(x), w.x16, (int64_t)s.M * h, stream),
+               "mlp bwd: x to f16");
+    xg = w.x16;
+  }
+  // transposed / converted operands
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tin, x, h, 0, w.xT, Mp, 0, s.M, h, Mp, 1, stream), "mlp bwd: x^T");
+  TSP_LAUNCH(tsp::launch_f32_to_bf16(dy, w.dy16, (int64_t)s.M * h, stream), "mlp bwd: dy to bf16");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_F32, dy, h, 0, w.dyT, Mp, 0, s.M, h, Mp, 1, stream),
+             "mlp bwd: dy^T");
+  // Wd_j [h][Fs] -> WdT rows j Fs .. : [Fs][h]
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_down, Fs, (int64_t)h * Fs, w.wdT, h, (int64_t)Fs * h, h, Fs,
+                                        h, s.D, stream),
+             "mlp bwd: Wd^T");
+  // Wg_j, Wu_j [Fs][h] -> WguT [h][D][2][Fs]
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_gate, h, (int64_t)Fs * h, w.wguT, 2 * (int64_t)F,
+                                        2 * (int64_t)Fs, Fs, h, Fs, s.D, stream),
+             "mlp bwd: Wg^T");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_up, h, (int64_t)Fs * h, w.wguT + Fs, 2 * (int64_t)F,
+                                        2 * (int64_t)Fs, Fs, h, Fs, s.D, stream),
+             "mlp bwd: Wu^T");
+  TSP_LAUNCH(tsp::launch_bwd_da(s, w.dy16, w.wdT, w.da, stream), "mlp bwd: dA");
+  TSP_LAUNCH(tsp::launch_bwd_gu(s, xg, x_dtype == TSP_BF16, w_gate, w_up, w.da, w.act, w.dgu, stream),
+             "mlp bwd: gate/up recompute");
+  TSP_LAUNCH(tsp::launch_bwd_dx(s, w.dgu, w.wguT, dx_residual, dx, w.partial, stream), "mlp bwd: dx");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w.act, F, 0, w.actT, Mp, 0, s.M, F, Mp, 1, stream),
+             "mlp bwd: a^T");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w.dgu, 2 * (int64_t)F, 0, w.dguT, Mp, 0, s.M, 2 * F, Mp, 1,
+                                        stream),
+             "mlp bwd: dGU^T");
+  TSP_LAUNCH(tsp::launch_bwd_dwd(s, Mp, w.dyT, w.actT, dw_down, stream), "mlp bwd: dW_down");
+  TSP_LAUNCH(tsp::launch_bwd_dwgu(s, Mp, w.dguT, w.xT, dw_gate, dw_up, stream), "mlp bwd: dW_gate, dW_up");
+  return TSP_OK;
 }
 
 // Checks of tsp_layer_fwd's arguments other than the workspace.

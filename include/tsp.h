@@ -113,7 +113,8 @@ typedef enum {
   TSP_FN_MLP = 2,        /* tsp_mlp_ring_fwd workspace */
   TSP_FN_LAYER = 3,      /* tsp_layer_fwd workspace */
   TSP_FN_KV_NATURAL = 4, /* size of the kv_natural output of tsp_kv_reorder */
-  TSP_FN_KV_GATHERED = 5 /* size of the kv_gathered buffer */
+  TSP_FN_KV_GATHERED = 5, /* size of the kv_gathered buffer */
+  TSP_FN_MLP_BWD = 6     /* tsp_mlp_ring_bwd workspace */
 } tsp_fn;
 
 /* Maps of the partition dims->partition selects, as described above (TSP
@@ -207,6 +208,42 @@ int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype,
                      const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                      const float* residual, float* y, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* Backward of the gated-MLP weight ring on rank dims->rank: the gradients of
+ *     m = sum_{s=0}^{D-1} (silu(x Wg_j^T) * (x Wu_j^T)) Wd_j^T,  j = (r - s) mod D
+ * for the upstream gradient dy = dL/dm of the rank's own tokens.  The TSP
+ * article presents TSP for training ("Zyphra Introduces Tensor and Sequence
+ * Parallelism (TSP)...", opening paragraph and "What you need to know") but
+ * describes only the forward schedule; this is its transpose.  The shards go
+ * round the ring again, each carrying an accumulator of its weight
+ * gradients: a rank adds its own tokens' contribution to the shard it holds,
+ * so every accumulator reaches its owner with the sum over all ranks; the
+ * input gradient stays local and sums over the shards (the transpose of the
+ * column/row split: bowenzhou.top "张量并行", section "机制：行切与列切").
+ * With all D shards resident, this call computes the rank's input gradient
+ * and its contribution to every shard's weight gradients:
+ *     dA_j = dy Wd_j,  dU_j = dA_j * silu(g_j),  dG_j = dA_j * u_j * silu'(g_j),
+ *     dx   = dx_residual + sum_s (dG_j Wg_j + dU_j Wu_j)   (ring order),
+ *     dWg_j = dG_j^T x,  dWu_j = dU_j^T x,  dWd_j = dy^T (silu(g_j) * u_j),
+ * with g_j = x Wg_j^T, u_j = x Wu_j^T recomputed, silu'(z) = s (1 + z (1 - s)),
+ * s = 1 / (1 + e^-z).
+ *   x            [B][T][h] MLP input of type x_dtype (as in tsp_mlp_ring_fwd)
+ *   dy           float32 [B][T][h]
+ *   w_gate, w_up, w_down   bf16, layouts of tsp_mlp_ring_fwd
+ *   dx_residual  float32 [B][T][h] or NULL, added to dx (pass dy for the
+ *                residual branch of y = x + MLP(x))
+ *   dx           float32 [B][T][h]; may alias dy or dx_residual
+ *   dw_gate, dw_up  float32 [D][F/D][h] (= [F][h]): this rank's contribution
+ *   dw_down      float32 [D][h][F/D]: this rank's contribution
+ *   ws           >= tsp_workspace_bytes(dims, TSP_FN_MLP_BWD) bytes
+ * Precision: dy and the gradients dA, dG, dU, the activation a and x enter
+ * the matrix cores as bf16 (bfloat16 keeps float32's range, which gradients
+ * need); the recomputation of g and u runs as in the forward; float32
+ * accumulation and float32 outputs. */
+int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const float* dy,
+                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                     const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Whole layer on rank dims->rank: h = x + Attn(x), y = h + MLP(h), with the
  * argument layouts of tsp_attn_fwd and tsp_mlp_ring_fwd.  h stays float32;

@@ -72,3 +72,48 @@ def rank_rows_rounded(inputs: dict, dims, b: int, rows, points=POINTS, kv=None, 
     hm = R("h16", hres)
     act = R("act", orc.silu(hm @ weights["w_g"].T) * (hm @ weights["w_u"].T))
     return hres + act @ weights["w_d"].T
+
+
+# --------------------------------------------------------------------------- #
+# Backward of the gated MLP: bfloat16 storage points
+# --------------------------------------------------------------------------- #
+BWD_POINTS = ("dy", "act", "dgu", "xw")
+
+
+def bf16(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (round to nearest even) and back, via
+    float32 (exact for every bfloat16 value; float64 -> float32 rounding
+    first is a double rounding only for values within 2^-29 relative of a
+    bfloat16 tie, which random data does not hit)."""
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def mlp_backward_rounded(x: np.ndarray, w_g: np.ndarray, w_u: np.ndarray, w_d: np.ndarray, dy: np.ndarray,
+                         points=BWD_POINTS, x_f16: bool = False) -> dict:
+    """The gated MLP's backward (``tsp_backward.mlp_backward``) in float64 with
+    the storage points in ``points`` rounded to bfloat16 where a matrix-core
+    implementation with 16-bit operands keeps them:
+
+        "dy"   the upstream gradient fed to dA = dy Wd and dWd = dy^T a;
+        "act"  the activation a = silu(g) u fed to dWd;
+        "dgu"  dG and dU fed to dx and to dWg, dWu;
+        "xw"   the MLP input fed to dWg, dWu.
+
+    ``x_f16``: the recomputation of g and u sees x rounded to binary16 (an
+    input handed over as float32)."""
+    unknown = set(points) - set(BWD_POINTS)
+    if unknown:
+        raise ValueError(f"unknown rounding points {sorted(unknown)}")
+    R = (lambda name, a: bf16(a) if name in points else a)
+    xg = f16(x) if x_f16 else x
+    g, u = xg @ w_g.T, xg @ w_u.T
+    s = 1.0 / (1.0 + np.exp(-g))
+    a = g * s * u
+    dyr = R("dy", dy)
+    da = dyr @ w_d
+    du, dg = R("dgu", da * g * s), R("dgu", da * u * (s + g * s * (1.0 - s)))
+    xw = R("xw", x)
+    return {"dx": dg @ w_g + du @ w_u, "dw_g": dg.T @ xw, "dw_u": du.T @ xw, "dw_d": dyr.T @ R("act", a)}

@@ -323,3 +323,22 @@ def test_noalloc_without_device_gives_hip_error(lib):
     d = _dims()
     rc = lib.tsp_layer_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert rc == B.TSP_ERR_HIP
+
+
+def test_mlp_bwd_argument_checks(lib):
+    d = _dims()
+    big = 1 << 40
+    f = lib.tsp_mlp_ring_bwd
+    args = lambda **kw: [kw.get(n, FAKE) for n in ("x",)] + [kw.get("xdt", B.TSP_BF16)] + \
+        [kw.get(n, FAKE) for n in ("dy", "wg", "wu", "wd")] + [kw.get("res", None)] + \
+        [kw.get(n, FAKE) for n in ("dx", "dwg", "dwu", "dwd", "ws")]
+    assert f(ctypes.byref(d), *args(xdt=7), big, None) == B.TSP_ERR_DTYPE
+    assert f(ctypes.byref(d), *args(dy=None), big, None) == B.TSP_ERR_NULL_POINTER
+    assert "dy is NULL" in lib.tsp_last_error().decode()
+    assert f(ctypes.byref(d), *args(dwd=None), big, None) == B.TSP_ERR_NULL_POINTER
+    assert f(ctypes.byref(d), *args(res=MISALIGNED), big, None) == B.TSP_ERR_MISALIGNED
+    need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_MLP_BWD)
+    assert need > 0 and need % 256 == 0
+    assert f(ctypes.byref(d), *args(), need - 1, None) == B.TSP_ERR_WORKSPACE
+    bad = _dims(batch=0)
+    assert f(ctypes.byref(bad), *args(), big, None) == B.TSP_ERR_BATCH

@@ -89,3 +89,51 @@ def test_wide70b_cheap_widening_does_not_reach_the_bar():
     assert max_abs > 2e-2
     max_abs, _ = _floor("wide70b_s32k_d8", points=("qkv", "p", "o"))   # h16 and act wide
     assert max_abs < 2e-2
+
+
+# --------------------------------------------------------------------------- #
+# Backward of the gated MLP: bfloat16 storage points
+# --------------------------------------------------------------------------- #
+def test_bf16_rounding_known_values():
+    # bfloat16 keeps 7 fraction bits: spacing 2^-7 in [1, 2), ties to even;
+    # float32's range (no overflow at 1e38, normals down to 2^-126)
+    ulp = 2.0 ** -7
+    vals = np.array([1 + ulp / 2, 1 + 3 * ulp / 2, 1 + ulp / 2 + 2 ** -20, 3e38, 2.0 ** -126, -1.0])
+    # 3e38 = 1.7632 x 2^127: the nearest 7-bit fraction is 98/128
+    want = np.array([1.0, 1 + 2 * ulp, 1 + ulp, (1 + 98 / 128) * 2.0 ** 127, 2.0 ** -126, -1.0])
+    assert np.array_equal(rm.bf16(vals), want)
+
+
+def _mlp_case(seed=41, n=24, h=32, F=48):
+    rng = np.random.default_rng(seed)
+    x = rm.bf16(rng.standard_normal((n, h)))
+    dy = rng.standard_normal((n, h))
+    wg, wu = rm.bf16(0.1 * rng.standard_normal((F, h))), rm.bf16(0.1 * rng.standard_normal((F, h)))
+    wd = rm.bf16(0.1 * rng.standard_normal((h, F)))
+    return x, wg, wu, wd, dy
+
+
+def test_backward_model_without_rounding_is_the_oracle():
+    from oracle import tsp_backward as bwd
+    x, wg, wu, wd, dy = _mlp_case()
+    ref = bwd.mlp_backward(x, wg, wu, wd, dy)
+    got = rm.mlp_backward_rounded(x, wg, wu, wd, dy, points=())
+    for k in ("dx", "dw_g", "dw_u", "dw_d"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-13, err_msg=k)
+    with pytest.raises(ValueError):
+        rm.mlp_backward_rounded(x, wg, wu, wd, dy, points=("o",))
+
+
+def test_backward_bf16_floor_sits_inside_the_relative_bars():
+    # every storage point rounded to bf16 leaves each gradient about 2.4e-3
+    # (relative Frobenius) and 3e-3 (max-abs over the largest element) from
+    # the float64 result: the GPU tests hold the backward to 5e-3 and 2e-2
+    from oracle import tsp_backward as bwd
+    x, wg, wu, wd, dy = _mlp_case(n=256, h=128, F=384)
+    ref = bwd.mlp_backward(x, wg, wu, wd, dy)
+    got = rm.mlp_backward_rounded(x, wg, wu, wd, dy)
+    for k in ("dx", "dw_g", "dw_u", "dw_d"):
+        diff = got[k] - ref[k]
+        rel = np.linalg.norm(diff) / np.linalg.norm(ref[k])
+        ma = np.abs(diff).max() / np.abs(ref[k]).max()
+        assert 1e-3 < rel < 3.5e-3 and ma < 1e-2, (k, rel, ma)
