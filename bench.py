@@ -240,6 +240,50 @@ def cpu_baseline(d, inp, target_s: float, max_rows: int):
                       f"{kmax} keys precomputed before timing"}
 
 
+def mlp_backward_measure(d, wl, prob, steps: int):
+    """Times tsp_mlp_ring_bwd (the MLP ring's backward on the rank's rows) on
+    the same weights: dy ~ N(0, 1) from the seeded generator, x = the rank's
+    bf16 input rows.  Algorithmic work: twice the forward MLP's, 12 M F h
+    (dA 2, dx 4, dW_down 2, dW_gate + dW_up 4); the recomputation of g and u
+    (4 M F h more) is executed but not counted."""
+    import numpy as np
+    import torch
+
+    import synth
+    from folded_tensor_sequence_amd import binding as B
+
+    T = d.seq // d.degree
+    M = d.batch * T
+    l2g = prob.l2g[d.rank].cpu().numpy()
+    dy = torch.from_numpy(np.ascontiguousarray(synth.make_grad(d, wl.seed)[:, l2g])).cuda()
+    w = prob.w
+    dx = torch.empty_like(dy)
+    dwg = torch.empty((d.ffn, d.hidden), dtype=torch.float32, device="cuda")
+    dwu = torch.empty_like(dwg)
+    dwd = torch.empty((d.degree, d.hidden, d.ffn // d.degree), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP_BWD), dtype=torch.uint8, device="cuda")
+    call = lambda: B.tsp_mlp_ring_bwd(d, prob.x_local, dy, w["w_gate"], w["w_up"], w["w_down"], dx, dwg, dwu, dwd,
+                                      ws, dx_residual=dy, x_dtype=B.TSP_BF16)
+    for _ in range(3):
+        call()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = 12.0 * M * d.ffn * d.hidden
+    executed = alg + 4.0 * M * d.ffn * d.hidden
+    del ws, dwg, dwu, dwd, dx, dy
+    return {"ms_per_call": round(ms, 5), "calls": steps, "gflop_algorithmic": round(alg / 1e9, 2),
+            "gflop_executed": round(executed / 1e9, 2), "tflops": round(alg / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(alg / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "input": "bf16 rank rows of x; dy float32 ~ N(0, 1); dx_residual = dy"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +420,7 @@ def main():
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(re_bytes / re_s / 1e9 / PEAK_HBM_GBS, 4)}
     del nat
+    out["mlp_ring_bwd"] = mlp_backward_measure(d, wl, prob, max(3, args.steps // 2))
     # HBM byte counters were recorded for the zigzag runs only
     out["roofline"]["traffic"] = recorded_traffic(wl.name, dominant) if d.partition == 0 else None
     if args.copy_calibration:

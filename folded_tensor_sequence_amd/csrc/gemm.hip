@@ -64,9 +64,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// The epilogue input of columns n..n+3 of row m, for the epilogues that read
+// one (the residual, or dA): loaded apart from the epilogue itself so that a
+// tile issues all its input loads before its first store (the stores may
+// alias the inputs as far as the compiler knows, so loads placed between
+// them would each wait for the previous group's round trip).
+template <int EPI>
+__device__ __forceinline__ f32x4 epilogue_input(const GemmArgs& a, int m, int n) {
+  f32x4 r{0.f, 0.f, 0.f, 0.f};
+  if (m >= a.M || n >= a.N) return r;
+  const int64_t off = (int64_t)m * a.N + n;
+  if constexpr (EPI == EPI_RESID_BF16X) {
+    const u32x2 xr = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.resid) + off);
+    r[0] = __uint_as_float(xr[0] << 16);
+    r[1] = __uint_as_float(xr[0] & 0xffff0000u);
+    r[2] = __uint_as_float(xr[1] << 16);
+    r[3] = __uint_as_float(xr[1] & 0xffff0000u);
+  } else if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_SWIGLU_BWD) {
+    if (a.resid != nullptr) r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
+  }
+  return r;
+}
+
+template <int EPI>
+constexpr bool epilogue_reads() {
+  return EPI == EPI_RESID_BF16X || EPI == EPI_RESID_F32 || EPI == EPI_SWIGLU_BWD;
+}
+
+// in: the epilogue input (epilogue_input) for the epilogues that read one.
 template <int EPI>
 __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const float* v,
-                                          const float* v2) {
+                                          const float* v2, const f32x4& in) {
   if (m >= a.M || n >= a.N) return;
   if constexpr (EPI == EPI_QKV) {
     const Shape& s = a.s;
@@ -90,12 +118,11 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
     }
   } else if constexpr (EPI == EPI_RESID_BF16X) {
     const int64_t off = (int64_t)m * a.N + n;
-    const u32x2 xr = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.resid) + off);
     f32x4 o;
-    o[0] = __uint_as_float(xr[0] << 16) + v[0];
-    o[1] = __uint_as_float(xr[0] & 0xffff0000u) + v[1];
-    o[2] = __uint_as_float(xr[1] << 16) + v[2];
-    o[3] = __uint_as_float(xr[1] & 0xffff0000u) + v[3];
+    o[0] = in[0] + v[0];
+    o[1] = in[1] + v[1];
+    o[2] = in[2] + v[2];
+    o[3] = in[3] + v[3];
     *reinterpret_cast<f32x4*>(a.out + off) = o;
     if (a.out16 != nullptr) {
       u32x2 pk{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
@@ -106,11 +133,10 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
     const int64_t off = (int64_t)m * a.N + n;
     f32x4 o{v[0], v[1], v[2], v[3]};
     if (a.resid != nullptr) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
-      o[0] = r[0] + v[0];
-      o[1] = r[1] + v[1];
-      o[2] = r[2] + v[2];
-      o[3] = r[3] + v[3];
+      o[0] = in[0] + v[0];
+      o[1] = in[1] + v[1];
+      o[2] = in[2] + v[2];
+      o[3] = in[3] + v[3];
     }
     *reinterpret_cast<f32x4*>(a.out + off) = o;
     if (a.out16 != nullptr) {
@@ -128,7 +154,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
     // then its dU block, per row).  The four columns lie in one shard.
     const Shape& s = a.s;
     const int64_t off = (int64_t)m * a.N + n;
-    const f32x4 da = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
+    const f32x4& da = in;
     float av[4], dg[4], du[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -266,7 +292,17 @@ template <int MB, int NBL, int NB, int EPI>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[NB][NBL][MB], int m_base,
                                            int n_base, int lrow, int lgrp, int split) {
 #pragma unroll
-  for (int y = 0; y < NBL; ++y)
+  for (int y = 0; y < NBL; ++y) {
+    // the inputs of this column block's groups first (see epilogue_input),
+    // then its stores: MB x 4 loads in flight at a time
+    f32x4 in[MB][4];
+    if constexpr (epilogue_reads<EPI>()) {
+#pragma unroll
+      for (int z = 0; z < MB; ++z)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          in[z][q4] = epilogue_input<EPI>(a, m_base + z * 32 + lrow, n_base + y * 32 + 8 * q4 + 4 * lgrp);
+    }
 #pragma unroll
     for (int z = 0; z < MB; ++z) {
       const int m = m_base + z * 32 + lrow;
@@ -288,12 +324,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
               f32x4 o{v[0], v[1], v[2], v[3]};
               *reinterpret_cast<f32x4*>(a.partial + ((int64_t)split * a.M + m) * a.N + n) = o;
             }
+          } else if constexpr (epilogue_reads<EPI>()) {
+            epilogue4<EPI>(a, m, n, v, v2, in[z][q4]);
           } else {
-            epilogue4<EPI>(a, m, n, v, v2);
+            epilogue4<EPI>(a, m, n, v, v2, f32x4{0.f, 0.f, 0.f, 0.f});
           }
         }
       }
     }
+  }
 }
 
 template <int BM, int BN, int NB, int WGM, int NW, int BK, int NST, bool SEGFAST, bool F16, bool CONVB, int EPI,
@@ -896,7 +935,7 @@ __global__ void gemm_reduce_kernel(GemmArgs a) {
       acc[3] += t[3];
     }
     float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    epilogue4<EPI>(a, m, n, v, v);
+    epilogue4<EPI>(a, m, n, v, v, epilogue_input<EPI>(a, m, n));
   }
 }
 

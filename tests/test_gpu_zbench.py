@@ -41,3 +41,6 @@ def test_bench_prints_one_json_line(partition):
     assert j["seeds"]["inputs"] == 2 and j["host"]["cores"] >= 1
     assert j["versions"]["torch"] and len(j["versions"]["libtsp_sources_sha256"]) == 16
     assert j["parity"] is None            # the oracle legs are off in this short run
+    b = j["mlp_ring_bwd"]
+    assert b["ms_per_call"] > 0 and b["calls"] >= 3 and b["gflop_algorithmic"] > 0
+    assert abs(b["tflops"] - b["gflop_algorithmic"] / b["ms_per_call"]) <= 1e-2 * b["tflops"]
