@@ -167,3 +167,43 @@ def test_silu_grad_closed_forms():
     zt = torch.tensor(z, requires_grad=True)
     torch.nn.functional.silu(zt).sum().backward()
     np.testing.assert_allclose(bwd.silu_grad(z), zt.grad.numpy(), rtol=1e-14, atol=1e-300)
+
+
+@pytest.mark.parametrize("shape", TINY)
+@pytest.mark.parametrize("partition", [0, 1], ids=["zigzag", "striped"])
+def test_rank_attention_shares_sum_to_the_unsharded_gradients(shape, partition):
+    # every rank's share of the attention backward: its input gradient rows
+    # equal the unsharded dx - dh; its K/V contributions summed over ranks
+    # are the unsharded ones; its weight-gradient shares sum to dW_Q/K/V/O
+    d, inp, dy = _setup(shape, seed=35)
+    d = dataclasses.replace(d, partition=partition)
+    full = bwd.layer_backward(inp, d, dy)
+    B, S, D = d.batch, d.seq, d.degree
+    hq_s, hkv_s, dh = d.n_q_heads // D, d.n_kv_heads // D, d.head_dim
+    tot_o = 0.0
+    tot_qkv = 0.0
+    contrib = 0.0
+    for r in range(D):
+        dr = dataclasses.replace(d, rank=r)
+        sh = bwd.rank_attention_backward(inp, dr, full["dh"])
+        rows = orc.local_to_global(S, D, r, partition)
+        np.testing.assert_allclose(sh["dx_attn"], (full["dx"] - full["dh"])[:, rows], rtol=1e-10, atol=1e-11)
+        tot_o = tot_o + sh["dw_o"]
+        tot_qkv = tot_qkv + sh["dw_qkv"]
+        contrib = contrib + sh["dkv_contrib"]
+    np.testing.assert_allclose(tot_o, full["dw_o"], rtol=1e-10, atol=1e-11)
+    # packed per-shard rows -> unsharded dW_q, dW_k, dW_v
+    for j in range(D):
+        ql = slice(j * hq_s * dh, (j + 1) * hq_s * dh)
+        kl = slice(j * hkv_s * dh, (j + 1) * hkv_s * dh)
+        np.testing.assert_allclose(tot_qkv[j, :hq_s * dh], full["dw_q"][ql], rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(tot_qkv[j, hq_s * dh:(hq_s + hkv_s) * dh], full["dw_k"][kl], rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(tot_qkv[j, (hq_s + hkv_s) * dh:], full["dw_v"][kl], rtol=1e-10, atol=1e-11)
+    # the summed contributions are the whole sequence's dK, dV (x^T of them = dW_K, dW_V)
+    x = orc.bf16_bits_to_f64(inp["x"])
+    for j in range(D):
+        kl = slice(j * hkv_s * dh, (j + 1) * hkv_s * dh)
+        np.testing.assert_allclose(np.einsum("bsk,bsh->kh", contrib[j, 0], x), full["dw_k"][kl], rtol=1e-10,
+                                   atol=1e-11)
+        np.testing.assert_allclose(np.einsum("bsk,bsh->kh", contrib[j, 1], x), full["dw_v"][kl], rtol=1e-10,
+                                   atol=1e-11)
