@@ -46,6 +46,7 @@ Gradient formulas (standard calculus; nothing is approximated):
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 
 import numpy as np
@@ -53,7 +54,8 @@ import numpy as np
 from .tsp_oracle import _dims, _part, bf16_bits_to_f64, causal_attention, global_to_slot, local_to_global, silu
 
 __all__ = ["sigmoid", "silu_grad", "mlp_backward", "attention_backward", "layer_backward",
-           "rank_mlp_backward", "tsp_backward_schedule"]
+           "rank_mlp_backward", "tsp_backward_schedule", "rank_attention_bwd_queries", "rank_attention_bwd_proj",
+           "reduce_scatter_dkv", "rank_attention_backward"]
 
 WEIGHTS = ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d")
 
@@ -289,78 +291,108 @@ def tsp_backward_schedule(inputs: dict, dims, dy: np.ndarray) -> dict:
 # One rank's share of the attention backward (the pieces of the schedule above
 # that rank r computes, for the per-kernel tests)
 # --------------------------------------------------------------------------- #
-def rank_attention_backward(inputs: dict, dims, dh_all: np.ndarray) -> dict:
-    """Rank dims.rank's share of the attention backward, given the gradient at
-    h = x + Attn(x) for every token (dh_all [B][S][h], sequence order):
+def rank_attention_bwd_queries(inputs: dict, dims, dh_rows: np.ndarray) -> dict:
+    """The part of rank dims.rank's attention backward that comes before the
+    reduce-scatter, from the gradient at h = x + Attn(x) of its own tokens
+    (dh_rows [B][T][h], local row order):
 
       dq          [B][T][Hq*dh]   its queries' gradient (unscaled Q space)
       dkv_contrib [D][2][B][S][Hkv/D*dh]  its queries' contribution to every
                   key's K and V gradient, per shard j, keys in sequence order
                   (what the reduce-scatter sums over ranks)
       dw_o        [h][Hq*dh]      its tokens' share of dW_O
-      dkv_own     [D][2][B][T][Hkv/D*dh]  the K/V gradient of its own tokens
-                  summed over every rank's queries (after the reduce-scatter)
-      dw_qkv      [D][(Hq/D + 2 Hkv/D)*dh][h]  its tokens' share of the packed
-                  Q/K/V weight gradients (the tsp_qkv_proj packing)
-      dx_attn     [B][T][h]       the attention branch's input gradient
-                  dQ W_Q + dK W_K + dV W_V (dh itself not added)
+      do, o       [B][T][Hq*dh]   the output gradient dh W_O and the
+                  recomputed attention output
     """
     B, S, D, r, h, Hq, Hkv, dh, F = _dims(dims)
     T = S // D
-    hq_s, hkv_s = Hq // D, Hkv // D
+    hkv_s = Hkv // D
     w = _weights(inputs)
     x_all = bf16_bits_to_f64(inputs["x"])
-    part = _part(dims)
-    l2g = [local_to_global(S, D, q, part) for q in range(D)]
+    rows = local_to_global(S, D, r, _part(dims))
     group = Hq // Hkv
-    pos = np.arange(S)
     k_all = x_all @ w["w_k"].T          # [B][S][Hkv*dh]
     v_all = x_all @ w["w_v"].T
-
-    def queries_share(rq):
-        """dq of rank rq's rows and their contribution to every key's dK, dV."""
-        rows = l2g[rq]
-        x = x_all[:, rows]
-        q = x @ w["w_q"].T
-        dhr = np.asarray(dh_all, dtype=np.float64)[:, rows]
-        do = dhr @ w["w_o"]
-        dq = np.zeros((B, T, Hq * dh))
-        dk = np.zeros((B, S, Hkv * dh))
-        dv = np.zeros((B, S, Hkv * dh))
-        o = np.zeros((B, T, Hq * dh))
-        for b in range(B):
-            for i in range(Hq):
-                kvh = i // group
-                sl, kl = slice(i * dh, (i + 1) * dh), slice(kvh * dh, (kvh + 1) * dh)
-                o[b, :, sl] = causal_attention(q[b, :, sl], k_all[b, :, kl], v_all[b, :, kl], rows)
-                gq, gk, gv = attention_backward(q[b, :, sl], k_all[b, :, kl], v_all[b, :, kl], rows, do[b, :, sl])
-                dq[b, :, sl] = gq
-                dk[b, :, kl] += gk
-                dv[b, :, kl] += gv
-        return dq, dk, dv, o, x, dhr
-
-    dq, dk, dv, o, x, dhr = queries_share(r)
+    q = x_all[:, rows] @ w["w_q"].T
+    dhr = np.asarray(dh_rows, dtype=np.float64)
+    do = dhr @ w["w_o"]
+    dq = np.zeros((B, T, Hq * dh))
+    dk = np.zeros((B, S, Hkv * dh))
+    dv = np.zeros((B, S, Hkv * dh))
+    o = np.zeros((B, T, Hq * dh))
+    for b in range(B):
+        for i in range(Hq):
+            kvh = i // group
+            sl, kl = slice(i * dh, (i + 1) * dh), slice(kvh * dh, (kvh + 1) * dh)
+            o[b, :, sl] = causal_attention(q[b, :, sl], k_all[b, :, kl], v_all[b, :, kl], rows)
+            gq, gk, gv = attention_backward(q[b, :, sl], k_all[b, :, kl], v_all[b, :, kl], rows, do[b, :, sl])
+            dq[b, :, sl] = gq
+            dk[b, :, kl] += gk
+            dv[b, :, kl] += gv
     dkv_contrib = np.zeros((D, 2, B, S, hkv_s * dh))
     for j in range(D):
         kl = slice(j * hkv_s * dh, (j + 1) * hkv_s * dh)
         dkv_contrib[j, 0], dkv_contrib[j, 1] = dk[:, :, kl], dv[:, :, kl]
     dw_o = np.einsum("bth,btc->hc", dhr, o)
-    # the reduce-scatter: every rank's contribution to rank r's tokens
-    dk_own = np.zeros((B, T, Hkv * dh))
-    dv_own = np.zeros((B, T, Hkv * dh))
-    for rq in range(D):
-        _, gk, gv, _, _, _ = queries_share(rq) if rq != r else (None, dk, dv, None, None, None)
-        dk_own += gk[:, l2g[r]]
-        dv_own += gv[:, l2g[r]]
-    dkv_own = np.zeros((D, 2, B, T, hkv_s * dh))
-    for j in range(D):
-        kl = slice(j * hkv_s * dh, (j + 1) * hkv_s * dh)
-        dkv_own[j, 0], dkv_own[j, 1] = dk_own[:, :, kl], dv_own[:, :, kl]
+    return {"dq": dq, "dkv_contrib": dkv_contrib, "dw_o": dw_o, "do": do, "o": o}
+
+
+def rank_attention_bwd_proj(inputs: dict, dims, dq: np.ndarray, dkv_own: np.ndarray) -> dict:
+    """The part after the reduce-scatter, from the rank's query gradient dq
+    [B][T][Hq*dh] and the K/V gradient of its own tokens summed over every
+    rank's queries (dkv_own [D][2][B][T][Hkv/D*dh], per shard j):
+
+      dw_qkv  [D][(Hq/D + 2 Hkv/D)*dh][h]  its tokens' share of the packed
+              Q/K/V weight gradients (the tsp_qkv_proj packing)
+      dx_attn [B][T][h]  the attention branch's input gradient
+              dQ W_Q + dK W_K + dV W_V (the residual's dh not added)
+    """
+    B, S, D, r, h, Hq, Hkv, dh, F = _dims(dims)
+    hq_s, hkv_s = Hq // D, Hkv // D
+    w = _weights(inputs)
+    x = bf16_bits_to_f64(inputs["x"])[:, local_to_global(S, D, r, _part(dims))]
+    dq = np.asarray(dq, dtype=np.float64)
+    dkv_own = np.asarray(dkv_own, dtype=np.float64)
+    dk_own = np.concatenate([dkv_own[j, 0] for j in range(D)], axis=2)   # [B][T][Hkv*dh]
+    dv_own = np.concatenate([dkv_own[j, 1] for j in range(D)], axis=2)
     dw_qkv = np.zeros((D, (hq_s + 2 * hkv_s) * dh, h))
     for j in range(D):
         ql, kl = slice(j * hq_s * dh, (j + 1) * hq_s * dh), slice(j * hkv_s * dh, (j + 1) * hkv_s * dh)
         g = np.concatenate([dq[:, :, ql], dk_own[:, :, kl], dv_own[:, :, kl]], axis=2)   # [B][T][nqkv_s]
         dw_qkv[j] = np.einsum("btn,bth->nh", g, x)
     dx_attn = dq @ w["w_q"] + dk_own @ w["w_k"] + dv_own @ w["w_v"]
-    return {"dq": dq, "dkv_contrib": dkv_contrib, "dw_o": dw_o, "dkv_own": dkv_own, "dw_qkv": dw_qkv,
-            "dx_attn": dx_attn, "do": dhr @ w["w_o"], "o": o}
+    return {"dw_qkv": dw_qkv, "dx_attn": dx_attn}
+
+
+def reduce_scatter_dkv(contribs: list, dims) -> np.ndarray:
+    """The reduce-scatter of the K/V gradients: rank dims.rank's own tokens'
+    rows of the D ranks' contributions ([D][2][B][S][Hkv/D*dh] each), summed
+    -> [D][2][B][T][Hkv/D*dh]."""
+    B, S, D, r, h, Hq, Hkv, dh, F = _dims(dims)
+    rows = local_to_global(S, D, r, _part(dims))
+    return sum(np.asarray(c, dtype=np.float64)[:, :, :, rows] for c in contribs)
+
+
+def rank_attention_backward(inputs: dict, dims, dh_all: np.ndarray) -> dict:
+    """Rank dims.rank's whole share of the attention backward, given the
+    gradient at h = x + Attn(x) for every token (dh_all [B][S][h], sequence
+    order): the entries of rank_attention_bwd_queries for its own tokens,
+    dkv_own (the reduce-scatter of every rank's contribution) and the entries
+    of rank_attention_bwd_proj."""
+    B, S, D, r, h, Hq, Hkv, dh, F = _dims(dims)
+    part = _part(dims)
+    dh_all = np.asarray(dh_all, dtype=np.float64)
+    shares = []
+    for rq in range(D):
+        drq = _with_rank(dims, rq)
+        shares.append(rank_attention_bwd_queries(inputs, drq, dh_all[:, local_to_global(S, D, rq, part)]))
+    own = shares[r]
+    dkv_own = reduce_scatter_dkv([sh["dkv_contrib"] for sh in shares], dims)
+    out = dict(own)
+    out["dkv_own"] = dkv_own
+    out.update(rank_attention_bwd_proj(inputs, dims, own["dq"], dkv_own))
+    return out
+
+
+def _with_rank(dims, rank):
+    return dataclasses.replace(dims, rank=rank)
