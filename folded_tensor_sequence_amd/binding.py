@@ -49,8 +49,11 @@ TSP_FN_LAYER = 3
 TSP_FN_KV_NATURAL = 4
 TSP_FN_KV_GATHERED = 5
 TSP_FN_MLP_BWD = 6
+TSP_FN_ATTN_BWD = 7
+TSP_FN_ATTN_BWD_PROJ = 8
+TSP_FN_DKV = 9
 
-KERNELS = {"qkv": 1, "reorder": 2, "attn": 3, "oproj": 4, "gateup": 5, "down": 6}
+KERNELS = {"qkv": 1, "reorder": 2, "attn": 3, "oproj": 4, "gateup": 5, "down": 6, "attn_bwd": 7}
 
 TUNE = {"gemm_qkv": 0, "gemm_oproj": 1, "gemm_gateup": 2, "gemm_down": 3, "split_oproj": 4,
         "split_down": 5, "attn_shape": 6, "attn_pair": 7, "attn_pieces": 8}
@@ -58,7 +61,7 @@ TUNE = {"gemm_qkv": 0, "gemm_oproj": 1, "gemm_gateup": 2, "gemm_down": 3, "split
 EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd",
             "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",
             "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning", "tsp_layer_fwd_noalloc",
-            "tsp_mlp_ring_bwd")
+            "tsp_mlp_ring_bwd", "tsp_attn_bwd", "tsp_attn_bwd_proj")
 
 # Size of the library's fixed scratch array (TSP_SCRATCH_BYTES in include/tsp.h).
 TSP_SCRATCH_BYTES = 128 * 1024 * 1024
@@ -99,6 +102,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tsp_layer_fwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_layer_fwd_noalloc": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "tsp_mlp_ring_bwd": [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_attn_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_attn_bwd_proj": [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -173,6 +178,8 @@ class _Sizes:
         self.w_o = 2 * d.hidden * d.n_q_heads * d.head_dim
         self.w_ffn = 2 * d.ffn * d.hidden
         self.q = 2 * self.M * d.n_q_heads * d.head_dim
+        self.dq = 2 * self.q                                  # float32 [B][T][Hq*dh]
+        self.dkv_own = 4 * 2 * self.M * d.n_kv_heads * d.head_dim
         self.l2g = 4 * self.T
         self.g2s = 4 * d.seq
         self.dims = d
@@ -304,6 +311,34 @@ def tsp_mlp_ring_bwd(dims, x, dy, w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_d
         _tensor(dx_residual, "dx_residual", "f32", z.f32, optional=True), _tensor(dx, "dx", "f32", z.f32),
         _tensor(dw_gate, "dw_gate", "f32", fw), _tensor(dw_up, "dw_up", "f32", fw),
         _tensor(dw_down, "dw_down", "f32", fw), wsp, wsn, _s(stream)))
+
+
+def tsp_attn_bwd(dims, x_local, w_qkv, w_o, kv_gathered, dh, dq, dkv_send, dw_o, ws, stream=None):
+    """Attention backward before the K/V-gradient reduce-scatter: dq, the rank's
+    contribution to every key's dK/dV (grouped by owner rank) and its dW_O share."""
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    wsp, wsn = _ws(dims, ws, TSP_FN_ATTN_BWD)
+    _check(load().tsp_attn_bwd(
+        ctypes.byref(d), _tensor(x_local, "x_local", "bf16", z.x16), _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv),
+        _tensor(w_o, "w_o", "bf16", z.w_o),
+        _tensor(kv_gathered, "kv_gathered", "f16", tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+        _tensor(dh, "dh", "f32", z.f32), _tensor(dq, "dq", "f32", z.dq),
+        _tensor(dkv_send, "dkv_send", "f32", tsp_workspace_bytes(dims, TSP_FN_DKV)),
+        _tensor(dw_o, "dw_o", "f32", 2 * z.w_o), wsp, wsn, _s(stream)))
+
+
+def tsp_attn_bwd_proj(dims, x_local, w_qkv, dq, dkv_own, dx, dw_qkv, ws, dx_residual=None, stream=None):
+    """Attention backward after the reduce-scatter: dx = dx_residual + dQ W_Q + dK W_K
+    + dV W_V and the rank's share of the packed dW_QKV."""
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    wsp, wsn = _ws(dims, ws, TSP_FN_ATTN_BWD_PROJ)
+    _check(load().tsp_attn_bwd_proj(
+        ctypes.byref(d), _tensor(x_local, "x_local", "bf16", z.x16), _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv),
+        _tensor(dq, "dq", "f32", z.dq), _tensor(dkv_own, "dkv_own", "f32", z.dkv_own),
+        _tensor(dx_residual, "dx_residual", "f32", z.f32, optional=True), _tensor(dx, "dx", "f32", z.f32),
+        _tensor(dw_qkv, "dw_qkv", "f32", 2 * z.w_qkv), wsp, wsn, _s(stream)))
 
 
 def tsp_layer_fwd(dims, x_local, w_qkv, w_o, w_gate, w_up, w_down, kv_gathered, y, ws, stream=None):

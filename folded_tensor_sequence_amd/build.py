@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtsp.so")
-SOURCES = ["tsp_abi.cpp", "zigzag.hip", "gemm.hip", "attention.hip", "transpose.hip"]
+SOURCES = ["tsp_abi.cpp", "zigzag.hip", "gemm.hip", "attention.hip", "attention_bwd.hip", "transpose.hip"]
 ARCH = "gfx950"
 
 # Packed FP32 instructions stay off: the kernels rely on ordinary float code.

@@ -49,6 +49,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "attn_common.h"
 #include "attn_plan.h"
 #include "common.h"
 #include "kernels.h"
@@ -61,6 +62,8 @@ struct AttnArgs {
   uint16_t* o;           // f16 [B][T][Hq*dh]
   float* part_o;         // [pieces][B*Hq][rb][dh] unnormalised outputs of split blocks
   float* part_ml;        // [pieces][B*Hq][2][rb] (scaled max, sum)
+  float* lse;            // optional [B][Hq][T]: log2 of each row's softmax normaliser
+                         // (scaled scores), so that p = 2^(s * scale_log2 - lse)
   Shape s;
   float scale_log2;      // log2(e) / sqrt(dh)
   int32_t rb;            // rows per block: 32 per wave (128 or 256)
@@ -68,12 +71,6 @@ struct AttnArgs {
   int32_t kt_max;        // key tiles per piece at most
   int32_t pair;          // 1: each earlier-chunk block rides with a later-chunk block
 };
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ void attn_load_lds16(const uint16_t* g, unsigned char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
-}
 
 // Row permutation inside each 32-key group: swaps 4-row blocks 1<->2, 5<->6.
 __device__ __forceinline__ int key_perm(int i) {
@@ -111,24 +108,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// Row of the all-gathered K/V buffer holding global position p.  Zigzag:
-// chunk q = p / c lives on rank q (q < D) or 2D-1-q, at local row p mod c
-// (+ c for the later chunk).  Striped: rank p mod D, local row p div D.
-__device__ __forceinline__ int64_t gathered_row(const Shape& s, int j, int sel, int b, int p) {
-  int g, t;
-  if (s.part == 1) {
-    g = p % s.D;
-    t = p / s.D;
-  } else {
-    const int qc = p / s.c;
-    g = qc < s.D ? qc : 2 * s.D - 1 - qc;
-    t = (qc < s.D ? 0 : s.c) + (p - qc * s.c);
-  }
-  return ((((int64_t)j * s.D + g) * 2 + sel) * s.B + b) * s.T + t;
-}
 
 // K/V tile addressing (KM):
 //   KM_ROW    any shape: every lane maps its own key through gathered_row;
@@ -447,6 +426,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
     if (!wave_active || !lane_valid) continue;
     if (!split) {
       const float inv = 1.0f / l_tot;
+      if (a.lse != nullptr && lgrp == 0) a.lse[((int64_t)b * s.Hq + qh) * s.T + t_lane] = m_run + log2f(l_tot);
       uint16_t* orow = a.o + ((int64_t)b * s.T + t_lane) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -518,6 +498,7 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   }
   const float inv = 1.0f / l;
   const int b = bh / s.Hq, qh = bh - b * s.Hq;
+  if (a.lse != nullptr && c4 == 0) a.lse[((int64_t)b * s.Hq + qh) * s.T + t] = mmax + log2f(l);
   uint16_t* orow = a.o + ((int64_t)b * s.T + t) * ((int64_t)s.Hq * DH) + (int64_t)qh * DH + 4 * c4;
   u32x2 pk{pack_f16x2(acc[0] * inv, acc[1] * inv), pack_f16x2(acc[2] * inv, acc[3] * inv)};
   *reinterpret_cast<u32x2*>(orow) = pk;
@@ -628,6 +609,12 @@ static AttnPlan plan_for(const Shape& s, int pair, AttnShape k) {
 // blocks are split along the keys estimate the makespan at all.
 AttnPlan attn_plan(const Shape& s) { return plan_for(s, -1, attn_shape(s)); }
 
+AttnPlan attn_plan_shape(const Shape& s, int nwv) {
+  for (const AttnShape& k : kShapes)
+    if (k.nwv == nwv) return plan_for(s, -1, k);
+  return plan_for(s, -1, kShapes[0]);
+}
+
 // Enough for every plan, so that a workspace sized once serves them all.
 size_t attn_partial_bytes(const Shape& s) {
   size_t most = 0;
@@ -660,9 +647,10 @@ static void launch_fa_shape(const AttnPlan& p, const AttnArgs& a, int km, hipStr
 }
 
 hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, uint16_t* o,
-                             float* partial, hipStream_t st) {
+                             float* partial, hipStream_t st, float* lse) {
   const AttnPlan p = attn_plan(s);
   AttnArgs a;
+  a.lse = lse;
   a.q = q;
   a.kv = kv_gathered;
   a.o = o;

@@ -46,9 +46,11 @@ struct GemmArgs {
   // split-K: nsplit > 1 writes float32 partial sums to partial[split][M][N]
   int32_t nsplit;
   float* partial;
-  // backward epilogues: a second float32 output and a second bf16 output
+  // backward epilogues: a second float32 output and a second bf16 output;
+  // EPI_DWD: columns per weight shard
   float* out2;
   uint16_t* aux16;
+  int32_t shard_w;
 };
 
 __device__ __forceinline__ float silu_f32(float z) {
@@ -129,7 +131,8 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
       *reinterpret_cast<u32x2*>(a.out16 + off) = pk;
     }
   } else if constexpr (EPI == EPI_RESID_F32) {
-    // float32 residual, or none (the branch alone) when resid is null
+    // float32 residual, or none (the branch alone) when resid is null; the
+    // float32 output may be skipped (out null) when only out16 is wanted
     const int64_t off = (int64_t)m * a.N + n;
     f32x4 o{v[0], v[1], v[2], v[3]};
     if (a.resid != nullptr) {
@@ -138,7 +141,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
       o[2] = in[2] + v[2];
       o[3] = in[3] + v[3];
     }
-    *reinterpret_cast<f32x4*>(a.out + off) = o;
+    if (a.out != nullptr) *reinterpret_cast<f32x4*>(a.out + off) = o;
     if (a.out16 != nullptr) {
       u32x2 pk{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
       *reinterpret_cast<u32x2*>(a.out16 + off) = pk;
@@ -174,11 +177,12 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
     *reinterpret_cast<u32x2*>(gu) = pg;
     *reinterpret_cast<u32x2*>(gu + s.F_s) = pu;
   } else if constexpr (EPI == EPI_DWD) {
-    // C [h][F] (row = hidden index, column = F index) -> dW_down [D][h][F/D]
-    const Shape& s = a.s;
-    const int j = n / s.F_s, f = n - j * s.F_s;
+    // C [M][N] (row m = hidden index, column n) -> out [N / w][M][w], w =
+    // shard_w: dW_down [D][h][F/D], dW_O [D][h][Hq/D dh]
+    const int w = a.shard_w;
+    const int j = n / w, f = n - j * w;
     f32x4 o{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(a.out + ((int64_t)j * s.h + m) * s.F_s + f) = o;
+    *reinterpret_cast<f32x4*>(a.out + ((int64_t)j * a.M + m) * w + f) = o;
   } else if constexpr (EPI == EPI_DWGU) {
     // C [2F][h], rows in the [D][2][F/D] order of the dG|dU buffer ->
     // dW_gate (out) or dW_up (out2), both [F][h]
@@ -1269,6 +1273,7 @@ hipError_t launch_bwd_dwd(const Shape& s, int m_pad, const uint16_t* dyT, const 
   a.K = m_pad;
   a.seg_len = m_pad;
   a.out = dw_down;
+  a.shard_w = s.F_s;
   return launch_cfg<false, false, EPI_DWD>(a, 0, 1, st);
 }
 
@@ -1286,6 +1291,103 @@ hipError_t launch_bwd_dwgu(const Shape& s, int m_pad, const uint16_t* dguT, cons
   a.out = dw_gate;
   a.out2 = dw_up;
   return launch_cfg<false, false, EPI_DWGU>(a, 0, 1, st);
+}
+
+// ---- backward of the attention (projections) --------------------------------
+// q = x Wq^T for the rank's tokens, Wq [Hq*dh][h] the Q rows of every shard:
+// the Q/K/V epilogue with every column a Q column (a shard of Hq/D dh).
+hipError_t launch_q_gemm(const Shape& s, const uint16_t* x, const uint16_t* w_q, uint16_t* q, hipStream_t st) {
+  Shape sq = s;
+  sq.nqkv_s = s.Hq_s * s.dh;
+  GemmArgs a = base_args(sq);
+  a.A = x;
+  a.lda = s.h;
+  a.B0 = a.B1 = w_q;
+  a.ldb = s.h;
+  a.M = s.M;
+  a.N = s.Hq * s.dh;
+  a.K = s.h;
+  a.seg_len = s.h;
+  a.q = q;
+  a.kv = nullptr;
+  a.src_rank = s.r;
+  return launch_single<false, false, EPI_QKV>(a, -1, -1, 1, st);
+}
+
+// dO = dh16 WoT^T stored f16 [M][Hq*dh]; WoT [Hq*dh][h] bf16.
+hipError_t launch_attn_bwd_do(const Shape& s, const uint16_t* dh16, const uint16_t* woT, uint16_t* dout,
+                              hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = dh16;
+  a.lda = s.h;
+  a.B0 = a.B1 = woT;
+  a.ldb = s.h;
+  a.M = s.M;
+  a.N = s.Hq * s.dh;
+  a.K = s.h;
+  a.seg_len = s.h;
+  a.out = nullptr;
+  a.out16 = dout;
+  a.resid = nullptr;
+  return launch_cfg<false, false, EPI_RESID_F32>(a, 0, 1, st);
+}
+
+// dW_O [D][h][Hq/D dh] = dhT oT^T (both [.][m_pad] bf16).
+hipError_t launch_attn_bwd_dwo(const Shape& s, int m_pad, const uint16_t* dhT, const uint16_t* oT, float* dw_o,
+                               hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = dhT;
+  a.lda = m_pad;
+  a.B0 = a.B1 = oT;
+  a.ldb = m_pad;
+  a.M = s.h;
+  a.N = s.Hq * s.dh;
+  a.K = m_pad;
+  a.seg_len = m_pad;
+  a.out = dw_o;
+  a.shard_w = s.Hq_s * s.dh;
+  return launch_cfg<false, false, EPI_DWD>(a, 0, 1, st);
+}
+
+// dx = dx_resid + sum over the shards (ring order) of G_j WqkvT_j^T, G [M][D
+// nqkv_s] the packed dQ | dK | dV rows of every shard, WqkvT [h][D nqkv_s].
+hipError_t launch_attn_bwd_dx(const Shape& s, const uint16_t* g16, const uint16_t* wqkvT, const float* dx_resid,
+                              float* dx, float* partial, hipStream_t st) {
+  GemmArgs a = base_args(s);
+  const int seg = s.nqkv_s;
+  a.A = g16;
+  a.lda = (int64_t)s.D * seg;
+  a.a_seg_step = seg;
+  a.B0 = a.B1 = wqkvT;
+  a.ldb = (int64_t)s.D * seg;
+  a.b_seg_step = seg;
+  a.M = s.M;
+  a.N = s.h;
+  a.K = s.D * seg;
+  a.seg_len = seg;
+  a.nseg = s.D;
+  a.ring_rank = s.r;
+  a.out = dx;
+  a.resid = dx_resid;
+  a.partial = partial;
+  return launch_single<false, false, EPI_RESID_F32>(a, -1, -1, gemm_split_plan(s), st);
+}
+
+// dW_QKV [D nqkv_s][h] = gT xT^T (both [.][m_pad] bf16): the packed layout.
+hipError_t launch_attn_bwd_dwqkv(const Shape& s, int m_pad, const uint16_t* gT, const uint16_t* xT, float* dw_qkv,
+                                 hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = gT;
+  a.lda = m_pad;
+  a.B0 = a.B1 = xT;
+  a.ldb = m_pad;
+  a.M = s.D * s.nqkv_s;
+  a.N = s.h;
+  a.K = m_pad;
+  a.seg_len = m_pad;
+  a.out = dw_qkv;
+  a.resid = nullptr;
+  return launch_cfg<false, false, EPI_RESID_F32>(a, 0, 1, st);
 }
 
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n4) {

@@ -97,8 +97,42 @@ struct AttnPlan {
   int split_rows;   // rb x (number of split blocks)
 };
 AttnPlan attn_plan(const Shape& s);
+// The default plan for blocks of nwv waves (4 or 8).
+AttnPlan attn_plan_shape(const Shape& s, int nwv);
 size_t attn_partial_bytes(const Shape& s);
+// lse (optional, float [B][Hq][T]): each row's log2 softmax normaliser of
+// the scaled scores, for the backward pass.
 hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, uint16_t* o,
-                             float* partial, hipStream_t st);
+                             float* partial, hipStream_t st, float* lse = nullptr);
+
+// ---- backward of the attention ----------------------------------------------
+// Projections (bf16 matrix cores): q = x Wq^T (Wq [Hq*dh][h], q f16 [B][Hq][T][dh]);
+// dO = dh16 WoT^T (f16 [M][Hq*dh]); dW_O [D][h][Hq/D dh] = dhT oT^T;
+// dx = dx_resid + G WqkvT^T (G [M][D nqkv_s] bf16, ring order over the
+// shards); dW_QKV [D nqkv_s][h] = gT xT^T.
+hipError_t launch_q_gemm(const Shape& s, const uint16_t* x, const uint16_t* w_q, uint16_t* q, hipStream_t st);
+hipError_t launch_attn_bwd_do(const Shape& s, const uint16_t* dh16, const uint16_t* woT, uint16_t* dout,
+                              hipStream_t st);
+hipError_t launch_attn_bwd_dwo(const Shape& s, int m_pad, const uint16_t* dhT, const uint16_t* oT, float* dw_o,
+                               hipStream_t st);
+hipError_t launch_attn_bwd_dx(const Shape& s, const uint16_t* g16, const uint16_t* wqkvT, const float* dx_resid,
+                              float* dx, float* partial, hipStream_t st);
+hipError_t launch_attn_bwd_dwqkv(const Shape& s, int m_pad, const uint16_t* gT, const uint16_t* xT, float* dw_qkv,
+                                 hipStream_t st);
+// out[b][r][c] = bf16(in[b][r][c]) (bit copy for a bf16 input), r < R, c < C
+// (C a multiple of 8, rows 16-byte aligned).
+hipError_t launch_copy_bf16(int tin, const void* in, int64_t ld_in, int64_t in_bstride, uint16_t* out,
+                            int64_t ld_out, int64_t out_bstride, int R, int C, int batches, hipStream_t st);
+
+// From the rank's Q (f16 [B][Hq][T][dh]), the all-gathered K/V, the
+// recomputed output O and its gradient dO (f16 [B][T][Hq*dh]) and the
+// forward's row normalisers lse ([B][Hq][T]): delta = rowsum(dO * O)
+// ([B][Hq][T], written), dq (float [B][T][Hq*dh], unscaled Q space) and the
+// rank's contribution to every key's K/V gradient, dkv_send (float
+// [D dst][D shard][K|V][B][T][Hkv/D*dh], grouped by the keys' owner ranks).
+// partial: attn_partial_bytes of scratch (pieces of split row blocks).
+hipError_t launch_attn_bwd_core(const Shape& s, const uint16_t* q, const uint16_t* kv_gathered, const uint16_t* o,
+                                const uint16_t* dout, const float* lse, float* delta, float* dq, float* dkv_send,
+                                float* partial, hipStream_t st);
 
 }  // namespace tsp

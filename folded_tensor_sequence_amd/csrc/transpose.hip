@@ -117,6 +117,50 @@ hipError_t launch_transpose_bf16(int tin, const void* in, int64_t ld_in, int64_t
   return hipGetLastError();
 }
 
+// out[b][r][c] = bf16(in[b][r][c]): 8 elements (one 16-byte store) per
+// thread; grid (ceil(C / 8 / 64), min(R, 65535), batches), 64 threads, rows
+// strided by the grid's y extent.
+template <int TIN>
+__global__ __launch_bounds__(64) void copy_bf16_kernel(const void* __restrict__ in, int64_t ld_in, int64_t in_bstride,
+                                                       uint16_t* __restrict__ out, int64_t ld_out,
+                                                       int64_t out_bstride, int R, int C) {
+  const int c = (blockIdx.x * 64 + threadIdx.x) * 8;
+  if (c >= C) return;
+  const int64_t bz = blockIdx.z;
+  for (int64_t r = blockIdx.y; r < R; r += gridDim.y) {
+    float v[8];
+    load8<TIN>(in, bz * in_bstride + r * ld_in + c, v);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)to_bf16(v[2 * e]) | ((uint32_t)to_bf16(v[2 * e + 1]) << 16);
+    *reinterpret_cast<u32x4*>(out + bz * out_bstride + r * ld_out + c) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+hipError_t launch_copy_bf16(int tin, const void* in, int64_t ld_in, int64_t in_bstride, uint16_t* out,
+                            int64_t ld_out, int64_t out_bstride, int R, int C, int batches, hipStream_t st) {
+  if (R < 0 || C < 0 || C % 8 != 0 || batches < 1 || batches > 65535) return hipErrorInvalidValue;
+  if (R == 0 || C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C / 8 + 63) / 64), (unsigned)(R < 65535 ? R : 65535), (unsigned)batches);
+  switch (tin) {
+    case TR_BF16:
+      hipLaunchKernelGGL(copy_bf16_kernel<TR_BF16>, grid, dim3(64), 0, st, in, ld_in, in_bstride, out, ld_out,
+                         out_bstride, R, C);
+      break;
+    case TR_F16:
+      hipLaunchKernelGGL(copy_bf16_kernel<TR_F16>, grid, dim3(64), 0, st, in, ld_in, in_bstride, out, ld_out,
+                         out_bstride, R, C);
+      break;
+    case TR_F32:
+      hipLaunchKernelGGL(copy_bf16_kernel<TR_F32>, grid, dim3(64), 0, st, in, ld_in, in_bstride, out, ld_out,
+                         out_bstride, R, C);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Elementwise float32 -> bf16 (round to nearest even), n a multiple of 4.
 __global__ void f32_to_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n4) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -154,6 +154,66 @@ size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullp
   return off + (part + 255) / 256 * 256;
 }
 
+// Sequential 256-byte aligned pieces of a workspace (base may be null to
+// only add up the size).
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = base != nullptr ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += up(bytes);
+    return p;
+  }
+};
+
+// Backward of the attention, part 1:
+// [q | Wq | o | lse | delta | dh16 | dh^T | Wo^T | dO | O^T | attention pieces]
+struct AttnBwdWs {
+  uint16_t *q, *wq, *o, *dh16, *dhT, *woT, *dout, *oT;
+  float *lse, *delta, *partial;
+};
+size_t ws_attn_bwd(const tsp::Shape& s, AttnBwdWs* w = nullptr, char* base = nullptr) {
+  AttnBwdWs tmp;
+  AttnBwdWs& x = w != nullptr ? *w : tmp;
+  const size_t M = s.M, h = s.h, qd = (size_t)s.Hq * s.dh, Mp = mpad(s), rows = (size_t)s.B * s.Hq * s.T;
+  Carve c{base};
+  x.q = c.take<uint16_t>(M * qd * 2);
+  x.wq = c.take<uint16_t>(qd * h * 2);
+  x.o = c.take<uint16_t>(M * qd * 2);
+  x.lse = c.take<float>(rows * 4);
+  x.delta = c.take<float>(rows * 4);
+  x.dh16 = c.take<uint16_t>(M * h * 2);
+  x.dhT = c.take<uint16_t>(h * Mp * 2);
+  x.woT = c.take<uint16_t>(qd * h * 2);
+  x.dout = c.take<uint16_t>(M * qd * 2);
+  x.oT = c.take<uint16_t>(qd * Mp * 2);
+  const size_t part = tsp::attn_partial_bytes(s);
+  x.partial = part > 0 ? c.take<float>(part) : nullptr;
+  return c.off;
+}
+
+// Part 2: [G | G^T | Wqkv^T | x^T | split-K partials]
+struct AttnBwdProjWs {
+  uint16_t *g16, *gT, *wqkvT, *xT;
+  float* partial;
+};
+size_t ws_attn_bwd_proj(const tsp::Shape& s, AttnBwdProjWs* w = nullptr, char* base = nullptr) {
+  AttnBwdProjWs tmp;
+  AttnBwdProjWs& x = w != nullptr ? *w : tmp;
+  const size_t M = s.M, h = s.h, Nall = (size_t)s.D * s.nqkv_s, Mp = mpad(s);
+  Carve c{base};
+  x.g16 = c.take<uint16_t>(M * Nall * 2);
+  x.gT = c.take<uint16_t>(Nall * Mp * 2);
+  x.wqkvT = c.take<uint16_t>(h * Nall * 2);
+  x.xT = c.take<uint16_t>(h * Mp * 2);
+  const int p = tsp::gemm_split_plan(s);
+  x.partial = p > 1 ? c.take<float>((size_t)p * M * h * 4) : nullptr;
+  return c.off;
+}
+
+size_t bytes_dkv(const tsp::Shape& s) { return (size_t)s.D * s.D * 2 * s.M * s.Hkv_s * s.dh * 4; }
+
 struct AttnWs {
   uint16_t *q, *o;
   float* partial;
@@ -373,6 +433,9 @@ size_t tsp_workspace_bytes(const tsp_dims_t* dims, int32_t fn) {
     case TSP_FN_KV_NATURAL: return bytes_kvnat(s);
     case TSP_FN_KV_GATHERED: return bytes_gathered(s);
     case TSP_FN_MLP_BWD: return ws_mlp_bwd(s);
+    case TSP_FN_ATTN_BWD: return ws_attn_bwd(s);
+    case TSP_FN_ATTN_BWD_PROJ: return ws_attn_bwd_proj(s);
+    case TSP_FN_DKV: return bytes_dkv(s);
     default: fail(TSP_ERR_INVALID_ARG, "unknown workspace selector %d", fn); return 0;
   }
 }
@@ -530,6 +593,96 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
              "mlp bwd: dGU^T");
   TSP_LAUNCH(tsp::launch_bwd_dwd(s, Mp, w.dyT, w.actT, dw_down, stream), "mlp bwd: dW_down");
   TSP_LAUNCH(tsp::launch_bwd_dwgu(s, Mp, w.dguT, w.xT, dw_gate, dw_up, stream), "mlp bwd: dW_gate, dW_up");
+  return TSP_OK;
+}
+
+int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const uint16_t* w_o,
+                 const uint16_t* kv_gathered, const float* dh, float* dq, float* dkv_send, float* dw_o, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(x_local, "x_local"));
+  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
+  TSP_TRY(need_ptr(w_o, "w_o"));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(need_ptr(dh, "dh"));
+  TSP_TRY(need_ptr(dq, "dq"));
+  TSP_TRY(need_ptr(dkv_send, "dkv_send"));
+  TSP_TRY(need_ptr(dw_o, "dw_o"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_attn_bwd(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_attn_bwd(s));
+  TSP_TRY(check_device("tsp_attn_bwd"));
+  AttnBwdWs w;
+  ws_attn_bwd(s, &w, static_cast<char*>(ws));
+  const int Mp = mpad(s), h = s.h, qs = s.Hq_s * s.dh;
+  // recomputation: Q rows of every shard, then Q and the attention output
+  // with its row normalisers
+  TSP_LAUNCH(tsp::launch_copy_bf16(tsp::TR_BF16, w_qkv, h, (int64_t)s.nqkv_s * h, w.wq, h, (int64_t)qs * h, qs, h,
+                                   s.D, stream),
+             "attn bwd: W_Q rows");
+  TSP_LAUNCH(tsp::launch_q_gemm(s, x_local, w.wq, w.q, stream), "attn bwd: Q");
+  TSP_LAUNCH(tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, stream, w.lse), "attn bwd: attention");
+  // dO = dh W_O (W_O_j [h][qs] -> WoT rows j qs ..: [qs][h])
+  TSP_LAUNCH(tsp::launch_f32_to_bf16(dh, w.dh16, (int64_t)s.M * h, stream), "attn bwd: dh to bf16");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_o, qs, (int64_t)h * qs, w.woT, h, (int64_t)qs * h, h, qs,
+                                        h, s.D, stream),
+             "attn bwd: W_O^T");
+  TSP_LAUNCH(tsp::launch_attn_bwd_do(s, w.dh16, w.woT, w.dout, stream), "attn bwd: dO");
+  {
+    const int slot = prof_open(TSP_K_ATTN_BWD, stream);
+    hipError_t e = tsp::launch_attn_bwd_core(s, w.q, kv_gathered, w.o, w.dout, w.lse, w.delta, dq, dkv_send,
+                                             w.partial, stream);
+    prof_close(slot, stream);
+    if (e != hipSuccess) return hip_fail(e, "attn bwd: dQ, dK, dV");
+  }
+  // dW_O = dh^T O
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_F32, dh, h, 0, w.dhT, Mp, 0, s.M, h, Mp, 1, stream),
+             "attn bwd: dh^T");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_F16, w.o, (int64_t)s.Hq * s.dh, 0, w.oT, Mp, 0, s.M, s.Hq * s.dh,
+                                        Mp, 1, stream),
+             "attn bwd: O^T");
+  TSP_LAUNCH(tsp::launch_attn_bwd_dwo(s, Mp, w.dhT, w.oT, dw_o, stream), "attn bwd: dW_O");
+  return TSP_OK;
+}
+
+int tsp_attn_bwd_proj(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const float* dq,
+                      const float* dkv_own, const float* dx_residual, float* dx, float* dw_qkv, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(x_local, "x_local"));
+  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
+  TSP_TRY(need_ptr(dq, "dq"));
+  TSP_TRY(need_ptr(dkv_own, "dkv_own"));
+  TSP_TRY(opt_ptr(dx_residual, "dx_residual"));
+  TSP_TRY(need_ptr(dx, "dx"));
+  TSP_TRY(need_ptr(dw_qkv, "dw_qkv"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_attn_bwd_proj(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_attn_bwd_proj(s));
+  TSP_TRY(check_device("tsp_attn_bwd_proj"));
+  AttnBwdProjWs w;
+  ws_attn_bwd_proj(s, &w, static_cast<char*>(ws));
+  const int Mp = mpad(s), h = s.h, qs = s.Hq_s * s.dh, kvs = s.Hkv_s * s.dh, n = s.nqkv_s;
+  const int64_t nall = (int64_t)s.D * n, own = (int64_t)s.M * kvs;
+  // G [M][D][dQ_j | dK_j | dV_j] in bf16
+  TSP_LAUNCH(tsp::launch_copy_bf16(tsp::TR_F32, dq, (int64_t)s.Hq * s.dh, qs, w.g16, nall, n, s.M, qs, s.D, stream),
+             "attn bwd proj: G (dQ)");
+  TSP_LAUNCH(tsp::launch_copy_bf16(tsp::TR_F32, dkv_own, kvs, 2 * own, w.g16 + qs, nall, n, s.M, kvs, s.D, stream),
+             "attn bwd proj: G (dK)");
+  TSP_LAUNCH(tsp::launch_copy_bf16(tsp::TR_F32, dkv_own + own, kvs, 2 * own, w.g16 + qs + kvs, nall, n, s.M, kvs,
+                                   s.D, stream),
+             "attn bwd proj: G (dV)");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w.g16, nall, 0, w.gT, Mp, 0, s.M, (int)nall, Mp, 1, stream),
+             "attn bwd proj: G^T");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_qkv, h, 0, w.wqkvT, nall, 0, (int)nall, h, (int)nall, 1,
+                                        stream),
+             "attn bwd proj: W_QKV^T");
+  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, x_local, h, 0, w.xT, Mp, 0, s.M, h, Mp, 1, stream),
+             "attn bwd proj: x^T");
+  TSP_LAUNCH(tsp::launch_attn_bwd_dx(s, w.g16, w.wqkvT, dx_residual, dx, w.partial, stream), "attn bwd proj: dx");
+  TSP_LAUNCH(tsp::launch_attn_bwd_dwqkv(s, Mp, w.gT, w.xT, dw_qkv, stream), "attn bwd proj: dW_QKV");
   return TSP_OK;
 }
 

@@ -114,7 +114,10 @@ typedef enum {
   TSP_FN_LAYER = 3,      /* tsp_layer_fwd workspace */
   TSP_FN_KV_NATURAL = 4, /* size of the kv_natural output of tsp_kv_reorder */
   TSP_FN_KV_GATHERED = 5, /* size of the kv_gathered buffer */
-  TSP_FN_MLP_BWD = 6     /* tsp_mlp_ring_bwd workspace */
+  TSP_FN_MLP_BWD = 6,    /* tsp_mlp_ring_bwd workspace */
+  TSP_FN_ATTN_BWD = 7,   /* tsp_attn_bwd workspace */
+  TSP_FN_ATTN_BWD_PROJ = 8, /* tsp_attn_bwd_proj workspace */
+  TSP_FN_DKV = 9         /* size of tsp_attn_bwd's dkv_send output */
 } tsp_fn;
 
 /* Maps of the partition dims->partition selects, as described above (TSP
@@ -245,6 +248,65 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
                      const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Backward of the attention on rank dims->rank, in the two parts that the
+ * K/V-gradient reduce-scatter separates.  The TSP article gives the forward
+ * schedule only ("How to Fold a Book": each rank projects its tokens with
+ * every shard, K and V are all-gathered, and each rank attends with its own
+ * queries over all keys); its transpose, for the gradient dh of the rank's
+ * tokens at the attention branch's output (h = x + Attn(x)):
+ *   1. tsp_attn_bwd: the rank recomputes Q = x W_Q^T and the attention
+ *      output O with its row normalisers (activation recomputation), forms
+ *      dO = dh W_O and, for every head, the softmax gradient
+ *          P = softmax(Q K^T / sqrt(dh)) (causal), dP = dO V^T,
+ *          dS = P * (dP - rowsum(dO * O)),
+ *          dQ = dS K / sqrt(dh),  dK = dS^T Q / sqrt(dh),  dV = P^T dO;
+ *      dK and dV of every key (all D ranks' tokens) are its contribution to
+ *      the reduce-scatter that returns each key's sum over all ranks' queries
+ *      to the key's owner.  Also its tokens' share of dW_O = dh^T O.
+ *   2. tsp_attn_bwd_proj, after the reduce-scatter: with dQ and the summed
+ *      dK, dV of its own tokens, the input gradient
+ *          dx = dx_residual + dQ W_Q + dK W_K + dV W_V
+ *      and its tokens' share of the packed dW_Q, dW_K, dW_V (summed at the
+ *      shard owners, the transpose of the weight broadcast).
+ * tsp_attn_bwd arguments:
+ *   x_local, w_qkv, w_o   as in tsp_attn_fwd
+ *   kv_gathered  f16, the all-gathered K/V (layout of tsp_attn_fwd), every
+ *                rank's slot filled (read only)
+ *   dh           float32 [B][T][h], the gradient at h of the rank's tokens
+ *   dq           float32 [B][T][Hq*dh] out: dL/dQ of the rank's queries
+ *                (Q = x W_Q^T, before the 1/sqrt(dh) scale)
+ *   dkv_send     float32 [D dst][D shard][K|V][B][T][Hkv/D*dh] out
+ *                (tsp_workspace_bytes(dims, TSP_FN_DKV) bytes): the rank's
+ *                contribution to the K and V gradients of every key, grouped
+ *                by the key's owner rank dst (so block dst is the piece the
+ *                reduce-scatter sends to rank dst) at the owner's local row;
+ *                zero for keys no query of this rank sees
+ *   dw_o         float32 [D][h][Hq/D*dh] out (the layout of w_o): this rank's
+ *                tokens' share of dW_O
+ *   ws           >= tsp_workspace_bytes(dims, TSP_FN_ATTN_BWD) bytes
+ * tsp_attn_bwd_proj arguments:
+ *   x_local, w_qkv  as in tsp_attn_fwd
+ *   dq           float32 [B][T][Hq*dh] (from tsp_attn_bwd)
+ *   dkv_own      float32 [D shard][K|V][B][T][Hkv/D*dh]: the sum over all D
+ *                ranks of their dkv_send blocks for this rank
+ *   dx_residual  float32 [B][T][h] or NULL, added to dx (pass dh for the
+ *                residual branch of h = x + Attn(x))
+ *   dx           float32 [B][T][h] out; may alias dx_residual
+ *   dw_qkv       float32 [D][(Hq/D + 2 Hkv/D)*dh][h] out (the layout of
+ *                w_qkv): this rank's tokens' share
+ *   ws           >= tsp_workspace_bytes(dims, TSP_FN_ATTN_BWD_PROJ) bytes
+ * Precision: Q, K, V, O, dO, P and dS enter the matrix cores as f16 (as in
+ * the forward; P and dS lie in [-1, 1] times dP's range); dh, O (for dW_O),
+ * the gradient rows and x enter the projection GEMMs as bf16; float32
+ * softmax, accumulation and outputs.  Both calls are deterministic (fixed
+ * summation order, no atomics). */
+int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const uint16_t* w_o,
+                 const uint16_t* kv_gathered, const float* dh, float* dq, float* dkv_send, float* dw_o, void* ws,
+                 size_t ws_bytes, hipStream_t stream);
+int tsp_attn_bwd_proj(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const float* dq,
+                      const float* dkv_own, const float* dx_residual, float* dx, float* dw_qkv, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
 /* Whole layer on rank dims->rank: h = x + Attn(x), y = h + MLP(h), with the
  * argument layouts of tsp_attn_fwd and tsp_mlp_ring_fwd.  h stays float32;
  * its f16 copy feeds the MLP matrix cores.
@@ -284,7 +346,8 @@ typedef enum {
   TSP_K_OPROJ = 4,   /* output projection GEMM (+ residual) */
   TSP_K_GATEUP = 5,  /* MLP gate/up GEMM with the SwiGLU epilogue */
   TSP_K_DOWN = 6,    /* MLP down-projection ring GEMM (+ residual) */
-  TSP_K_COUNT = 7
+  TSP_K_ATTN_BWD = 7, /* attention backward core: Delta, dQ (+ merge), dK/dV kernels */
+  TSP_K_COUNT = 8
 } tsp_kernel_id;
 
 /* Live timing of one kernel: after tsp_profile_kernel(id, n) the next n

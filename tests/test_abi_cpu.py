@@ -342,3 +342,43 @@ def test_mlp_bwd_argument_checks(lib):
     assert f(ctypes.byref(d), *args(), need - 1, None) == B.TSP_ERR_WORKSPACE
     bad = _dims(batch=0)
     assert f(ctypes.byref(bad), *args(), big, None) == B.TSP_ERR_BATCH
+
+
+def test_attn_bwd_argument_checks(lib):
+    d = _dims()
+    big = 1 << 40
+    f = lib.tsp_attn_bwd
+    names = ("x", "wqkv", "wo", "kv", "dh", "dq", "send", "dwo", "ws")
+    args = lambda **kw: [kw.get(n, FAKE) for n in names]
+    for n, label in zip(names, ("x_local", "w_qkv", "w_o", "kv_gathered", "dh", "dq", "dkv_send", "dw_o", "ws")):
+        assert f(ctypes.byref(d), *args(**{n: None}), big, None) == B.TSP_ERR_NULL_POINTER
+        assert f"{label} is NULL" in lib.tsp_last_error().decode()
+    assert f(ctypes.byref(d), *args(dh=MISALIGNED), big, None) == B.TSP_ERR_MISALIGNED
+    need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_ATTN_BWD)
+    assert need > 0 and need % 256 == 0
+    assert f(ctypes.byref(d), *args(), need - 1, None) == B.TSP_ERR_WORKSPACE
+    assert f(ctypes.byref(_dims(rank=5)), *args(), big, None) == B.TSP_ERR_RANK
+    g = lib.tsp_attn_bwd_proj
+    pnames = ("x", "wqkv", "dq", "own", "res", "dx", "dwqkv", "ws")
+    pargs = lambda **kw: [kw.get(n, None if n == "res" else FAKE) for n in pnames]
+    assert g(ctypes.byref(d), *pargs(own=None), big, None) == B.TSP_ERR_NULL_POINTER
+    assert "dkv_own is NULL" in lib.tsp_last_error().decode()
+    assert g(ctypes.byref(d), *pargs(res=MISALIGNED), big, None) == B.TSP_ERR_MISALIGNED
+    need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_ATTN_BWD_PROJ)
+    assert g(ctypes.byref(d), *pargs(), need - 1, None) == B.TSP_ERR_WORKSPACE
+    # past validation, no device: a HIP error, nothing launched
+    if not __import__("torch").cuda.is_available():
+        assert g(ctypes.byref(d), *pargs(), big, None) == B.TSP_ERR_HIP
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_attn_bwd_buffer_sizes(lib, name):
+    # the K/V-gradient send buffer: [D dst][D shard][K|V][B][T][Hkv/D dh] float32
+    d = synth.WORKLOADS[name].dims
+    s = B.dims_struct(d)
+    T = d.seq // d.degree
+    assert lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_DKV) == \
+        d.degree * d.degree * 2 * d.batch * T * (d.n_kv_heads // d.degree) * d.head_dim * 4
+    for fn in (B.TSP_FN_ATTN_BWD, B.TSP_FN_ATTN_BWD_PROJ):
+        n = lib.tsp_workspace_bytes(ctypes.byref(s), fn)
+        assert n > 0 and n % 256 == 0
