@@ -333,7 +333,7 @@ def rank_attention_bwd_queries(inputs: dict, dims, dh_rows: np.ndarray) -> dict:
     for j in range(D):
         kl = slice(j * hkv_s * dh, (j + 1) * hkv_s * dh)
         dkv_contrib[j, 0], dkv_contrib[j, 1] = dk[:, :, kl], dv[:, :, kl]
-    dw_o = np.einsum("bth,btc->hc", dhr, o)
+    dw_o = dhr.reshape(-1, h).T @ o.reshape(-1, Hq * dh)
     return {"dq": dq, "dkv_contrib": dkv_contrib, "dw_o": dw_o, "do": do, "o": o}
 
 
@@ -359,7 +359,7 @@ def rank_attention_bwd_proj(inputs: dict, dims, dq: np.ndarray, dkv_own: np.ndar
     for j in range(D):
         ql, kl = slice(j * hq_s * dh, (j + 1) * hq_s * dh), slice(j * hkv_s * dh, (j + 1) * hkv_s * dh)
         g = np.concatenate([dq[:, :, ql], dk_own[:, :, kl], dv_own[:, :, kl]], axis=2)   # [B][T][nqkv_s]
-        dw_qkv[j] = np.einsum("btn,bth->nh", g, x)
+        dw_qkv[j] = g.reshape(-1, g.shape[2]).T @ x.reshape(-1, h)
     dx_attn = dq @ w["w_q"] + dk_own @ w["w_k"] + dv_own @ w["w_v"]
     return {"dw_qkv": dw_qkv, "dx_attn": dx_attn}
 

@@ -43,11 +43,12 @@ int main() {
             for (int32_t dh : dhs)
               for (int32_t part = -1; part <= 2; ++part) {
                 tsp_dims_t d{b, S, D, D > 1 ? D - 1 : 0, h, 4 * (D > 0 ? D : 1), 2 * (D > 0 ? D : 1), dh, F, part};
-                size_t ws[7];
-                for (int fn = 0; fn <= 6; ++fn) ws[fn] = tsp_workspace_bytes(&d, fn);
+                size_t ws[10];
+                for (int fn = 0; fn <= 9; ++fn) ws[fn] = tsp_workspace_bytes(&d, fn);
                 if (ws[3] > 0) {
                   ++valid;
-                  if (ws[0] != 0 || ws[1] == 0 || ws[2] == 0 || ws[6] == 0 || ws[3] < ws[1]) {
+                  if (ws[0] != 0 || ws[1] == 0 || ws[2] == 0 || ws[6] == 0 || ws[3] < ws[1] || ws[7] == 0 ||
+                      ws[8] == 0 || ws[9] == 0) {
                     std::fprintf(stderr, "inconsistent workspace sizes\n");
                     ++failures;
                   }
@@ -59,6 +60,12 @@ int main() {
                                           f32(P), f32(P), P, ws[6], nullptr),
                          TSP_ERR_HIP);
                   EXPECT(tsp_kv_reorder(&d, u16(P), u16(P), S, nullptr), TSP_ERR_HIP);
+                  EXPECT(tsp_attn_bwd(&d, u16(P), u16(P), u16(P), u16(P), f32(P), f32(P), f32(P), f32(P), P, ws[7],
+                                      nullptr),
+                         TSP_ERR_HIP);
+                  EXPECT(tsp_attn_bwd_proj(&d, u16(P), u16(P), f32(P), f32(P), nullptr, f32(P), f32(P), P, ws[8],
+                                           nullptr),
+                         TSP_ERR_HIP);
                 }
               }
   if (valid < 100) {
@@ -93,6 +100,17 @@ int main() {
          TSP_ERR_WORKSPACE);
   EXPECT(tsp_layer_fwd_noalloc(&d, u16(P), u16(P), u16(P), u16(P), u16(P), u16(P), u16(P), nullptr, nullptr),
          TSP_ERR_NULL_POINTER);
+  const size_t w7 = tsp_workspace_bytes(&d, TSP_FN_ATTN_BWD), w8 = tsp_workspace_bytes(&d, TSP_FN_ATTN_BWD_PROJ);
+  EXPECT(tsp_attn_bwd(&d, u16(P), u16(P), u16(P), u16(P), f32(P), f32(P), nullptr, f32(P), P, w7, nullptr),
+         TSP_ERR_NULL_POINTER);
+  EXPECT(tsp_attn_bwd(&d, u16(P), u16(P), u16(P), u16(P), f32(Q), f32(P), f32(P), f32(P), P, w7, nullptr),
+         TSP_ERR_MISALIGNED);
+  EXPECT(tsp_attn_bwd(&d, u16(P), u16(P), u16(P), u16(P), f32(P), f32(P), f32(P), f32(P), P, w7 - 1, nullptr),
+         TSP_ERR_WORKSPACE);
+  EXPECT(tsp_attn_bwd_proj(&d, u16(P), u16(P), f32(P), f32(P), f32(Q), f32(P), f32(P), P, w8, nullptr),
+         TSP_ERR_MISALIGNED);
+  EXPECT(tsp_attn_bwd_proj(&d, u16(P), u16(P), f32(P), f32(P), nullptr, f32(P), f32(P), P, w8 - 1, nullptr),
+         TSP_ERR_WORKSPACE);
   tsp_dims_t big{2, 16384, 8, 3, 4096, 32, 8, 128, 14336, 0};
   EXPECT(tsp_layer_fwd_noalloc(&big, u16(P), u16(P), u16(P), u16(P), u16(P), u16(P), u16(P), f32(P), nullptr),
          TSP_ERR_SCRATCH);

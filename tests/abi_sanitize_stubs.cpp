@@ -48,7 +48,30 @@ hipError_t launch_bwd_dwgu(const Shape&, int, const uint16_t*, const uint16_t*, 
 }
 AttnPlan attn_plan(const Shape&) { return AttnPlan{}; }
 size_t attn_partial_bytes(const Shape& s) { return (size_t)s.M * s.Hq * (s.dh + 2) * 4; }
-hipError_t launch_flash_attn(const Shape&, const uint16_t*, const uint16_t*, uint16_t*, float*, hipStream_t) {
+AttnPlan attn_plan_shape(const Shape&, int) { return AttnPlan{}; }
+hipError_t launch_flash_attn(const Shape&, const uint16_t*, const uint16_t*, uint16_t*, float*, hipStream_t, float*) {
+  return hipSuccess;
+}
+hipError_t launch_copy_bf16(int, const void*, int64_t, int64_t, uint16_t*, int64_t, int64_t, int, int, int,
+                            hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_q_gemm(const Shape&, const uint16_t*, const uint16_t*, uint16_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_attn_bwd_do(const Shape&, const uint16_t*, const uint16_t*, uint16_t*, hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_attn_bwd_dwo(const Shape&, int, const uint16_t*, const uint16_t*, float*, hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_attn_bwd_dx(const Shape&, const uint16_t*, const uint16_t*, const float*, float*, float*,
+                              hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_attn_bwd_dwqkv(const Shape&, int, const uint16_t*, const uint16_t*, float*, hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_attn_bwd_core(const Shape&, const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
+                                const float*, float*, float*, float*, float*, hipStream_t) {
   return hipSuccess;
 }
 }  // namespace tsp
