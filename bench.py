@@ -284,6 +284,80 @@ def mlp_backward_measure(d, wl, prob, steps: int):
             "input": "bf16 rank rows of x; dy float32 ~ N(0, 1); dx_residual = dy"}
 
 
+def attn_backward_measure(d, wl, prob, steps: int):
+    """Times the attention backward of the rank: tsp_attn_bwd (before the K/V
+    gradient reduce-scatter) and tsp_attn_bwd_proj (after it) on the same
+    weights and all-gathered K/V; dh ~ N(0, 1) from the seeded generator.  The
+    reduce-scatter's output is stood in for by the rank's own block of its
+    send buffer (same shape; the timing does not depend on the values).
+    Algorithmic work: twice the forward's attention part (Q/K/V and output
+    projections, causal attention): each projection has an input-gradient
+    and a weight-gradient product, attention four products (dP, dV, dQ, dK)
+    per forward pair.  Executed on top: the recomputed Q projection and
+    forward attention, the scores recomputed in both kernels and dP in the
+    key-major one."""
+    import numpy as np
+    import torch
+
+    import synth
+    from folded_tensor_sequence_amd import binding as B
+
+    T = d.seq // d.degree
+    l2g = prob.l2g[d.rank].cpu().numpy()
+    dh = torch.from_numpy(np.ascontiguousarray(synth.make_grad(d, wl.seed + 1)[:, l2g])).cuda()
+    w = prob.w
+    qd = d.n_q_heads * d.head_dim
+    nqkv = (d.n_q_heads + 2 * d.n_kv_heads) // d.degree * d.head_dim
+    dq = torch.empty((d.batch, T, qd), dtype=torch.float32, device="cuda")
+    send = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_DKV) // 4, dtype=torch.float32, device="cuda")
+    per = send.numel() // d.degree
+    own = send[d.rank * per:(d.rank + 1) * per]
+    dwo = torch.empty((d.degree, d.hidden, qd // d.degree), dtype=torch.float32, device="cuda")
+    dx = torch.empty_like(dh)
+    dwqkv = torch.empty((d.degree, nqkv, d.hidden), dtype=torch.float32, device="cuda")
+    ws1 = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_BWD), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_BWD_PROJ), dtype=torch.uint8, device="cuda")
+    p1 = lambda: B.tsp_attn_bwd(d, prob.x_local, w["w_qkv"], w["w_o"], prob.kv_gathered, dh, dq, send, dwo, ws1)
+    p2 = lambda: B.tsp_attn_bwd_proj(d, prob.x_local, w["w_qkv"], dq, own, dx, dwqkv, ws2, dx_residual=dh)
+    for _ in range(3):
+        p1()
+        p2()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t1 = t2 = 0.0
+    B.tsp_profile_kernel("attn_bwd", steps)
+    for _ in range(steps):
+        ev[0].record(stream)
+        p1()
+        ev[1].record(stream)
+        p2()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t1 += ev[0].elapsed_time(ev[1])
+        t2 += ev[1].elapsed_time(ev[2])
+    n_core, core_ms = B.tsp_profile_result()
+    B.tsp_profile_kernel(None)
+    t1, t2 = t1 / steps, t2 / steps
+    f = layer_flops(d)
+    alg = 2.0 * (f["qkv"] + f["o"] + f["attn"])
+    core_alg = 2.0 * f["attn"]
+    executed = alg + f["qkv"] * d.n_q_heads / (d.n_q_heads + 2 * d.n_kv_heads) + f["attn"] * 2.5
+    ms = t1 + t2
+    del ws1, ws2, send, dq, dwo, dx, dwqkv, dh
+    core = core_ms / max(n_core, 1)
+    return {"ms_per_call": round(ms, 5), "ms_before_reduce_scatter": round(t1, 5),
+            "ms_after_reduce_scatter": round(t2, 5), "calls": steps,
+            "gflop_algorithmic": round(alg / 1e9, 2), "gflop_executed": round(executed / 1e9, 2),
+            "tflops": round(alg / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(alg / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "core_kernels": {"avg_ms": round(core, 5), "launches": n_core,
+                             "gflop_algorithmic": round(core_alg / 1e9, 2),
+                             "tflops": round(core_alg / (core * 1e-3) / 1e12, 2),
+                             "what": "Delta, dQ (+ piece sums) and dK/dV kernels; algorithmic = the four "
+                                     "gradient products of the causal pairs"},
+            "input": "bf16 rank rows of x; dh float32 ~ N(0, 1); dx_residual = dh"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +495,7 @@ def main():
                                  "frac": round(re_bytes / re_s / 1e9 / PEAK_HBM_GBS, 4)}
     del nat
     out["mlp_ring_bwd"] = mlp_backward_measure(d, wl, prob, max(3, args.steps // 2))
+    out["attn_bwd"] = attn_backward_measure(d, wl, prob, max(3, args.steps // 2))
     # HBM byte counters were recorded for the zigzag runs only
     out["roofline"]["traffic"] = recorded_traffic(wl.name, dominant) if d.partition == 0 else None
     if args.copy_calibration:

@@ -380,7 +380,7 @@ def reset_tuning():
 
 def tsp_profile_kernel(kernel, max_launches: int = 1):
     """Arm live HIP-event timing of the next launches of one kernel ('qkv', 'reorder',
-    'attn', 'oproj', 'gateup', 'down'; None disarms)."""
+    'attn', 'oproj', 'gateup', 'down', 'attn_bwd'; None disarms)."""
     kid = 0 if kernel is None else KERNELS[kernel]
     _check(load().tsp_profile_kernel(kid, int(max_launches)))
 

@@ -355,8 +355,11 @@ __global__ void attn_bwd_dq_merge_kernel(AttnBwdArgs a) {
 // keys), P and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS.  The
 // block's keys' K/V gradient contributions go to the send buffer of the
 // keys' owner ranks (zeros for keys no query of the rank sees).
+// One work group per CU: the wave keeps its keys' K and V rows, both
+// accumulators and the two halves' X and dP in registers (about 420 VGPRs at
+// head_dim 128); measured faster than two groups per CU with spills.
 template <int DH>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   constexpr int NWV = 4, BQ = 64, KROW = DH * 2, TILE = BQ * KROW;
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;  // Q | dO | L | Delta
   constexpr int KRPI = 1024 / KROW, TI = BQ / KRPI, QW = 2 * TI / NWV;
@@ -449,20 +452,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
       const unsigned char* sd = sq + TILE;
       const float* sl = reinterpret_cast<const float*>(sq + 2 * TILE);
       const float* sdl = sl + BQ;
+      // X and dP of both 32-query halves together: four independent
+      // accumulation chains keep the matrix cores busy
+      f32x16 xacc[2], dpacc[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 xacc, dpacc;
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          xacc[e] = 0.0f;
-          dpacc[e] = 0.0f;
+          xacc[qb][e] = 0.0f;
+          dpacc[qb][e] = 0.0f;
         }
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
           const int off = (qb * 32 + lrow) * KROW + (((2 * ks + lgrp) ^ fl) << 4);
-          xacc = mfma_f16(*reinterpret_cast<const u32x4*>(sq + off), kf[ks], xacc);
-          dpacc = mfma_f16(*reinterpret_cast<const u32x4*>(sd + off), vf[ks], dpacc);
+          xacc[qb] = mfma_f16(*reinterpret_cast<const u32x4*>(sq + off), kf[ks], xacc[qb]);
+          dpacc[qb] = mfma_f16(*reinterpret_cast<const u32x4*>(sd + off), vf[ks], dpacc[qb]);
         }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           // registers 8 st .. 8 st + 7 (rows 32 qb + 8 j + 4 lgrp + (0..3),
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int v = 4 * j + u;
-              p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(xacc[v], sc, -lv[u]));
+              p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(xacc[qb][v], sc, -lv[u]));
               if (masked) {
                 // a select, not a branch: rows past T and keys after the
                 // query's position get probability 0
@@ -486,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
                 const bool keep = (t < s.T) & (kpos <= local_pos(s, t));
                 p[u] = keep ? p[u] : 0.0f;
               }
-              d[u] = p[u] * (dpacc[v] - dv[u]);
+              d[u] = p[u] * (dpacc[qb][v] - dv[u]);
             }
             pf[2 * jj] = pack_f16x2(p[0], p[1]);
             pf[2 * jj + 1] = pack_f16x2(p[2], p[3]);
@@ -501,7 +510,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
             dkacc[db] = mfma_f16(tr_read(qr + tro[db][0], qr + tro[db][1]), dsf, dkacc[db]);
           }
         }
-      }
     }
     wait_loads();
     barrier_nofence();
