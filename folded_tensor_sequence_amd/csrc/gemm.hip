@@ -1274,7 +1274,7 @@ hipError_t launch_bwd_dwd(const Shape& s, int m_pad, const uint16_t* dyT, const 
   a.seg_len = m_pad;
   a.out = dw_down;
   a.shard_w = s.F_s;
-  return launch_cfg<false, false, EPI_DWD>(a, 0, 1, st);
+  return launch_cfg<false, false, EPI_DWD>(a, 3, 1, st);  // 256x256: short contraction over the tokens
 }
 
 hipError_t launch_bwd_dwgu(const Shape& s, int m_pad, const uint16_t* dguT, const uint16_t* xT, float* dw_gate,
@@ -1290,7 +1290,7 @@ hipError_t launch_bwd_dwgu(const Shape& s, int m_pad, const uint16_t* dguT, cons
   a.seg_len = m_pad;
   a.out = dw_gate;
   a.out2 = dw_up;
-  return launch_cfg<false, false, EPI_DWGU>(a, 0, 1, st);
+  return launch_cfg<false, false, EPI_DWGU>(a, 3, 1, st);  // 256x256: short contraction over the tokens
 }
 
 // ---- backward of the attention (projections) --------------------------------
@@ -1311,7 +1311,8 @@ hipError_t launch_q_gemm(const Shape& s, const uint16_t* x, const uint16_t* w_q,
   a.q = q;
   a.kv = nullptr;
   a.src_rank = s.r;
-  return launch_single<false, false, EPI_QKV>(a, -1, -1, 1, st);
+  // 128x128 tiles: N = Hq dh alone gives few 256-row tiles (88 at the 8K layer)
+  return launch_cfg<false, false, EPI_QKV>(a, 5, 1, st);
 }
 
 // dO = dh16 WoT^T stored f16 [M][Hq*dh]; WoT [Hq*dh][h] bf16.
@@ -1329,7 +1330,7 @@ hipError_t launch_attn_bwd_do(const Shape& s, const uint16_t* dh16, const uint16
   a.out = nullptr;
   a.out16 = dout;
   a.resid = nullptr;
-  return launch_cfg<false, false, EPI_RESID_F32>(a, 0, 1, st);
+  return launch_cfg<false, false, EPI_RESID_F32>(a, 5, 1, st);  // as launch_q_gemm
 }
 
 // dW_O [D][h][Hq/D dh] = dhT oT^T (both [.][m_pad] bf16).
@@ -1346,7 +1347,7 @@ hipError_t launch_attn_bwd_dwo(const Shape& s, int m_pad, const uint16_t* dhT, c
   a.seg_len = m_pad;
   a.out = dw_o;
   a.shard_w = s.Hq_s * s.dh;
-  return launch_cfg<false, false, EPI_DWD>(a, 0, 1, st);
+  return launch_cfg<false, false, EPI_DWD>(a, 3, 1, st);  // 256x256: short contraction over the tokens
 }
 
 // dx = dx_resid + sum over the shards (ring order) of G_j WqkvT_j^T, G [M][D
@@ -1387,7 +1388,8 @@ hipError_t launch_attn_bwd_dwqkv(const Shape& s, int m_pad, const uint16_t* gT, 
   a.seg_len = m_pad;
   a.out = dw_qkv;
   a.resid = nullptr;
-  return launch_cfg<false, false, EPI_RESID_F32>(a, 0, 1, st);
+  // short contraction (the tokens): 256x256 tiles, fewer operand bytes per product
+  return launch_cfg<false, false, EPI_RESID_F32>(a, 3, 1, st);
 }
 
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n4) {
