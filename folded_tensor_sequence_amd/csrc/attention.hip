@@ -60,10 +60,12 @@ struct AttnArgs {
   const uint16_t* q;     // f16 [B][Hq][T][dh]
   const uint16_t* kv;    // f16 all-gathered K/V [D shard][D src][K|V][B][T][Hkv/D * dh]
   uint16_t* o;           // f16 [B][T][Hq*dh]
-  float* part_o;         // [pieces][B*Hq][rb][dh] unnormalised outputs of split blocks
+  float* part_o;         // f16 [pieces][B*Hq][rb][dh] outputs of split blocks, each piece's
+                         // normalised by its own sum (float-sized slots, half used)
   float* part_ml;        // [pieces][B*Hq][2][rb] (scaled max, sum)
   float* lse;            // optional [B][Hq][T]: log2 of each row's softmax normaliser
                          // (scaled scores), so that p = 2^(s * scale_log2 - lse)
+  MergeTab mtab;         // the split blocks, for the merge
   Shape s;
   float scale_log2;      // log2(e) / sqrt(dh)
   int32_t rb;            // rows per block: 32 per wave (128 or 256)
@@ -440,14 +442,20 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
     } else {
       const int64_t pidx = (int64_t)(piece_base + slot) * per_bh + bh;
       const int r = t_lane - g.t0;
-      float* po = a.part_o + (pidx * RBR + r) * DH;
+      // the piece's output normalised by its own sum (|.| <= max |v|: f16
+      // holds it whatever the piece's length); the merge weights it back.  A
+      // row whose keys in this piece are all masked has sum 0 and weight 0:
+      // it stores zeros (not 0 / 0)
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (pidx * RBR + r) * DH;
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = db * 32 + 8 * q4 + 4 * lgrp;
-          f32x4 v{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
-          *reinterpret_cast<f32x4*>(po + d) = v;
+          u32x2 pk{pack_f16x2(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv),
+                   pack_f16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(po + d) = pk;
         }
       if (lgrp == 0) {
         a.part_ml[(pidx * 2 + 0) * RBR + r] = m_run;
@@ -458,43 +466,67 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
 }
 
 // Combines the pieces of every split block, in piece order:
-// O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p, m = max_p m_p.
-// One thread per (row, 4 head-dim columns).  A split block holds
-// B Hq rb DH / 4 items, a multiple of the 256-thread work group, so the
-// block is located from the work group's first item: that search is the same
-// for every lane (scalar), and only the item within the block is per lane.
+// O = sum_p w_p Ô_p / sum_p w_p, w_p = 2^(m_p - m) l_p, m = max_p m_p, with
+// Ô_p = O_p / l_p the piece's normalised output.  One thread per (row, 4
+// head-dim columns).  A split block holds B Hq rb DH / 4 items, a multiple of
+// the 256-thread work group, so the block is located from the work group's
+// first item (the same for every lane), through the host's table of split
+// blocks.
 template <int DH>
 __global__ void attn_merge_kernel(AttnArgs a) {
   const Shape& s = a.s;
   const int per_bh = s.B * s.Hq;
   constexpr int cols = DH / 4;
-  // locate the split block this work group belongs to
-  const PlanKey plan{s.c, s.D, s.r, s.part, a.rb, a.nrb, a.kt_max, a.pair};
-  const MergePos mp = merge_block_of(plan, (long long)per_bh * a.rb * cols, (long long)blockIdx.x * blockDim.x);
-  if (mp.bi < 0) return;
-  const BlockGeo& g = mp.g;
-  const int64_t item = mp.item + threadIdx.x;
+  const long long ipb = (long long)per_bh * a.rb * cols;  // items per split block
+  // locate the split block this work group belongs to: from the host's
+  // table, or by walking the plan when the table could not hold it
+  BlockGeo g;
+  int piece_base, npieces;
+  long long item0;
+  if (a.mtab.n >= 0) {
+    const long long first = (long long)blockIdx.x * blockDim.x;
+    const int e = (int)(first / ipb);
+    if (e >= a.mtab.n) return;
+    g = block_rows(s.c, s.D, s.r, s.part, a.rb, a.nrb, a.mtab.bi[e]);
+    piece_base = a.mtab.base[e];
+    npieces = a.mtab.np[e];
+    item0 = first - (long long)e * ipb;
+  } else {
+    const PlanKey plan{s.c, s.D, s.r, s.part, a.rb, a.nrb, a.kt_max, a.pair};
+    const MergePos mp = merge_block_of(plan, ipb, (long long)blockIdx.x * blockDim.x);
+    if (mp.bi < 0) return;
+    g = mp.g;
+    piece_base = mp.piece_base;
+    npieces = mp.npieces;
+    item0 = mp.item;
+  }
+  const int64_t item = item0 + threadIdx.x;
   const int c4 = (int)(item % cols);
   const int r = (int)((item / cols) % a.rb);
   const int bh = (int)(item / (cols * a.rb));
   const int t = g.t0 + r;
   if (t >= g.row_end) return;
   float mmax = -INFINITY;
-  for (int p = 0; p < mp.npieces; ++p) {
-    const int64_t pidx = (int64_t)(mp.piece_base + p) * per_bh + bh;
+  for (int p = 0; p < npieces; ++p) {
+    const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
     mmax = fmaxf(mmax, a.part_ml[(pidx * 2 + 0) * a.rb + r]);
   }
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int p = 0; p < mp.npieces; ++p) {
-    const int64_t pidx = (int64_t)(mp.piece_base + p) * per_bh + bh;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * a.rb + r] - mmax);
-    l += w * a.part_ml[(pidx * 2 + 1) * a.rb + r];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (pidx * a.rb + r) * DH + 4 * c4);
-    acc[0] += w * v[0];
-    acc[1] += w * v[1];
-    acc[2] += w * v[2];
-    acc[3] += w * v[3];
+  for (int p = 0; p < npieces; ++p) {
+    const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
+    // weight of the piece: 2^(m_p - m) l_p, its output stored normalised
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[(pidx * 2 + 0) * a.rb + r] - mmax) *
+                    a.part_ml[(pidx * 2 + 1) * a.rb + r];
+    l += w;
+    const u32x2 v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(a.part_o) +
+                                                    (pidx * a.rb + r) * DH + 4 * c4);
+    const uint32_t v0 = v[0], v1 = v[1];
+    const f16x2 h0 = __builtin_bit_cast(f16x2, v0), h1 = __builtin_bit_cast(f16x2, v1);
+    acc[0] += w * (float)h0[0];
+    acc[1] += w * (float)h0[1];
+    acc[2] += w * (float)h1[0];
+    acc[3] += w * (float)h1[1];
   }
   const float inv = 1.0f / l;
   const int b = bh / s.Hq, qh = bh - b * s.Hq;
@@ -662,6 +694,7 @@ hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* 
   a.nrb = p.nrb;
   a.kt_max = p.kt_max;
   a.pair = p.pair;
+  a.mtab = merge_table(PlanKey{s.c, s.D, s.r, s.part, p.rb, p.nrb, p.kt_max, p.pair});
   // the whole-tile paths address a tile's K and V rows with 31-bit offsets
   // (the largest: the V row of the last key, from the tile's base row)
   const int64_t kvd = (int64_t)s.Hkv_s * s.dh;

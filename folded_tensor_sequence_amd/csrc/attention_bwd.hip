@@ -60,6 +60,7 @@ struct AttnBwdArgs {
   float scale_log2;      // log2(e) / sqrt(dh)
   float scale;           // 1 / sqrt(dh)
   int32_t rb, nrb, kt_max, pair;  // the dQ kernel's work plan
+  MergeTab mtab;                  // its split blocks, for the piece sums
 };
 
 namespace {
@@ -316,25 +317,42 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 
 // Sums the pieces of every split row block, in piece order, into dQ.  One
 // thread per (row, 4 head-dim columns); the block is located as in the
-// forward's merge.
+// forward's merge (the host's table of split blocks).
 template <int DH>
 __global__ void attn_bwd_dq_merge_kernel(AttnBwdArgs a) {
   const Shape& s = a.s;
   const int per_bh = s.B * s.Hq;
   constexpr int cols = DH / 4;
-  const PlanKey plan{s.c, s.D, s.r, s.part, a.rb, a.nrb, a.kt_max, a.pair};
-  const MergePos mp = merge_block_of(plan, (long long)per_bh * a.rb * cols, (long long)blockIdx.x * blockDim.x);
-  if (mp.bi < 0) return;
-  const BlockGeo& g = mp.g;
-  const int64_t item = mp.item + threadIdx.x;
+  const long long ipb = (long long)per_bh * a.rb * cols;
+  BlockGeo g;
+  int piece_base, npieces;
+  long long item0;
+  if (a.mtab.n >= 0) {
+    const long long first = (long long)blockIdx.x * blockDim.x;
+    const int e = (int)(first / ipb);
+    if (e >= a.mtab.n) return;
+    g = block_rows(s.c, s.D, s.r, s.part, a.rb, a.nrb, a.mtab.bi[e]);
+    piece_base = a.mtab.base[e];
+    npieces = a.mtab.np[e];
+    item0 = first - (long long)e * ipb;
+  } else {
+    const PlanKey plan{s.c, s.D, s.r, s.part, a.rb, a.nrb, a.kt_max, a.pair};
+    const MergePos mp = merge_block_of(plan, ipb, (long long)blockIdx.x * blockDim.x);
+    if (mp.bi < 0) return;
+    g = mp.g;
+    piece_base = mp.piece_base;
+    npieces = mp.npieces;
+    item0 = mp.item;
+  }
+  const int64_t item = item0 + threadIdx.x;
   const int c4 = (int)(item % cols);
   const int r = (int)((item / cols) % a.rb);
   const int bh = (int)(item / (cols * a.rb));
   const int t = g.t0 + r;
   if (t >= g.row_end) return;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < mp.npieces; ++p) {
-    const int64_t pidx = (int64_t)(mp.piece_base + p) * per_bh + bh;
+  for (int p = 0; p < npieces; ++p) {
+    const int64_t pidx = (int64_t)(piece_base + p) * per_bh + bh;
     const f32x4 v = *reinterpret_cast<const f32x4*>(a.part + (pidx * a.rb + r) * DH + 4 * c4);
     acc[0] += v[0];
     acc[1] += v[1];
@@ -589,6 +607,7 @@ hipError_t launch_attn_bwd_core(const Shape& s, const uint16_t* q, const uint16_
   a.nrb = p.nrb;
   a.kt_max = p.kt_max;
   a.pair = p.pair;
+  a.mtab = merge_table(PlanKey{s.c, s.D, s.r, s.part, p.rb, p.nrb, p.kt_max, p.pair});
   if (s.dh == 128) return launch_bwd_dh<128>(a, p, st);
   return launch_bwd_dh<64>(a, p, st);
 }

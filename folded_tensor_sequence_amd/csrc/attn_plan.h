@@ -215,6 +215,41 @@ TSP_HD inline MergePos merge_block_of(const PlanKey& k, long long items_per_bloc
   return m;
 }
 
+// The split blocks in workspace slot order, as merge_block_of walks them,
+// for the merge kernels (passed as a kernel argument so that no work group
+// repeats the walk): entry e is block bi[e] with pieces [base[e], base[e] +
+// np[e]).  n = -1 when the plan has more split blocks than the table holds
+// (the merge then walks the plan itself).
+constexpr int kMergeTab = 32;
+struct MergeTab {
+  int n;
+  int bi[kMergeTab], base[kMergeTab], np[kMergeTab];
+};
+
+TSP_HD inline MergeTab merge_table(const PlanKey& k) {
+  MergeTab t;
+  t.n = 0;
+  int base = 0;
+  for (int bi = 0; bi < 2 * k.nrb; ++bi) {
+    const BlockGeo g = block_geo(k.c, k.D, k.r, k.part, k.rbr, k.nrb, k.kt_max, k.pair, bi);
+    const PieceSplit q = piece_split(k, g, bi);
+    for (int which = 0; which < 2; ++which) {
+      const int n = which == 0 ? q.nh : q.nl;
+      if (n <= 1) continue;
+      if (t.n >= kMergeTab) {
+        t.n = -1;
+        return t;
+      }
+      t.bi[t.n] = which == 0 ? bi : 2 * k.nrb - 1 - bi;
+      t.base[t.n] = base;
+      t.np[t.n] = n;
+      ++t.n;
+      base += n;
+    }
+  }
+  return t;
+}
+
 // Whole-plan counts: work units per (sequence, q-head) pair, workspace slots
 // of the split blocks, rows of the split blocks.
 struct PlanCounts {

@@ -112,6 +112,12 @@ static int check(int B, int S, int D, int r, int part, int Hq, int rbr, long lon
   const long long ipb = (long long)per_bh * rbr * 32;
   const long long total = (long long)n.split_rows * per_bh * 32;
   std::vector<int> merged(nb, 0);
+  // the host's table of split blocks: when it holds the plan, entry e is the
+  // block merge_block_of finds for the items of the e-th split block
+  const MergeTab tab = merge_table(k);
+  int split_blocks = 0;
+  for (int bi = 0; bi < nb; ++bi) split_blocks += pieces_of[bi] > 1 ? 1 : 0;
+  if (tab.n >= 0 ? tab.n != split_blocks : split_blocks <= kMergeTab) FAIL("merge table size");
   for (long long item = 0; item < total; item += 256) {
     const MergePos m = merge_block_of(k, ipb, item);
     if (m.bi < 0 || m.bi >= nb || pieces_of[m.bi] < 2) FAIL("merge block");
@@ -119,6 +125,12 @@ static int check(int B, int S, int D, int r, int part, int Hq, int rbr, long lon
     if (m.g.t0 != block_rows(c, D, r, part, rbr, k.nrb, m.bi).t0) FAIL("merge rows");
     if (m.item < 0 || m.item + 256 > ipb) FAIL("merge item");
     if (m.item == 0) ++merged[m.bi];
+    if (tab.n >= 0) {
+      const long long e = item / ipb;
+      if (e >= tab.n || tab.bi[e] != m.bi || tab.base[e] != m.piece_base || tab.np[e] != m.npieces ||
+          item - e * ipb != m.item)
+        FAIL("merge table entry");
+    }
   }
   for (int bi = 0; bi < nb; ++bi)
     if (merged[bi] != (pieces_of[bi] > 1 ? 1 : 0)) FAIL("merge misses a split block");
