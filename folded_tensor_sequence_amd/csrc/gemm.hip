@@ -339,6 +339,63 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
   }
 }
 
+// Epilogues written as whole rows: each 32 x 32 result block of a wave (both
+// weights' blocks for two-weight tiles) goes through the wave's own LDS
+// region (row pitch 36 floats: the writes of 16 rows at one column group hit
+// 16 distinct bank groups) and is read back as 8 rows x 32 columns per
+// instruction, so each store (and epilogue-input load) instruction covers
+// whole runs of a row (128 bytes of float32, 64 of a 16-bit output) instead
+// of 16 bytes of each of 32 rows: large outputs no longer rely on the L2
+// merging partial lines before it evicts them.  LDS operations of one wave
+// complete in order, so a wave reads its own writes without a barrier.
+constexpr int kRowPitch = 36;
+template <int NB>
+constexpr int rows_lds_floats() {
+  return NB * 32 * kRowPitch;
+}
+template <int MB, int NBL, int NB, int EPI>
+__device__ __forceinline__ void store_tile_rows(const GemmArgs& a, const f32x16 (&acc)[NB][NBL][MB], int m_base,
+                                                int n_base, int lane, float* lds, int split) {
+  constexpr int P = kRowPitch;
+  const int lrow = lane & 31, lgrp = lane >> 5;
+  const int rr = lane >> 3, cc = (lane & 7) * 4;
+#pragma unroll
+  for (int y = 0; y < NBL; ++y)
+#pragma unroll
+    for (int z = 0; z < MB; ++z) {
+#pragma unroll
+      for (int x = 0; x < NB; ++x)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v{acc[x][y][z][4 * q4], acc[x][y][z][4 * q4 + 1], acc[x][y][z][4 * q4 + 2],
+                        acc[x][y][z][4 * q4 + 3]};
+          *reinterpret_cast<f32x4*>(lds + (x * 32 + lrow) * P + 8 * q4 + 4 * lgrp) = v;
+        }
+      f32x4 in[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (epilogue_reads<EPI>())
+          in[i] = epilogue_input<EPI>(a, m_base + z * 32 + rr + 8 * i, n_base + y * 32 + cc);
+        else
+          in[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m_base + z * 32 + rr + 8 * i, n = n_base + y * 32 + cc;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lds + (rr + 8 * i) * P + cc);
+        const f32x4 w = *reinterpret_cast<const f32x4*>(lds + ((NB - 1) * 32 + rr + 8 * i) * P + cc);
+        const float vv[4] = {v[0], v[1], v[2], v[3]};
+        const float ww[4] = {w[0], w[1], w[2], w[3]};
+        if constexpr (EPI == EPI_PARTIAL) {
+          if (m < a.M && n < a.N)
+            *reinterpret_cast<f32x4*>(a.partial + ((int64_t)split * a.M + m) * a.N + n) = v;
+        } else {
+          epilogue4<EPI>(a, m, n, vv, ww, in[i]);
+        }
+      }
+    }
+}
+
 template <int BM, int BN, int NB, int WGM, int NW, int BK, int NST, bool SEGFAST, bool F16, bool CONVB, int EPI,
           int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
@@ -591,7 +648,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
   // drain: nothing left to issue
   for (; kt < kt1; ++kt) finish_tile(false);
 
-  store_tile<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lrow, lgrp, split);
+  if constexpr (EPI != EPI_QKV) {
+    static_assert(NW * rows_lds_floats<NB>() * 4 <= NST * STAGE, "row staging fits the operand stages");
+    __syncthreads();  // every wave is done with the operand stages
+    store_tile_rows<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lane,
+                                      reinterpret_cast<float*>(smem) + wave * rows_lds_floats<NB>(), split);
+  } else {
+    store_tile<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lrow, lgrp, split);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -912,7 +976,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
             pair[1][y][z][e] = col0 ? t : own;
           }
     }
-    store_tile<HB, NBL, 2, EPI>(a, pair, m0 + wm * WM + (wn == 0 ? 0 : HB * 32), n0, lrow, lgrp, split);
+    static_assert(NW * rows_lds_floats<2>() * 4 <= 2 * STAGE, "row staging fits in the stages");
+    wait_vmcnt<63>();
+    lds_barrier();                                    // every wave has read its partner's half
+    store_tile_rows<HB, NBL, 2, EPI>(a, pair, m0 + wm * WM + (wn == 0 ? 0 : HB * 32), n0, lane,
+                                     reinterpret_cast<float*>(smem) + wave * rows_lds_floats<2>(), split);
+  } else if constexpr (EPI != EPI_QKV) {
+    static_assert(NW * rows_lds_floats<NB>() * 4 <= 2 * STAGE, "row staging fits in the stages");
+    wait_vmcnt<63>();
+    lds_barrier();                                    // every wave's last operand reads are done
+    store_tile_rows<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lane,
+                                      reinterpret_cast<float*>(smem) + wave * rows_lds_floats<NB>(), split);
   } else {
     store_tile<MB, NBL, NB, EPI>(a, acc, m0 + wm * WM, n0 + wn * WN, lrow, lgrp, split);
   }
