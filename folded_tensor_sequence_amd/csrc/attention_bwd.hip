@@ -151,7 +151,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int QW = 2 * TI / NWV;   // K and V instructions per wave
   constexpr int RBR = 32 * NWV;
   constexpr int NDB = DH / 32, NKS = DH / 16;
-  __shared__ __align__(16) unsigned char smem[2 * STAGE];
+  // the two stages as two arrays, named at compile time (see stage_mem)
+  __shared__ __align__(16) unsigned char smem0[STAGE];
+  __shared__ __align__(16) unsigned char smem1[STAGE];
+  auto stage_mem = [&](auto ST_) __attribute__((always_inline)) -> unsigned char* {
+    if constexpr (decltype(ST_)::value == 0)
+      return smem0;
+    else
+      return smem1;
+  };
 
   const Shape& s = a.s;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -216,8 +224,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     const float lse_q = a.lse[rowix];
     const float delta_q = a.delta[rowix];
 
-    auto issue = [&](int kt, int stage) {
-      unsigned char* sb = smem + stage * STAGE;
+    auto issue = [&](int kt, auto ST_) __attribute__((always_inline)) {
+      unsigned char* sb = stage_mem(ST_);
 #pragma unroll
       for (int i = 0; i < QW; ++i) {
         const int qi = wave + NWV * i;
@@ -236,15 +244,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
       for (int e = 0; e < 16; ++e) dqacc[x][e] = 0.0f;
     const float sc = a.scale_log2;
 
-    if (kt_begin < kt_end) issue(kt_begin, 0);
+    if (kt_begin < kt_end) issue(kt_begin, IC<0>{});
     wait_loads();
     barrier_nofence();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const int stage = (kt - kt_begin) & 1;
-      if (kt + 1 < kt_end) issue(kt + 1, stage ^ 1);
+    // tile kt_begin + j sits in stage j mod 2
+    auto step = [&](int kt, auto ST_) __attribute__((always_inline)) {
+      if (kt + 1 < kt_end) issue(kt + 1, IC<decltype(ST_)::value ^ 1>{});
       const int key0 = kt * BN;
       if (wave_active && key0 <= wave_maxpos) {
-        const unsigned char* sk = smem + stage * STAGE;
+        const unsigned char* sk = stage_mem(ST_);
         const unsigned char* sv = sk + TILE;
         const bool masked = key0 + BN - 1 > wave_minpos;
 #pragma unroll
@@ -292,7 +300,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
       }
       wait_loads();
       barrier_nofence();
+    };
+    int kt = kt_begin;
+    for (; kt + 1 < kt_end; kt += 2) {
+      step(kt, IC<0>{});
+      step(kt + 1, IC<1>{});
     }
+    if (kt < kt_end) step(kt, IC<0>{});
 
     if (!wave_active || !lane_valid) continue;
     const float scl = a.scale;
@@ -382,7 +396,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;  // Q | dO | L | Delta
   constexpr int KRPI = 1024 / KROW, TI = BQ / KRPI, QW = 2 * TI / NWV;
   constexpr int NDB = DH / 32, NKS = DH / 16;
-  __shared__ __align__(16) unsigned char smem[2 * STAGE];
+  // the two stages as two arrays, named at compile time (see stage_mem)
+  __shared__ __align__(16) unsigned char smem0[STAGE];
+  __shared__ __align__(16) unsigned char smem1[STAGE];
+  auto stage_mem = [&](auto ST_) __attribute__((always_inline)) -> unsigned char* {
+    if constexpr (decltype(ST_)::value == 0)
+      return smem0;
+    else
+      return smem1;
+  };
 
   const Shape& s = a.s;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -423,8 +445,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   const int items = t_first < s.T ? (nqt - qt0) * grp : 0;
 
   // stage of item it: tile qt0 + it / grp, q-head G grp + it % grp
-  auto issue = [&](int it, int stage) {
-    unsigned char* sb = smem + stage * STAGE;
+  auto issue = [&](int it, auto ST_) __attribute__((always_inline)) {
+    unsigned char* sb = stage_mem(ST_);
     const int t0 = (qt0 + it / grp) * BQ;
     const int qh = G * grp + it % grp;
 #pragma unroll
@@ -455,18 +477,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
     }
   const float sc = a.scale_log2;
 
-  if (items > 0) issue(0, 0);
+  if (items > 0) issue(0, IC<0>{});
   wait_loads();
   barrier_nofence();
-  for (int it = 0; it < items; ++it) {
-    const int stage = it & 1;
-    if (it + 1 < items) issue(it + 1, stage ^ 1);
+  // item it sits in stage it mod 2
+  auto step = [&](int it, auto ST_) __attribute__((always_inline)) {
+    if (it + 1 < items) issue(it + 1, IC<decltype(ST_)::value ^ 1>{});
     const int t0 = (qt0 + it / grp) * BQ;
     const int t_last = t0 + BQ - 1 < s.T ? t0 + BQ - 1 : s.T - 1;
     // queries of the tile before the wave's first key see none of its keys
     if (local_pos(s, t_last) >= k0w) {
       const bool masked = local_pos(s, t0) < k0w + 31 || t0 + BQ > s.T;
-      const unsigned char* sq = smem + stage * STAGE;
+      const unsigned char* sq = stage_mem(ST_);
       const unsigned char* sd = sq + TILE;
       const float* sl = reinterpret_cast<const float*>(sq + 2 * TILE);
       const float* sdl = sl + BQ;
@@ -531,7 +553,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
     }
     wait_loads();
     barrier_nofence();
+  };
+  int it = 0;
+  for (; it + 1 < items; it += 2) {
+    step(it, IC<0>{});
+    step(it + 1, IC<1>{});
   }
+  if (it < items) step(it, IC<0>{});
 
   if (kpos >= s.S) return;
   // owner rank and local row of the key
