@@ -56,7 +56,7 @@ TSP_FN_DKV = 9
 KERNELS = {"qkv": 1, "reorder": 2, "attn": 3, "oproj": 4, "gateup": 5, "down": 6, "attn_bwd": 7}
 
 TUNE = {"gemm_qkv": 0, "gemm_oproj": 1, "gemm_gateup": 2, "gemm_down": 3, "split_oproj": 4,
-        "split_down": 5, "attn_shape": 6, "attn_pair": 7, "attn_pieces": 8}
+        "split_down": 5, "attn_shape": 6, "attn_pair": 7, "attn_pieces": 8, "bwd_weights": 9}
 
 EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd",
             "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",

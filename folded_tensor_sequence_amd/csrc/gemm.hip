@@ -51,6 +51,13 @@ struct GemmArgs {
   float* out2;
   uint16_t* aux16;
   int32_t shard_w;
+  // K-major B (the staged kernel's BKM mode): element (k, n) of B, k = kk
+  // within K segment j, sits at B0 + j b_seg_step + kk ldbk + col(n) for
+  // kk < b_half and at B1 + j b_seg_step + (kk - b_half) ldbk + col(n)
+  // otherwise, col(n) = (n / b_w) b_shard + n % b_w (column blocks of b_w,
+  // one per weight shard).
+  int64_t ldbk, b_shard;
+  int32_t b_w, b_half;
 };
 
 __device__ __forceinline__ float silu_f32(float z) {
@@ -692,8 +699,24 @@ __device__ __forceinline__ void sched_stage_step(std::integer_sequence<int, I...
   (sched_stage_one<I, NMFMA, NFRAG, CPT, LOADS>(), ...);
 }
 
+// Transposing LDS read of two 4-row groups (rows r and r + 4 of one column
+// per lane): the 8 k-values of a K-major operand fragment.
+typedef short gv4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) gv4i16 lds_gv4i16;
+__device__ __forceinline__ u32x4 tr_read2(const unsigned char* p0, const unsigned char* p1) {
+  const gv4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_gv4i16*)p0);
+  const gv4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_gv4i16*)p1);
+  const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
+  return u32x4{h0[0], h0[1], h1[0], h1[1]};
+}
+
+// BKM: B is K-major (a weight read as stored, for the backward products).
+// Its stage holds the tile's 64 k-rows of BN columns (2 BN bytes each), the
+// 16-byte runs of 8 columns XOR-swizzled by (k % 4) * 4 so that the
+// transposing reads of 4 consecutive k-rows hit 4 different bank windows;
+// a fragment (8 consecutive k of one column) is two transposing reads.
 template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG,
-          bool SPLIT>
+          bool SPLIT, bool BKM = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
   // LDS rows of 64 K-values padded from 128 to 144 bytes: the 16 rows one
   // operand read touches then start in 16 different bank groups, and the
@@ -709,13 +732,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
   constexpr int WM = BM / WGM, WN = SPLIT ? BN : BN / WGN;
   constexpr int MB = WM / 32, NBL = WN / 32;
   static_assert(!SPLIT || MB % 2 == 0, "split pairs halves of the wave rows");
-  constexpr int R = BM + NB * BN;       // LDS rows per stage
-  constexpr int STAGE = R * ROWB;
+  static_assert(!BKM || (NB == 1 && !SPLIT && !CONVB && SEGFAST && (BN == 128 || BN == 256) && EPI != EPI_QKV),
+                "K-major B mode");
+  constexpr int R = BM + NB * BN;       // LDS rows per stage (N-major B)
+  constexpr int STAGE = BKM ? BM * ROWB + BK * 2 * BN : R * ROWB;
   constexpr int RS = 8 * NW;            // rows covered by one chunk round
   constexpr int CPT = R / RS;           // staged 16-byte chunks per thread per tile
   constexpr int CA = BM / RS;           // ... of which rows of A
   constexpr int KS = BK / 16;
-  constexpr int NFRAG = MB + NBW * NBL, NMFMA = MB * NBW * NBL;
+  constexpr int RUNS = BN / 8;          // BKM: 16-byte runs per k-row
+  constexpr int NFRAG = MB + (BKM ? 2 : 1) * NBW * NBL, NMFMA = MB * NBW * NBL;
   static_assert(NW % WGM == 0 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(BM % RS == 0, "chunk rounds must not straddle A and B");
   static_assert(NB == 2 || BN % RS == 0, "a single weight fills whole chunk rounds");
@@ -749,9 +775,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
   // a per-lane cursor already includes the slot), K offset excluded
   const int slot_k = SEGFAST ? cslot * 8 : 0;
   uint32_t goff[CPT];
+  // BKM: each B chunk's k-row in the tile, column offset col(n) and LDS offset
+  int bkrow[BKM ? CPT - CA : 1], blds[BKM ? CPT - CA : 1];
+  int64_t bcol[BKM ? CPT - CA : 1];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int row = crow + RS * i;
+    if constexpr (BKM) {
+      if (i >= CA) {
+        const int c = (i - CA) * (64 * NW) + tid;
+        const int krow = c / RUNS, run = c % RUNS;
+        int n = n0 + run * 8;
+        n = n < a.N ? n : a.N - 8;  // N is a multiple of 8
+        bkrow[i - CA] = krow;
+        bcol[i - CA] = (int64_t)(n / a.b_w) * a.b_shard + n % a.b_w;
+        blds[i - CA] = BM * ROWB + krow * (2 * BN) + ((run ^ ((krow & 3) << 2)) << 4);
+        goff[i] = 0;
+        continue;
+      }
+    }
     if (i < CA) {
       int m = m0 + row;
       m = m < a.M ? m : a.M - 1;
@@ -779,6 +821,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
     cur_kk = k - cur_s * a.seg_len;
   }
   uint32_t ak = 0, bk = 0;
+  int tj = 0, tkk = 0;  // BKM: segment and offset in it of the last tile loaded
   // NSTG register sets of staged chunks: loads run NSTG tiles ahead of the
   // LDS stage they are written to
   static_assert(NSTG == 1 || NSTG == 2, "one or two register sets");
@@ -793,6 +836,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
       }
       ak = (uint32_t)(((int64_t)j * a.a_seg_step + cur_kk) * 2);
       bk = (uint32_t)(((int64_t)j * a.b_seg_step + cur_kk) * 2);
+      tj = j;
+      tkk = cur_kk;
       cur_kk += BK;
       if (cur_kk >= a.seg_len) {
         cur_kk -= a.seg_len;
@@ -807,6 +852,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
     if (i < CA) {
       base = reinterpret_cast<const unsigned char*>(a.A);
       off += ak;
+    } else if constexpr (BKM) {
+      const int kk = tkk + bkrow[i - CA];
+      const bool hi = kk >= a.b_half;
+      base = reinterpret_cast<const unsigned char*>(hi ? a.B1 : a.B0);
+      off = (uint32_t)(((int64_t)tj * a.b_seg_step + (int64_t)(hi ? kk - a.b_half : kk) * a.ldbk + bcol[i - CA]) * 2);
     } else {
       const int first = (RS * i - BM) / BN, last = (RS * i + RS - 1 - BM) / BN;  // compile-time
       int which = first;
@@ -821,7 +871,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
     if constexpr (CONVB) {
       if (i >= CA) v = bf16x8_to_f16x8(v);
     }
-    *reinterpret_cast<u32x4*>(smem + stage * STAGE + lds_w + i * RS * ROWB) = v;
+    const int lo = (BKM && i >= CA) ? blds[BKM ? i - CA : 0] : lds_w + i * RS * ROWB;
+    *reinterpret_cast<u32x4*>(smem + stage * STAGE + lo) = v;
   };
   auto load_tile = [&](u32x4 (&dst)[CPT]) __attribute__((always_inline)) {
     next_offsets();
@@ -840,6 +891,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
         for (int e = 0; e < 16; ++e) acc[x][y][z][e] = 0.0f;
 
   const int lrow = lane & 31, lgrp = lane >> 5;
+  // BKM: byte offsets (within a 16-row K step of the B stage) of the two
+  // transposing reads of column block y: lane (gq = lane / 16, sl = lane %
+  // 16) points at row 8 (gq / 2) + sl / 4 (+ 4) and columns wn WN + 32 y +
+  // 16 (gq % 2) + 4 (sl % 4) .. + 3, and receives column wn WN + 32 y +
+  // lane % 32, rows 8 (lane / 32) + (0..7)
+  int btr[BKM ? NBL : 1][2];
+  if constexpr (BKM) {
+    const int gq = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int y = 0; y < NBL; ++y)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * (gq >> 1) + (sl >> 2) + 4 * h;
+        const int c = wn * WN + 32 * y + 16 * (gq & 1) + 4 * (sl & 3);
+        btr[y][h] = r * (2 * BN) + (((c >> 3) ^ ((r & 3) << 2)) << 4) + (c & 7) * 2;
+      }
+  }
   u32x4 af[2][MB], bf[2][NBW][NBL];
   auto read_frags = [&](int stage, int ks, int buf) __attribute__((always_inline)) {
     const unsigned char* sa = smem + stage * STAGE;
@@ -848,13 +916,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
 #pragma unroll
     for (int z = 0; z < MB; ++z)
       af[buf][z] = *reinterpret_cast<const u32x4*>(sa + (wm * WM + z * 32 + lrow) * ROWB + pch);
+    if constexpr (BKM) {
+      const unsigned char* sk = sb + ks * 16 * (2 * BN);
 #pragma unroll
-    for (int x = 0; x < NBW; ++x)
+      for (int y = 0; y < NBL; ++y) bf[buf][0][y] = tr_read2(sk + btr[y][0], sk + btr[y][1]);
+    } else {
 #pragma unroll
-      for (int y = 0; y < NBL; ++y) {
-        const int brow = SPLIT ? wn * BN + y * 32 : x * BN + wn * WN + y * 32;
-        bf[buf][x][y] = *reinterpret_cast<const u32x4*>(sb + (brow + lrow) * ROWB + pch);
-      }
+      for (int x = 0; x < NBW; ++x)
+#pragma unroll
+        for (int y = 0; y < NBL; ++y) {
+          const int brow = SPLIT ? wn * BN + y * 32 : x * BN + wn * WN + y * 32;
+          bf[buf][x][y] = *reinterpret_cast<const u32x4*>(sb + (brow + lrow) * ROWB + pch);
+        }
+    }
   };
   auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -1060,13 +1134,14 @@ static bool staged_fits(const GemmArgs& a) {
   return a_end < ((int64_t)1 << 32) - 64 && b_end < ((int64_t)1 << 32) - 64 && a.K % 64 == 0;
 }
 
-template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG, bool SPLIT>
+template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG, bool SPLIT,
+          bool BKM = false>
 static hipError_t launch_staged_seg(GemmArgs a, int nsplit, hipStream_t st) {
   const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
   if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BF16X) {
     if (nsplit > 1 && a.partial != nullptr) {
       a.nsplit = nsplit;
-      hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI_PARTIAL, NSTG, SPLIT>),
+      hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI_PARTIAL, NSTG, SPLIT, BKM>),
                          dim3(mt * nt * nsplit), dim3(64 * NW), 0, st, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1077,7 +1152,7 @@ static hipError_t launch_staged_seg(GemmArgs a, int nsplit, hipStream_t st) {
     }
   }
   a.nsplit = 1;
-  hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI, NSTG, SPLIT>), dim3(mt * nt),
+  hipLaunchKernelGGL((gemm_staged_kernel<BM, BN, NB, WGM, NW, SEGFAST, F16, CONVB, EPI, NSTG, SPLIT, BKM>), dim3(mt * nt),
                      dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
@@ -1090,6 +1165,27 @@ static hipError_t launch_staged(const GemmArgs& a, int nsplit, hipStream_t st) {
   if (a.seg_len % 64 == 0)
     return launch_staged_seg<BM, BN, NB, WGM, NW, true, F16, CONVB, EPI, NSTG, SPLIT>(a, nsplit, st);
   return launch_staged_seg<BM, BN, NB, WGM, NW, false, F16, CONVB, EPI, NSTG, SPLIT>(a, nsplit, st);
+}
+
+// K-major B (BKM): bf16 operands, segments whole multiples of 64, N and the
+// column blocks multiples of 8, every operand within 32-bit byte offsets of
+// its base.  hipErrorInvalidValue (nothing launched) otherwise.
+static bool bkm_fits(const GemmArgs& a) {
+  if (a.K % 64 != 0 || a.seg_len % 64 != 0 || a.N % 8 != 0 || a.b_w % 8 != 0 || a.b_half <= 0 ||
+      a.b_half > a.seg_len)
+    return false;
+  const int64_t lim = ((int64_t)1 << 32) - 64;
+  const int64_t a_end = ((int64_t)(a.M - 1) * a.lda + (int64_t)(a.nseg - 1) * a.a_seg_step + a.seg_len) * 2;
+  const int64_t col_end = (int64_t)((a.N - 1) / a.b_w) * a.b_shard + a.b_w;
+  const int64_t rows = a.b_half > a.seg_len - a.b_half ? a.b_half : a.seg_len - a.b_half;
+  const int64_t b_end = ((int64_t)(a.nseg - 1) * a.b_seg_step + (rows - 1) * a.ldbk + col_end) * 2;
+  return a_end < lim && b_end < lim;
+}
+
+template <int BM, int BN, int WGM, int NW, int EPI>
+static hipError_t launch_staged_bkm(const GemmArgs& a, int nsplit, hipStream_t st) {
+  if (!bkm_fits(a)) return hipErrorInvalidValue;
+  return launch_staged_seg<BM, BN, 1, WGM, NW, true, false, false, EPI, 1, false, true>(a, nsplit, st);
 }
 
 // Overrides set through tsp_set_tuning (for tests and tuning): a GEMM
@@ -1464,6 +1560,110 @@ hipError_t launch_attn_bwd_dwqkv(const Shape& s, int m_pad, const uint16_t* gT, 
   a.resid = nullptr;
   // short contraction (the tokens): 256x256 tiles, fewer operand bytes per product
   return launch_cfg<false, false, EPI_RESID_F32>(a, 3, 1, st);
+}
+
+// --------------------------------------------------------------------------
+// Backward products with the weight read as stored (K-major B: the staged
+// kernel's BKM mode), no transposed copy:
+//   KMAJ_DA      dA  = dy16 W_down      W_down [D][h][F/D]: K = h, a column
+//                                       block of F/D per shard
+//   KMAJ_DX_MLP  dx  = dx_resid + sum over the shards (ring order) of
+//                      dG_j W_gate,j + dU_j W_up,j   (K segment j = the
+//                      2 F/D columns [dG_j | dU_j] of dGU; its first F/D
+//                      rows from W_gate [F][h], the rest from W_up)
+//   KMAJ_DO      dO  = dh16 W_O         W_O [D][h][Hq/D dh]: K = h
+//   KMAJ_DX_ATTN dx  = dx_resid + G W_QKV  W_QKV [D nqkv_s][h], K segments
+//                      of nqkv_s in ring order
+// --------------------------------------------------------------------------
+static GemmArgs kmajor_args(const Shape& s, int use) {
+  GemmArgs a = base_args(s);
+  a.M = s.M;
+  switch (use) {
+    case KMAJ_DA:
+      a.lda = s.h;
+      a.N = s.F;
+      a.K = a.seg_len = a.b_half = s.h;
+      a.ldbk = a.b_w = s.F_s;
+      a.b_shard = (int64_t)s.h * s.F_s;
+      break;
+    case KMAJ_DX_MLP:
+      a.lda = 2 * (int64_t)s.F;
+      a.a_seg_step = 2 * s.F_s;
+      a.N = s.h;
+      a.K = 2 * s.F;
+      a.seg_len = 2 * s.F_s;
+      a.b_half = s.F_s;
+      a.nseg = s.D;
+      a.ring_rank = s.r;
+      a.ldbk = a.b_w = s.h;
+      a.b_seg_step = (int64_t)s.F_s * s.h;
+      break;
+    case KMAJ_DO:
+      a.lda = s.h;
+      a.N = s.Hq * s.dh;
+      a.K = a.seg_len = a.b_half = s.h;
+      a.ldbk = a.b_w = s.Hq_s * s.dh;
+      a.b_shard = (int64_t)s.h * s.Hq_s * s.dh;
+      break;
+    default:  // KMAJ_DX_ATTN
+      a.lda = (int64_t)s.D * s.nqkv_s;
+      a.a_seg_step = s.nqkv_s;
+      a.N = s.h;
+      a.K = s.D * s.nqkv_s;
+      a.seg_len = a.b_half = s.nqkv_s;
+      a.nseg = s.D;
+      a.ring_rank = s.r;
+      a.ldbk = a.b_w = s.h;
+      a.b_seg_step = (int64_t)s.nqkv_s * s.h;
+      break;
+  }
+  return a;
+}
+
+bool kmajor_ok(const Shape& s, int use) { return bkm_fits(kmajor_args(s, use)); }
+
+hipError_t launch_bwd_da_kmajor(const Shape& s, const uint16_t* dy16, const uint16_t* w_down, float* da,
+                                hipStream_t st) {
+  GemmArgs a = kmajor_args(s, KMAJ_DA);
+  a.A = dy16;
+  a.B0 = a.B1 = w_down;
+  a.out = da;
+  a.resid = nullptr;
+  return launch_staged_bkm<256, 128, 4, 8, EPI_RESID_F32>(a, 1, st);
+}
+
+hipError_t launch_bwd_dx_kmajor(const Shape& s, const uint16_t* dgu, const uint16_t* w_g, const uint16_t* w_u,
+                                const float* dx_resid, float* dx, float* partial, hipStream_t st) {
+  GemmArgs a = kmajor_args(s, KMAJ_DX_MLP);
+  a.A = dgu;
+  a.B0 = w_g;
+  a.B1 = w_u;
+  a.out = dx;
+  a.resid = dx_resid;
+  a.partial = partial;
+  return launch_staged_bkm<256, 128, 4, 8, EPI_RESID_F32>(a, partial != nullptr ? gemm_split_plan(s) : 1, st);
+}
+
+hipError_t launch_attn_bwd_do_kmajor(const Shape& s, const uint16_t* dh16, const uint16_t* w_o, uint16_t* dout,
+                                     hipStream_t st) {
+  GemmArgs a = kmajor_args(s, KMAJ_DO);
+  a.A = dh16;
+  a.B0 = a.B1 = w_o;
+  a.out = nullptr;
+  a.out16 = dout;
+  a.resid = nullptr;
+  return launch_staged_bkm<128, 128, 2, 8, EPI_RESID_F32>(a, 1, st);
+}
+
+hipError_t launch_attn_bwd_dx_kmajor(const Shape& s, const uint16_t* g16, const uint16_t* w_qkv,
+                                     const float* dx_resid, float* dx, float* partial, hipStream_t st) {
+  GemmArgs a = kmajor_args(s, KMAJ_DX_ATTN);
+  a.A = g16;
+  a.B0 = a.B1 = w_qkv;
+  a.out = dx;
+  a.resid = dx_resid;
+  a.partial = partial;
+  return launch_staged_bkm<256, 128, 4, 8, EPI_RESID_F32>(a, partial != nullptr ? gemm_split_plan(s) : 1, st);
 }
 
 __global__ void f32_to_f16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y, int64_t n4) {

@@ -119,6 +119,22 @@ hipError_t launch_attn_bwd_dx(const Shape& s, const uint16_t* g16, const uint16_
                               float* dx, float* partial, hipStream_t st);
 hipError_t launch_attn_bwd_dwqkv(const Shape& s, int m_pad, const uint16_t* gT, const uint16_t* xT, float* dw_qkv,
                                  hipStream_t st);
+// The same backward products with the weight read as stored (K-major, no
+// transposed copy): dA = dy16 W_down, dx = dx_resid + ring sum of dG_j
+// W_gate,j + dU_j W_up,j, dO = dh16 W_O, dx = dx_resid + G W_QKV (ring
+// order).  kmajor_ok(s, use) tells whether the variant applies to the shape
+// (K segments whole multiples of 64, operands within 32-bit offsets); the
+// launchers return hipErrorInvalidValue, launching nothing, when it does not.
+enum { KMAJ_DA = 0, KMAJ_DX_MLP = 1, KMAJ_DO = 2, KMAJ_DX_ATTN = 3 };
+bool kmajor_ok(const Shape& s, int use);
+hipError_t launch_bwd_da_kmajor(const Shape& s, const uint16_t* dy16, const uint16_t* w_down, float* da,
+                                hipStream_t st);
+hipError_t launch_bwd_dx_kmajor(const Shape& s, const uint16_t* dgu, const uint16_t* w_g, const uint16_t* w_u,
+                                const float* dx_resid, float* dx, float* partial, hipStream_t st);
+hipError_t launch_attn_bwd_do_kmajor(const Shape& s, const uint16_t* dh16, const uint16_t* w_o, uint16_t* dout,
+                                     hipStream_t st);
+hipError_t launch_attn_bwd_dx_kmajor(const Shape& s, const uint16_t* g16, const uint16_t* w_qkv,
+                                     const float* dx_resid, float* dx, float* partial, hipStream_t st);
 // out[b][r][c] = bf16(in[b][r][c]) (bit copy for a bf16 input), r < R, c < C
 // (C a multiple of 8, rows 16-byte aligned).
 hipError_t launch_copy_bf16(int tin, const void* in, int64_t ld_in, int64_t in_bstride, uint16_t* out,

@@ -98,7 +98,7 @@ int opt_ptr(const void* p, const char* name) {
 }
 
 // Process-wide kernel-choice overrides (tsp_set_tuning); -1 = default.
-std::atomic<int> g_tune[TSP_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
+std::atomic<int> g_tune[TSP_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 
 constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -126,34 +126,6 @@ size_t bytes_partial(const tsp::Shape& s) {
 // Backward of the MLP ring: M rows padded to 64 on the transposed copies.
 int mpad(const tsp::Shape& s) { return (s.M + 63) / 64 * 64; }
 
-struct MlpBwdWs {
-  uint16_t *x16, *xT, *dy16, *dyT, *wdT, *wguT, *act, *dgu, *actT, *dguT;
-  float *da, *partial;
-};
-
-// [x16 | xT | dy16 | dyT | wdT | wguT | da | act | dgu | actT | dguT | split-K partials]
-size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullptr) {
-  const size_t M = s.M, h = s.h, F = s.F, Mp = mpad(s);
-  const size_t sizes[] = {M * h * 2, h * Mp * 2, M * h * 2, h * Mp * 2, F * h * 2, h * 2 * F * 2,
-                          M * F * 4, M * F * 2, M * 2 * F * 2, F * Mp * 2, 2 * F * Mp * 2};
-  void** slots[] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  if (w != nullptr) {
-    void** ptrs[] = {(void**)&w->x16, (void**)&w->xT, (void**)&w->dy16, (void**)&w->dyT, (void**)&w->wdT,
-                     (void**)&w->wguT, (void**)&w->da, (void**)&w->act, (void**)&w->dgu, (void**)&w->actT,
-                     (void**)&w->dguT};
-    for (int i = 0; i < 11; ++i) slots[i] = ptrs[i];
-  }
-  size_t off = 0;
-  for (int i = 0; i < 11; ++i) {
-    if (slots[i] != nullptr) *slots[i] = base + off;
-    off += (sizes[i] + 255) / 256 * 256;
-  }
-  const int p = tsp::gemm_split_plan(s);
-  const size_t part = p > 1 ? (size_t)p * M * h * 4 : 0;
-  if (w != nullptr) w->partial = part > 0 ? reinterpret_cast<float*>(base + off) : nullptr;
-  return off + (part + 255) / 256 * 256;
-}
-
 // Sequential 256-byte aligned pieces of a workspace (base may be null to
 // only add up the size).
 struct Carve {
@@ -167,8 +139,41 @@ struct Carve {
   }
 };
 
+// The backward products that take a weight as their second operand read it
+// as stored (K-major) unless TSP_TUNE_BWD_WEIGHTS asks for transposed copies
+// or the shape does not suit the K-major kernel; only then does the
+// workspace hold the copies.
+bool kmajor(const tsp::Shape& s, int use) { return tsp::tune_get(TSP_TUNE_BWD_WEIGHTS) != 1 && tsp::kmajor_ok(s, use); }
+
+struct MlpBwdWs {
+  uint16_t *x16, *xT, *dy16, *dyT, *wdT, *wguT, *act, *dgu, *actT, *dguT;
+  float *da, *partial;
+};
+
+// [x16 | xT | dy16 | dyT | (wdT) | (wguT) | da | act | dgu | actT | dguT | split-K partials]
+size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullptr) {
+  MlpBwdWs tmp;
+  MlpBwdWs& x = w != nullptr ? *w : tmp;
+  const size_t M = s.M, h = s.h, F = s.F, Mp = mpad(s);
+  Carve c{base};
+  x.x16 = c.take<uint16_t>(M * h * 2);
+  x.xT = c.take<uint16_t>(h * Mp * 2);
+  x.dy16 = c.take<uint16_t>(M * h * 2);
+  x.dyT = c.take<uint16_t>(h * Mp * 2);
+  x.wdT = kmajor(s, tsp::KMAJ_DA) ? nullptr : c.take<uint16_t>(F * h * 2);
+  x.wguT = kmajor(s, tsp::KMAJ_DX_MLP) ? nullptr : c.take<uint16_t>(h * 2 * F * 2);
+  x.da = c.take<float>(M * F * 4);
+  x.act = c.take<uint16_t>(M * F * 2);
+  x.dgu = c.take<uint16_t>(M * 2 * F * 2);
+  x.actT = c.take<uint16_t>(F * Mp * 2);
+  x.dguT = c.take<uint16_t>(2 * F * Mp * 2);
+  const int p = tsp::gemm_split_plan(s);
+  x.partial = p > 1 ? c.take<float>((size_t)p * M * h * 4) : nullptr;
+  return c.off;
+}
+
 // Backward of the attention, part 1:
-// [q | Wq | o | lse | delta | dh16 | dh^T | Wo^T | dO | O^T | attention pieces]
+// [q | Wq | o | lse | delta | dh16 | dh^T | (Wo^T) | dO | O^T | attention pieces]
 struct AttnBwdWs {
   uint16_t *q, *wq, *o, *dh16, *dhT, *woT, *dout, *oT;
   float *lse, *delta, *partial;
@@ -185,7 +190,7 @@ size_t ws_attn_bwd(const tsp::Shape& s, AttnBwdWs* w = nullptr, char* base = nul
   x.delta = c.take<float>(rows * 4);
   x.dh16 = c.take<uint16_t>(M * h * 2);
   x.dhT = c.take<uint16_t>(h * Mp * 2);
-  x.woT = c.take<uint16_t>(qd * h * 2);
+  x.woT = kmajor(s, tsp::KMAJ_DO) ? nullptr : c.take<uint16_t>(qd * h * 2);
   x.dout = c.take<uint16_t>(M * qd * 2);
   x.oT = c.take<uint16_t>(qd * Mp * 2);
   const size_t part = tsp::attn_partial_bytes(s);
@@ -193,7 +198,7 @@ size_t ws_attn_bwd(const tsp::Shape& s, AttnBwdWs* w = nullptr, char* base = nul
   return c.off;
 }
 
-// Part 2: [G | G^T | Wqkv^T | x^T | split-K partials]
+// Part 2: [G | G^T | (Wqkv^T) | x^T | split-K partials]
 struct AttnBwdProjWs {
   uint16_t *g16, *gT, *wqkvT, *xT;
   float* partial;
@@ -205,7 +210,7 @@ size_t ws_attn_bwd_proj(const tsp::Shape& s, AttnBwdProjWs* w = nullptr, char* b
   Carve c{base};
   x.g16 = c.take<uint16_t>(M * Nall * 2);
   x.gT = c.take<uint16_t>(Nall * Mp * 2);
-  x.wqkvT = c.take<uint16_t>(h * Nall * 2);
+  x.wqkvT = kmajor(s, tsp::KMAJ_DX_ATTN) ? nullptr : c.take<uint16_t>(h * Nall * 2);
   x.xT = c.take<uint16_t>(h * Mp * 2);
   const int p = tsp::gemm_split_plan(s);
   x.partial = p > 1 ? c.take<float>((size_t)p * M * h * 4) : nullptr;
@@ -571,21 +576,32 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
   TSP_LAUNCH(tsp::launch_f32_to_bf16(dy, w.dy16, (int64_t)s.M * h, stream), "mlp bwd: dy to bf16");
   TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_F32, dy, h, 0, w.dyT, Mp, 0, s.M, h, Mp, 1, stream),
              "mlp bwd: dy^T");
-  // Wd_j [h][Fs] -> WdT rows j Fs .. : [Fs][h]
-  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_down, Fs, (int64_t)h * Fs, w.wdT, h, (int64_t)Fs * h, h, Fs,
-                                        h, s.D, stream),
-             "mlp bwd: Wd^T");
-  // Wg_j, Wu_j [Fs][h] -> WguT [h][D][2][Fs]
-  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_gate, h, (int64_t)Fs * h, w.wguT, 2 * (int64_t)F,
-                                        2 * (int64_t)Fs, Fs, h, Fs, s.D, stream),
-             "mlp bwd: Wg^T");
-  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_up, h, (int64_t)Fs * h, w.wguT + Fs, 2 * (int64_t)F,
-                                        2 * (int64_t)Fs, Fs, h, Fs, s.D, stream),
-             "mlp bwd: Wu^T");
-  TSP_LAUNCH(tsp::launch_bwd_da(s, w.dy16, w.wdT, w.da, stream), "mlp bwd: dA");
+  // dA = dy W_down and dx = sum dG_j W_gate,j + dU_j W_up,j read the weights
+  // as stored; the workspace holds transposed copies (wdT, wguT) only where
+  // the K-major products do not apply
+  if (w.wdT == nullptr) {
+    TSP_LAUNCH(tsp::launch_bwd_da_kmajor(s, w.dy16, w_down, w.da, stream), "mlp bwd: dA");
+  } else {
+    // Wd_j [h][Fs] -> WdT rows j Fs .. : [Fs][h]
+    TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_down, Fs, (int64_t)h * Fs, w.wdT, h, (int64_t)Fs * h, h,
+                                          Fs, h, s.D, stream),
+               "mlp bwd: Wd^T");
+    TSP_LAUNCH(tsp::launch_bwd_da(s, w.dy16, w.wdT, w.da, stream), "mlp bwd: dA");
+  }
   TSP_LAUNCH(tsp::launch_bwd_gu(s, xg, x_dtype == TSP_BF16, w_gate, w_up, w.da, w.act, w.dgu, stream),
              "mlp bwd: gate/up recompute");
-  TSP_LAUNCH(tsp::launch_bwd_dx(s, w.dgu, w.wguT, dx_residual, dx, w.partial, stream), "mlp bwd: dx");
+  if (w.wguT == nullptr) {
+    TSP_LAUNCH(tsp::launch_bwd_dx_kmajor(s, w.dgu, w_gate, w_up, dx_residual, dx, w.partial, stream), "mlp bwd: dx");
+  } else {
+    // Wg_j, Wu_j [Fs][h] -> WguT [h][D][2][Fs]
+    TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_gate, h, (int64_t)Fs * h, w.wguT, 2 * (int64_t)F,
+                                          2 * (int64_t)Fs, Fs, h, Fs, s.D, stream),
+               "mlp bwd: Wg^T");
+    TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_up, h, (int64_t)Fs * h, w.wguT + Fs, 2 * (int64_t)F,
+                                          2 * (int64_t)Fs, Fs, h, Fs, s.D, stream),
+               "mlp bwd: Wu^T");
+    TSP_LAUNCH(tsp::launch_bwd_dx(s, w.dgu, w.wguT, dx_residual, dx, w.partial, stream), "mlp bwd: dx");
+  }
   TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w.act, F, 0, w.actT, Mp, 0, s.M, F, Mp, 1, stream),
              "mlp bwd: a^T");
   TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w.dgu, 2 * (int64_t)F, 0, w.dguT, Mp, 0, s.M, 2 * F, Mp, 1,
@@ -623,12 +639,17 @@ int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t
              "attn bwd: W_Q rows");
   TSP_LAUNCH(tsp::launch_q_gemm(s, x_local, w.wq, w.q, stream), "attn bwd: Q");
   TSP_LAUNCH(tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, stream, w.lse), "attn bwd: attention");
-  // dO = dh W_O (W_O_j [h][qs] -> WoT rows j qs ..: [qs][h])
+  // dO = dh W_O: W_O read as stored, or through the copy WoT (W_O_j
+  // [h][qs] -> WoT rows j qs ..: [qs][h]) where the workspace holds one
   TSP_LAUNCH(tsp::launch_f32_to_bf16(dh, w.dh16, (int64_t)s.M * h, stream), "attn bwd: dh to bf16");
-  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_o, qs, (int64_t)h * qs, w.woT, h, (int64_t)qs * h, h, qs,
-                                        h, s.D, stream),
-             "attn bwd: W_O^T");
-  TSP_LAUNCH(tsp::launch_attn_bwd_do(s, w.dh16, w.woT, w.dout, stream), "attn bwd: dO");
+  if (w.woT == nullptr) {
+    TSP_LAUNCH(tsp::launch_attn_bwd_do_kmajor(s, w.dh16, w_o, w.dout, stream), "attn bwd: dO");
+  } else {
+    TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_o, qs, (int64_t)h * qs, w.woT, h, (int64_t)qs * h, h, qs,
+                                          h, s.D, stream),
+               "attn bwd: W_O^T");
+    TSP_LAUNCH(tsp::launch_attn_bwd_do(s, w.dh16, w.woT, w.dout, stream), "attn bwd: dO");
+  }
   {
     const int slot = prof_open(TSP_K_ATTN_BWD, stream);
     hipError_t e = tsp::launch_attn_bwd_core(s, w.q, kv_gathered, w.o, w.dout, w.lse, w.delta, dq, dkv_send,
@@ -676,12 +697,19 @@ int tsp_attn_bwd_proj(const tsp_dims_t* dims, const uint16_t* x_local, const uin
              "attn bwd proj: G (dV)");
   TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w.g16, nall, 0, w.gT, Mp, 0, s.M, (int)nall, Mp, 1, stream),
              "attn bwd proj: G^T");
-  TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_qkv, h, 0, w.wqkvT, nall, 0, (int)nall, h, (int)nall, 1,
-                                        stream),
-             "attn bwd proj: W_QKV^T");
   TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, x_local, h, 0, w.xT, Mp, 0, s.M, h, Mp, 1, stream),
              "attn bwd proj: x^T");
-  TSP_LAUNCH(tsp::launch_attn_bwd_dx(s, w.g16, w.wqkvT, dx_residual, dx, w.partial, stream), "attn bwd proj: dx");
+  // dx = dx_resid + G W_QKV: W_QKV read as stored, or through its transposed
+  // copy where the workspace holds one
+  if (w.wqkvT == nullptr) {
+    TSP_LAUNCH(tsp::launch_attn_bwd_dx_kmajor(s, w.g16, w_qkv, dx_residual, dx, w.partial, stream),
+               "attn bwd proj: dx");
+  } else {
+    TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_qkv, h, 0, w.wqkvT, nall, 0, (int)nall, h, (int)nall, 1,
+                                          stream),
+               "attn bwd proj: W_QKV^T");
+    TSP_LAUNCH(tsp::launch_attn_bwd_dx(s, w.g16, w.wqkvT, dx_residual, dx, w.partial, stream), "attn bwd proj: dx");
+  }
   TSP_LAUNCH(tsp::launch_attn_bwd_dwqkv(s, Mp, w.gT, w.xT, dw_qkv, stream), "attn bwd proj: dW_QKV");
   return TSP_OK;
 }

@@ -372,7 +372,11 @@ int tsp_profile_result(int32_t* launches, float* total_ms);
  *   TSP_TUNE_SPLIT_*   split-K factor 1..4 of the output / down projection
  *   TSP_TUNE_ATTN_SHAPE  4: 4 waves x 2 K/V stages, 8: 8 waves x 3 stages
  *   TSP_TUNE_ATTN_PAIR   0 or 1: pair the two halves' row blocks or not
- *   TSP_TUNE_ATTN_PIECES target number of attention work units (> 0) */
+ *   TSP_TUNE_ATTN_PIECES target number of attention work units (> 0)
+ *   TSP_TUNE_BWD_WEIGHTS 1: the backward calls multiply by transposed copies
+ *                        of the weights (held in their workspace) instead of
+ *                        reading the weights as stored; the workspace size
+ *                        (tsp_workspace_bytes) depends on this knob */
 typedef enum {
   TSP_TUNE_GEMM_QKV = 0,
   TSP_TUNE_GEMM_OPROJ = 1,
@@ -383,7 +387,8 @@ typedef enum {
   TSP_TUNE_ATTN_SHAPE = 6,
   TSP_TUNE_ATTN_PAIR = 7,
   TSP_TUNE_ATTN_PIECES = 8,
-  TSP_TUNE_COUNT = 9
+  TSP_TUNE_BWD_WEIGHTS = 9,
+  TSP_TUNE_COUNT = 10
 } tsp_tune_knob;
 
 int tsp_set_tuning(int32_t knob, int32_t value);

@@ -46,6 +46,21 @@ hipError_t launch_bwd_dwd(const Shape&, int, const uint16_t*, const uint16_t*, f
 hipError_t launch_bwd_dwgu(const Shape&, int, const uint16_t*, const uint16_t*, float*, float*, hipStream_t) {
   return hipSuccess;
 }
+bool kmajor_ok(const Shape& s, int use) { return use != KMAJ_DX_MLP || s.F_s % 32 == 0; }
+hipError_t launch_bwd_da_kmajor(const Shape&, const uint16_t*, const uint16_t*, float*, hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_bwd_dx_kmajor(const Shape&, const uint16_t*, const uint16_t*, const uint16_t*, const float*, float*,
+                                float*, hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_attn_bwd_do_kmajor(const Shape&, const uint16_t*, const uint16_t*, uint16_t*, hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_attn_bwd_dx_kmajor(const Shape&, const uint16_t*, const uint16_t*, const float*, float*, float*,
+                                     hipStream_t) {
+  return hipSuccess;
+}
 AttnPlan attn_plan(const Shape&) { return AttnPlan{}; }
 size_t attn_partial_bytes(const Shape& s) { return (size_t)s.M * s.Hq * (s.dh + 2) * 4; }
 AttnPlan attn_plan_shape(const Shape&, int) { return AttnPlan{}; }

@@ -382,3 +382,45 @@ def test_attn_bwd_buffer_sizes(lib, name):
     for fn in (B.TSP_FN_ATTN_BWD, B.TSP_FN_ATTN_BWD_PROJ):
         n = lib.tsp_workspace_bytes(ctypes.byref(s), fn)
         assert n > 0 and n % 256 == 0
+
+
+def _up256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("name", ["llama7b_s8k_d8", "tiny_d2"])
+def test_bwd_weight_copies_in_workspace(lib, name):
+    # The backward calls read W_down, W_gate/W_up, W_O and W_QKV as stored;
+    # TSP_TUNE_BWD_WEIGHTS = 1 switches to transposed copies, which the
+    # workspaces then hold: exactly one extra weight-sized piece per copy.
+    d = synth.WORKLOADS[name].dims
+    s = B.dims_struct(d)
+    h, F, qd = d.hidden, d.ffn, d.n_q_heads * d.head_dim
+    nall = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim
+    fns = (B.TSP_FN_MLP_BWD, B.TSP_FN_ATTN_BWD, B.TSP_FN_ATTN_BWD_PROJ)
+    assert (F // d.degree) % 32 == 0  # the K-major dx applies to both shapes
+    base = [lib.tsp_workspace_bytes(ctypes.byref(s), fn) for fn in fns]
+    try:
+        assert lib.tsp_set_tuning(B.TUNE["bwd_weights"], 1) == B.TSP_OK
+        copies = [lib.tsp_workspace_bytes(ctypes.byref(s), fn) for fn in fns]
+    finally:
+        lib.tsp_set_tuning(B.TUNE["bwd_weights"], -1)
+    assert copies[0] - base[0] == _up256(F * h * 2) + _up256(2 * F * h * 2)
+    assert copies[1] - base[1] == _up256(qd * h * 2)
+    assert copies[2] - base[2] == _up256(nall * h * 2)
+    assert [lib.tsp_workspace_bytes(ctypes.byref(s), fn) for fn in fns] == base
+
+
+def test_bwd_dx_copies_when_shard_width_is_not_a_multiple_of_32(lib):
+    # F/D = 176: the K-major dx of the MLP backward does not apply (its K
+    # segments of 2 F/D are not whole multiples of 64), so the workspace
+    # holds the transposed W_gate / W_up copy whatever the knob says
+    d = synth.Dims(1, 256, 4, 3, 192, 8, 4, 64, 704, 0)
+    s = B.dims_struct(d)
+    base = lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_MLP_BWD)
+    try:
+        assert lib.tsp_set_tuning(B.TUNE["bwd_weights"], 1) == B.TSP_OK
+        copies = lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_MLP_BWD)
+    finally:
+        lib.tsp_set_tuning(B.TUNE["bwd_weights"], -1)
+    assert copies - base == _up256(704 * 192 * 2)

@@ -21,7 +21,7 @@ from folded_tensor_sequence_amd.harness import pack_weights
 from oracle import tsp_backward as bwd
 from oracle import tsp_oracle as orc
 
-from gpu_util import MAX_ABS, REL_FROB, SWEEP, dims_of, errors, inputs_for
+from gpu_util import MAX_ABS, REL_FROB, SWEEP, dims_of, errors, inputs_for, tuning
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +155,36 @@ def test_attn_bwd_tiny_layer_and_determinism():
     dq2, send2, dwo2 = R.bwd(d.rank, dh_rows)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(send, send2) and torch.equal(dwo, dwo2)
+
+
+# dO = dh W_O and dx = G W_QKV read the weights as stored (K-major
+# products); TSP_TUNE_BWD_WEIGHTS = 1 multiplies by transposed copies held in
+# the workspaces.  Same K order, so the outputs agree bit for bit.
+@pytest.mark.parametrize("name", ["gqa4_dh128_d4_r2", "c24_generic_reorder"])
+def test_attn_bwd_weight_copies_match_kmajor(name):
+    shape = SWEEP[name][:9] + (0,)
+    d = dims_of(shape)
+    _case(f"attn_bwd {name} weights as stored vs transposed copies {d}")
+    inp = inputs_for(shape, 0.02, 101)
+    R = _Ranks(d, inp)
+    r = d.rank
+    dh_rows = torch.from_numpy(np.ascontiguousarray(synth.make_grad(d, 13)[:, R.l2g[r]])).cuda()
+    own = torch.randn(B.tsp_workspace_bytes(d, B.TSP_FN_DKV) // 4 // d.degree, device="cuda") * 0.05
+    outs = []
+    for knob in (None, 1):
+        with tuning(bwd_weights=knob):
+            n1 = B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_BWD)
+            n2 = B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_BWD_PROJ)
+            R.ws1 = torch.empty(n1, dtype=torch.uint8, device="cuda")
+            R.ws2 = torch.empty(n2, dtype=torch.uint8, device="cuda")
+            dq, send, dwo = R.bwd(r, dh_rows)
+            dx, dwqkv = R.proj(r, dq, own, dh_rows)
+            torch.cuda.synchronize()
+            outs.append((n1, n2, dq, send, dwo, dx, dwqkv))
+    (a1, a2, *a), (b1, b2, *b) = outs
+    assert b1 > a1 and b2 > a2  # the copies live in the workspaces
+    for name_, x, y in zip(("dq", "dkv_send", "dw_o", "dx", "dw_qkv"), a, b):
+        assert torch.equal(x, y), name_
 
 
 @pytest.mark.parametrize("name", ["gqa4_dh128_d4_r2", "mha_d2_r1"])

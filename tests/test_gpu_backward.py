@@ -18,7 +18,7 @@ from folded_tensor_sequence_amd.harness import pack_weights
 from oracle import tsp_backward as bwd
 from oracle import tsp_oracle as orc
 
-from gpu_util import MAX_ABS, REL_FROB, SWEEP, dims_of, errors, inputs_for
+from gpu_util import MAX_ABS, REL_FROB, SWEEP, dims_of, errors, inputs_for, tuning
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,25 @@ def test_mlp_ring_bwd_without_residual_in_place_and_deterministic(name):
     # the weight gradients do not depend on the residual and repeat bit for bit
     for k, v in (("dwg", dwg), ("dwu", dwu), ("dwd", dwd)):
         assert torch.equal(v, keep[k]), k
+
+
+# dA = dy W_down and dx = sum dG_j W_gate,j + dU_j W_up,j read the weights as
+# stored (K-major products); TSP_TUNE_BWD_WEIGHTS = 1 multiplies by
+# transposed copies instead.  Both sum every product in the same K order, so
+# the outputs agree bit for bit (the default path is the one held to the
+# oracle above).  ffn_tail_d4_r3 (F/D = 176) takes the copies for dx either
+# way.
+@pytest.mark.parametrize("name", ["tiny_d2", "gqa8_b2_c96", "ffn_tail_d4_r3", "wide_tiles_dh128"])
+def test_mlp_ring_bwd_weight_copies_match_kmajor(name):
+    d, sigma, seed = _shape(name)
+    _case(f"mlp_ring_bwd {name} weights as stored vs transposed copies")
+    inp = inputs_for(d.astuple(), sigma, seed)
+    gpu, _, _ = _run(d, inp, "bf16")
+    with tuning(bwd_weights=1):
+        gpu_t, ref, _ = _run(d, inp, "bf16")
+    for k in ("dx", "dw_g", "dw_u", "dw_d"):
+        _check(k, gpu_t[k], ref[k])
+        assert np.array_equal(gpu[k], gpu_t[k]), k
 
 
 # Rank 5 of D = 8 (the ring starts at shard 5) and the striped partition.
