@@ -442,8 +442,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
     const int q = units >> 3, rem = units & 7;
     u = xcd * q + (xcd < rem ? xcd : rem) + idx;
   }
+  // tiles in groups of 8 row tiles, row tile fastest inside a group: the
+  // tiles an XCD runs at once share 8 A row blocks and a few B column blocks
+  // in its L2 (the weight-gradient products' operands are far larger than
+  // one L2)
   const int tile = u % ntiles, split = u / ntiles;
-  const int mt = tile % mtiles, nt = tile / mtiles;
+  constexpr int GM = 8;
+  const int ntn = (a.N + BN - 1) / BN;
+  const int group = tile / (GM * ntn), first_m = group * GM;
+  const int gsz = mtiles - first_m < GM ? mtiles - first_m : GM;
+  const int gin = tile - group * (GM * ntn);
+  const int mt = first_m + gin % gsz, nt = gin / gsz;
   const int m0 = mt * BM, n0 = nt * BN;
   const int nk_all = a.K / BK;
   const int per = (nk_all + a.nsplit - 1) / a.nsplit;
