@@ -139,24 +139,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
   constexpr int RBR = 32 * NWV;              // rows per block
   constexpr int NDB = DH / 32;
   constexpr int NKS = DH / 16;
-  // One array per stage of the ring, each stage named at compile time: the
-  // compiler's wait analysis then tells direct loads in flight into one
-  // stage from the transposing V reads of another.  (With one array for the
-  // whole ring it makes every transposing read wait for all loads in flight,
-  // those of the tiles prefetched for later steps included.)
-  static_assert(NST >= 2 && NST <= 3, "two or three stages");
-  __shared__ __align__(16) unsigned char smem0[STAGE];
-  __shared__ __align__(16) unsigned char smem1[STAGE];
-  __shared__ __align__(16) unsigned char smem2[NST > 2 ? STAGE : 16];
-  auto stage_mem = [&](auto ST_) __attribute__((always_inline)) -> unsigned char* {
-    constexpr int st = decltype(ST_)::value;
-    if constexpr (st == 0)
-      return smem0;
-    else if constexpr (st == 1)
-      return smem1;
-    else
-      return smem2;
-  };
+  __shared__ __align__(16) unsigned char smem[NST * STAGE];
 
   const Shape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -248,8 +231,8 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
     }
 
     int kq = (kt_begin * BN) / s.c, kr = kt_begin * BN - kq * s.c;
-    auto issue = [&](int kt, auto ST_) __attribute__((always_inline)) {
-      unsigned char* sb = stage_mem(ST_);
+    auto issue = [&](int kt, int stage) {
+      unsigned char* sb = smem + stage * STAGE;
       const int key0 = kt * BN;
       if constexpr (KM == KM_STRIPE) {
         const int64_t row0 = ((int64_t)jsh * s.D * 2 * s.B + b) * s.T + key0 / s.D;
@@ -404,12 +387,12 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
 
     {
       int issued = 0;
-      static_for<0, NST - 1>([&](auto I) __attribute__((always_inline)) {
-        if (kt_begin + decltype(I)::value < kt_end) {
-          issue(kt_begin + decltype(I)::value, I);
+#pragma unroll
+      for (int i = 0; i < NST - 1; ++i)
+        if (kt_begin + i < kt_end) {
+          issue(kt_begin + i, i);
           ++issued;
         }
-      });
       wait_tile(issued - 1);
       barrier();
     }
@@ -418,10 +401,10 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 && NST == 2 ? 2 : 1) void flash_
     auto step = [&](int kt, auto ST_) __attribute__((always_inline)) {
       constexpr int stage = decltype(ST_)::value;
       constexpr int fill = (stage + NST - 1) % NST;
-      if (kt + NST - 1 < kt_end) issue(kt + NST - 1, IC<fill>{});
+      if (kt + NST - 1 < kt_end) issue(kt + NST - 1, fill);
       const int key0 = kt * BN;
       if (wave_active && key0 <= wave_maxpos) {
-        const unsigned char* sk = stage_mem(ST_);
+        const unsigned char* sk = smem + stage * STAGE;
         f32x16 sacc[2];
         u32x4 pf[2][2];
         s_block(sk, sacc);
