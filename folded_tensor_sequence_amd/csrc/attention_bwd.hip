@@ -477,6 +477,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
     }
   const float sc = a.scale_log2;
 
+  // The lane's key is seen by the local rows [tmin, T): positions grow with
+  // the local row, tmin is the first one whose position reaches the key.
+  const int tmin = first_row_from(s, kpos);
+  const unsigned mspan = (unsigned)(s.T - tmin);
+
   if (items > 0) issue(0, IC<0>{});
   wait_loads();
   barrier_nofence();
@@ -510,6 +515,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
           xacc[qb] = mfma_f16(*reinterpret_cast<const u32x4*>(sq + off), kf[ks], xacc[qb]);
           dpacc[qb] = mfma_f16(*reinterpret_cast<const u32x4*>(sd + off), vf[ks], dpacc[qb]);
         }
+      // masked tiles: scores of rows outside [tmin, T) become -inf (their
+      // probability and dS are then 0), in one block ahead of the
+      // probabilities so that those stay free of branches
+      if (masked) {
+        const int mbase = t0 + 4 * lgrp - tmin;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = qb * 32 + 8 * (v >> 2) + (v & 3);
+            xacc[qb][v] = (unsigned)(mbase + r) < mspan ? xacc[qb][v] : -INFINITY;
+          }
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -528,13 +546,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
             for (int u = 0; u < 4; ++u) {
               const int v = 4 * j + u;
               p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(xacc[qb][v], sc, -lv[u]));
-              if (masked) {
-                // a select, not a branch: rows past T and keys after the
-                // query's position get probability 0
-                const int t = t0 + r0 + u;
-                const bool keep = (t < s.T) & (kpos <= local_pos(s, t));
-                p[u] = keep ? p[u] : 0.0f;
-              }
               d[u] = p[u] * (dpacc[qb][v] - dv[u]);
             }
             pf[2 * jj] = pack_f16x2(p[0], p[1]);
