@@ -269,6 +269,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
             sacc = mfma_f16(*reinterpret_cast<const u32x4*>(sk + off), qf[ks], sacc);
             dpacc = mfma_f16(*reinterpret_cast<const u32x4*>(sv + off), dof[ks], dpacc);
           }
+          // causal edge: scores of keys after the query's position become
+          // -inf (probability and dS 0), in one block ahead of the
+          // probabilities so that those stay free of branches
+          if (masked) {
+            const int lim = qpos - key0 - 32 * kb - 4 * lgrp;  // keep key offset <= lim
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[v] = 8 * (v >> 2) + (v & 3) <= lim ? sacc[v] : -INFINITY;
+          }
           // dS^T for keys key0 + 32 kb + 8 (v / 4) + 4 lgrp + v % 4
           u32x4 dsf[2];
 #pragma unroll
@@ -279,11 +287,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
               for (int u = 0; u < 2; ++u) {
                 const int v = 8 * st + 2 * w + u;
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], sc, -lse_q));
-                if (masked) {
-                  const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * lgrp + (v & 3);
-                  if (key > qpos) p = 0.0f;
-                }
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], sc, -lse_q));
                 d2[u] = p * (dpacc[v] - delta_q);
               }
               dsf[st][w] = pack_f16x2(d2[0], d2[1]);
