@@ -721,9 +721,10 @@ __device__ __forceinline__ u32x4 tr_read2(const unsigned char* p0, const unsigne
 
 // BKM: B is K-major (a weight read as stored, for the backward products).
 // Its stage holds the tile's 64 k-rows of BN columns (2 BN bytes each), the
-// 16-byte runs of 8 columns XOR-swizzled by (k % 4) * 4 so that the
-// transposing reads of 4 consecutive k-rows hit 4 different bank windows;
-// a fragment (8 consecutive k of one column) is two transposing reads.
+// 16-byte runs of 8 columns of row k rotated by 4 (k % 4) runs so that the
+// transposing reads of 4 consecutive k-rows hit 4 different 64-byte bank
+// windows; a fragment (8 consecutive k of one column) is two transposing
+// reads.
 template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG,
           bool SPLIT, bool BKM = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
@@ -741,7 +742,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
   constexpr int WM = BM / WGM, WN = SPLIT ? BN : BN / WGN;
   constexpr int MB = WM / 32, NBL = WN / 32;
   static_assert(!SPLIT || MB % 2 == 0, "split pairs halves of the wave rows");
-  static_assert(!BKM || (NB == 1 && !SPLIT && !CONVB && SEGFAST && (BN == 128 || BN == 256) && EPI != EPI_QKV),
+  static_assert(!BKM || (NB == 1 && !SPLIT && !CONVB && SEGFAST && (BN == 128 || BN == 192 || BN == 256) &&
+                         EPI != EPI_QKV),
                 "K-major B mode");
   constexpr int R = BM + NB * BN;       // LDS rows per stage (N-major B)
   constexpr int STAGE = BKM ? BM * ROWB + BK * 2 * BN : R * ROWB;
@@ -798,7 +800,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
         n = n < a.N ? n : a.N - 8;  // N is a multiple of 8
         bkrow[i - CA] = krow;
         bcol[i - CA] = (int64_t)(n / a.b_w) * a.b_shard + n % a.b_w;
-        blds[i - CA] = BM * ROWB + krow * (2 * BN) + ((run ^ ((krow & 3) << 2)) << 4);
+        blds[i - CA] = BM * ROWB + krow * (2 * BN) + (((run + 4 * (krow & 3)) % RUNS) << 4);
         goff[i] = 0;
         continue;
       }
@@ -914,7 +916,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
       for (int h = 0; h < 2; ++h) {
         const int r = 8 * (gq >> 1) + (sl >> 2) + 4 * h;
         const int c = wn * WN + 32 * y + 16 * (gq & 1) + 4 * (sl & 3);
-        btr[y][h] = r * (2 * BN) + (((c >> 3) ^ ((r & 3) << 2)) << 4) + (c & 7) * 2;
+        btr[y][h] = r * (2 * BN) + ((((c >> 3) + 4 * (r & 3)) % RUNS) << 4) + (c & 7) * 2;
       }
   }
   u32x4 af[2][MB], bf[2][NBW][NBL];
@@ -1638,7 +1640,8 @@ hipError_t launch_bwd_da_kmajor(const Shape& s, const uint16_t* dy16, const uint
   a.B0 = a.B1 = w_down;
   a.out = da;
   a.resid = nullptr;
-  return launch_staged_bkm<256, 128, 4, 8, EPI_RESID_F32>(a, 1, st);
+  // 256x192 tiles: one round of work groups at the 8K layer (4 x 58 tiles)
+  return launch_staged_bkm<256, 192, 4, 8, EPI_RESID_F32>(a, 1, st);
 }
 
 hipError_t launch_bwd_dx_kmajor(const Shape& s, const uint16_t* dgu, const uint16_t* w_g, const uint16_t* w_u,
