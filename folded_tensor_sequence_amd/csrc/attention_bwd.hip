@@ -382,27 +382,37 @@ __global__ void attn_bwd_dq_merge_kernel(AttnBwdArgs a) {
 }
 
 // ---- dK, dV: key-major -----------------------------------------------------
-// Work group u: key block kb = u / (B Hkv) (128 keys, 32 per wave; lower
-// keys, which more of the rank's queries see, come first) of (sequence,
-// kv-head).  It loops over the tiles of 64 of the rank's local rows from the
-// first row whose position reaches the block's first key (local rows are in
-// increasing position order), and over the q-heads of the kv-head's group;
-// per (tile, q-head) a wave computes X = Q K^T and dP = dO V^T (queries x its
-// keys), P and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS.  The
-// block's keys' K/V gradient contributions go to the send buffer of the
-// keys' owner ranks (zeros for keys no query of the rank sees).
-// One work group per CU: the wave keeps its keys' K and V rows, both
-// accumulators and the two halves' X and dP in registers (about 420 VGPRs at
-// head_dim 128); measured faster than two groups per CU with spills.
+// Work group u: key block kb = u / (B Hkv) (128 keys; lower keys, which more
+// of the rank's queries see, come first) of (sequence, kv-head).  It loops
+// over the tiles of 64 of the rank's local rows from the first row whose
+// position reaches the block's first key (local rows are in increasing
+// position order), and over the q-heads of the kv-head's group.  Eight
+// waves: wave w takes the 32 keys kg = w % 4 of the block and the 32 rows
+// hf = w / 4 of every tile; per (tile, q-head) it computes X = Q K^T and
+// dP = dO V^T (its rows x its keys), P and dS, and accumulates
+// dV^T += dO^T P and dK^T += Q^T dS over its rows.  The block's K and V rows
+// sit in LDS (read once), so a wave holds only its accumulators and two
+// waves share a SIMD: one's exp work runs beside the other's products.  At
+// the end the two waves of a key group add their sums through LDS and the
+// keys' K/V gradient contributions go to the send buffer of the keys' owner
+// ranks (zeros for keys no query of the rank sees).
 template <int DH>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
-  constexpr int NWV = 4, BQ = 64, KROW = DH * 2, TILE = BQ * KROW;
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
+  constexpr int NWV = 8, BQ = 64, KROW = DH * 2, TILE = BQ * KROW;
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;  // Q | dO | L | Delta
   constexpr int KRPI = 1024 / KROW, TI = BQ / KRPI, QW = 2 * TI / NWV;
   constexpr int NDB = DH / 32, NKS = DH / 16;
-  // the two stages as two arrays, named at compile time (see stage_mem)
+  constexpr int KEYS = 128, KV_BYTES = 2 * KEYS * KROW;  // K rows | V rows
+  constexpr int KV_INS = KV_BYTES / 1024 / NWV;          // direct loads per wave
+  static_assert(QW * NWV == 2 * TI && KV_INS * NWV * 1024 == KV_BYTES, "loads split evenly over the waves");
+  // per-lane partial sums of one wave (dV or dK), register-major
+  constexpr int PART = NDB * 16 * 64 * 4;
+  static_assert(4 * PART <= KV_BYTES && 2 * PART <= STAGE, "the pair sums fit in the freed LDS");
+  // the two stages and the K/V rows as three arrays, named at compile time
+  // (see stage_mem)
   __shared__ __align__(16) unsigned char smem0[STAGE];
   __shared__ __align__(16) unsigned char smem1[STAGE];
+  __shared__ __align__(16) unsigned char kvs[KV_BYTES];
   auto stage_mem = [&](auto ST_) __attribute__((always_inline)) -> unsigned char* {
     if constexpr (decltype(ST_)::value == 0)
       return smem0;
@@ -413,26 +423,27 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   const Shape& s = a.s;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 31, lgrp = lane >> 5;
+  const int kg = wave & 3, hf = wave >> 2;
   const int per_bg = s.B * s.Hkv;
   const int kb = blockIdx.x / per_bg, bg = blockIdx.x - kb * per_bg;
   const int b = bg / s.Hkv, G = bg - b * s.Hkv;
   const int jsh = G / s.Hkv_s, hk = G - jsh * s.Hkv_s;
   const int grp = s.Hq / s.Hkv;
   const int kvd = s.Hkv_s * DH;
-  const int k0 = kb * (32 * NWV), k0w = k0 + 32 * wave;
+  const int k0 = kb * KEYS, k0w = k0 + 32 * kg;
   const int kpos = k0w + lrow;
-  const int kp = kpos < s.S ? kpos : s.S - 1;
 
-  // the lane's key: K and V rows as the k-operand of X and dP
-  u32x4 kf[NKS], vf[NKS];
-  {
-    const uint16_t* krow = a.kv + gathered_row(s, jsh, 0, b, kp) * kvd + (int64_t)hk * DH;
-    const uint16_t* vrow = a.kv + gathered_row(s, jsh, 1, b, kp) * kvd + (int64_t)hk * DH;
+  // the block's K and V rows into LDS (rows swizzled as the tiles' rows)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = *reinterpret_cast<const u32x4*>(krow + ks * 16 + lgrp * 8);
-      vf[ks] = *reinterpret_cast<const u32x4*>(vrow + ks * 16 + lgrp * 8);
-    }
+  for (int i = 0; i < KV_INS; ++i) {
+    const int q = wave + NWV * i;
+    const int row = KRPI * q + lane / (KROW / 16);  // 0 .. 2 KEYS - 1: K rows, then V rows
+    const int sel = row >= KEYS ? 1 : 0;
+    const int r = row - sel * KEYS;
+    int key = k0 + r;
+    key = key < s.S ? key : s.S - 1;  // keys past the sequence end are never stored
+    const uint16_t* src = a.kv + gathered_row(s, jsh, sel, b, key) * kvd + (int64_t)hk * DH;
+    attn_load_lds16(src + ((lane % (KROW / 16)) ^ bswz<DH>(r)) * 8, kvs + q * 1024);
   }
 
   int tro[NDB][2];
@@ -480,11 +491,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
       dkacc[x][e] = 0.0f;
     }
   const float sc = a.scale_log2;
-
   // The lane's key is seen by the local rows [tmin, T): positions grow with
   // the local row, tmin is the first one whose position reaches the key.
   const int tmin = first_row_from(s, kpos);
   const unsigned mspan = (unsigned)(s.T - tmin);
+  // the wave's keys' K and V rows (the second operands of X and dP) start
+  // at this offset in the K/V array
+  const int kvrow = (32 * kg + lrow) * KROW;
 
   if (items > 0) issue(0, IC<0>{});
   wait_loads();
@@ -493,78 +506,78 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   auto step = [&](int it, auto ST_) __attribute__((always_inline)) {
     if (it + 1 < items) issue(it + 1, IC<decltype(ST_)::value ^ 1>{});
     const int t0 = (qt0 + it / grp) * BQ;
-    const int t_last = t0 + BQ - 1 < s.T ? t0 + BQ - 1 : s.T - 1;
-    // queries of the tile before the wave's first key see none of its keys
-    if (local_pos(s, t_last) >= k0w) {
-      const bool masked = local_pos(s, t0) < k0w + 31 || t0 + BQ > s.T;
-      const unsigned char* sq = stage_mem(ST_);
+    const int th = t0 + 32 * hf;  // the wave's first row
+    const int t_last = th + 31 < s.T ? th + 31 : s.T - 1;
+    // rows before the wave's first key see none of its keys
+    if (th < s.T && local_pos(s, t_last) >= k0w) {
+      const bool masked = local_pos(s, th) < k0w + 31 || th + 32 > s.T;
+      // re-read the K and V fragments every item instead of keeping them live
+      // across the loop (the compiler would hoist the invariant reads and
+      // hold 16 more fragments): the offset goes through an empty asm
+      int kvo = kvrow;
+      asm volatile("" : "+v"(kvo));
+      const unsigned char* kw = kvs + kvo;
+      const unsigned char* vw = kw + KEYS * KROW;
+      const unsigned char* sq = stage_mem(ST_) + 32 * hf * KROW;
       const unsigned char* sd = sq + TILE;
-      const float* sl = reinterpret_cast<const float*>(sq + 2 * TILE);
+      const float* sl = reinterpret_cast<const float*>(stage_mem(ST_) + 2 * TILE) + 32 * hf;
       const float* sdl = sl + BQ;
-      // X and dP of both 32-query halves together: four independent
-      // accumulation chains keep the matrix cores busy
-      f32x16 xacc[2], dpacc[2];
+      f32x16 xacc, dpacc;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          xacc[qb][e] = 0.0f;
-          dpacc[qb][e] = 0.0f;
-        }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int off = (qb * 32 + lrow) * KROW + (((2 * ks + lgrp) ^ fl) << 4);
-          xacc[qb] = mfma_f16(*reinterpret_cast<const u32x4*>(sq + off), kf[ks], xacc[qb]);
-          dpacc[qb] = mfma_f16(*reinterpret_cast<const u32x4*>(sd + off), vf[ks], dpacc[qb]);
-        }
-      // masked tiles: scores of rows outside [tmin, T) become -inf (their
-      // probability and dS are then 0), in one block ahead of the
-      // probabilities so that those stay free of branches
-      if (masked) {
-        const int mbase = t0 + 4 * lgrp - tmin;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = qb * 32 + 8 * (v >> 2) + (v & 3);
-            xacc[qb][v] = (unsigned)(mbase + r) < mspan ? xacc[qb][v] : -INFINITY;
-          }
+      for (int e = 0; e < 16; ++e) {
+        xacc[e] = 0.0f;
+        dpacc[e] = 0.0f;
       }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int off = (((2 * ks + lgrp) ^ fl) << 4);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kw + off);
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(vw + off);
+        xacc = mfma_f16(*reinterpret_cast<const u32x4*>(sq + lrow * KROW + off), kf, xacc);
+        dpacc = mfma_f16(*reinterpret_cast<const u32x4*>(sd + lrow * KROW + off), vf, dpacc);
+      }
+      // causal edge and rows past T: scores of rows outside [tmin, T) become
+      // -inf (probability and dS 0), in one block ahead of the probabilities
+      // so that those stay free of branches
+      if (masked) {
+        const int mbase = th + 4 * lgrp - tmin;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          // registers 8 st .. 8 st + 7 (rows 32 qb + 8 j + 4 lgrp + (0..3),
-          // j = 2 st, 2 st + 1) form the k-operand of step st
-          u32x4 pf, dsf;
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * st + jj;
-            const int r0 = qb * 32 + 8 * j + 4 * lgrp;
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(sl + r0);
-            const f32x4 dv = *reinterpret_cast<const f32x4*>(sdl + r0);
-            float p[4], d[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int v = 4 * j + u;
-              p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(xacc[qb][v], sc, -lv[u]));
-              d[u] = p[u] * (dpacc[qb][v] - dv[u]);
-            }
-            pf[2 * jj] = pack_f16x2(p[0], p[1]);
-            pf[2 * jj + 1] = pack_f16x2(p[2], p[3]);
-            dsf[2 * jj] = pack_f16x2(d[0], d[1]);
-            dsf[2 * jj + 1] = pack_f16x2(d[2], d[3]);
-          }
-          const unsigned char* dr = sd + (qb * 32 + st * 16) * KROW;
-          const unsigned char* qr = sq + (qb * 32 + st * 16) * KROW;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dvacc[db] = mfma_f16(tr_read(dr + tro[db][0], dr + tro[db][1]), pf, dvacc[db]);
-            dkacc[db] = mfma_f16(tr_read(qr + tro[db][0], qr + tro[db][1]), dsf, dkacc[db]);
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int r = 8 * (v >> 2) + (v & 3);
+          xacc[v] = (unsigned)(mbase + r) < mspan ? xacc[v] : -INFINITY;
         }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        // registers 8 st .. 8 st + 7 (rows 8 j + 4 lgrp + (0..3) of the
+        // wave's 32, j = 2 st, 2 st + 1) form the k-operand of step st
+        u32x4 pf, dsf;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * st + jj;
+          const int r0 = 8 * j + 4 * lgrp;
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(sl + r0);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(sdl + r0);
+          float p[4], d[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int v = 4 * j + u;
+            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(xacc[v], sc, -lv[u]));
+            d[u] = p[u] * (dpacc[v] - dv[u]);
+          }
+          pf[2 * jj] = pack_f16x2(p[0], p[1]);
+          pf[2 * jj + 1] = pack_f16x2(p[2], p[3]);
+          dsf[2 * jj] = pack_f16x2(d[0], d[1]);
+          dsf[2 * jj + 1] = pack_f16x2(d[2], d[3]);
+        }
+        const unsigned char* dr = sd + st * 16 * KROW;
+        const unsigned char* qr = sq + st * 16 * KROW;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dvacc[db] = mfma_f16(tr_read(dr + tro[db][0], dr + tro[db][1]), pf, dvacc[db]);
+          dkacc[db] = mfma_f16(tr_read(qr + tro[db][0], qr + tro[db][1]), dsf, dkacc[db]);
+        }
+      }
     }
     wait_loads();
     barrier_nofence();
@@ -576,7 +589,35 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   }
   if (it < items) step(it, IC<0>{});
 
-  if (kpos >= s.S) return;
+  // the pair's sums: the second-half wave of each key group leaves its dV
+  // partial in the K/V rows' array and its dK partial in a stage (every
+  // wave is past its last LDS read: the loop ends on a barrier, and with no
+  // item the K/V rows were never read), the first-half wave adds them
+  if (items == 0) {
+    wait_loads();  // the K/V rows' loads land before that memory is reused
+    barrier_nofence();
+  }
+  float* pv = reinterpret_cast<float*>(kvs + kg * PART) + lane;
+  float* pk = reinterpret_cast<float*>((kg < 2 ? smem0 : smem1) + (kg & 1) * PART) + lane;
+  if (hf == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pv[(db * 16 + e) * 64] = dvacc[db][e];
+        pk[(db * 16 + e) * 64] = dkacc[db][e];
+      }
+  }
+  wait_loads();
+  barrier_nofence();
+  if (hf == 1 || kpos >= s.S) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dvacc[db][e] += pv[(db * 16 + e) * 64];
+      dkacc[db][e] += pk[(db * 16 + e) * 64];
+    }
   // owner rank and local row of the key
   int g, t;
   if (s.part == 1) {
@@ -623,7 +664,7 @@ static hipError_t launch_bwd_dh(const AttnBwdArgs& a, const AttnPlan& p, hipStre
     if (e != hipSuccess) return e;
   }
   const int nkb = (s.S + 127) / 128;
-  hipLaunchKernelGGL(attn_bwd_dkv_kernel<DH>, dim3((unsigned)((int64_t)nkb * s.B * s.Hkv)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_bwd_dkv_kernel<DH>, dim3((unsigned)((int64_t)nkb * s.B * s.Hkv)), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
