@@ -720,11 +720,19 @@ __device__ __forceinline__ u32x4 tr_read2(const unsigned char* p0, const unsigne
 }
 
 // BKM: B is K-major (a weight read as stored, for the backward products).
-// Its stage holds the tile's 64 k-rows of BN columns (2 BN bytes each), the
-// 16-byte runs of 8 columns of row k rotated by 4 (k % 4) runs so that the
-// transposing reads of 4 consecutive k-rows hit 4 different 64-byte bank
-// windows; a fragment (8 consecutive k of one column) is two transposing
-// reads.
+// Its stage holds the tile's 64 k-rows of BN columns (2 BN bytes each) as
+// 16-byte runs of 8 columns, swizzled so that the transposing reads of 4
+// consecutive k-rows (32 bytes of each) hit 4 different 64-byte bank windows;
+// a fragment (8 consecutive k of one column) is two transposing reads.
+// Physical run of logical run `run` of k-row k: inside each whole group of 16
+// runs, run XOR 4 (k % 4); in the 8-run tail of a 192-column row (384 bytes,
+// so consecutive rows start half a bank cycle apart), run XOR 4 ((k / 2) % 2).
+template <int RUNS>
+__device__ __forceinline__ int bkm_run(int run, int k) {
+  constexpr int FULL = RUNS & ~15;
+  static_assert(RUNS == FULL || RUNS - FULL == 8, "whole 16-run groups and at most an 8-run tail");
+  return run < FULL ? run ^ ((k & 3) << 2) : FULL + ((run - FULL) ^ (((k >> 1) & 1) << 2));
+}
 template <int BM, int BN, int NB, int WGM, int NW, bool SEGFAST, bool F16, bool CONVB, int EPI, int NSTG,
           bool SPLIT, bool BKM = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
@@ -800,7 +808,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
         n = n < a.N ? n : a.N - 8;  // N is a multiple of 8
         bkrow[i - CA] = krow;
         bcol[i - CA] = (int64_t)(n / a.b_w) * a.b_shard + n % a.b_w;
-        blds[i - CA] = BM * ROWB + krow * (2 * BN) + (((run + 4 * (krow & 3)) % RUNS) << 4);
+        blds[i - CA] = BM * ROWB + krow * (2 * BN) + (bkm_run<RUNS>(run, krow) << 4);
         goff[i] = 0;
         continue;
       }
@@ -916,7 +924,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
       for (int h = 0; h < 2; ++h) {
         const int r = 8 * (gq >> 1) + (sl >> 2) + 4 * h;
         const int c = wn * WN + 32 * y + 16 * (gq & 1) + 4 * (sl & 3);
-        btr[y][h] = r * (2 * BN) + ((((c >> 3) + 4 * (r & 3)) % RUNS) << 4) + (c & 7) * 2;
+        btr[y][h] = r * (2 * BN) + (bkm_run<RUNS>(c >> 3, r) << 4) + (c & 7) * 2;
       }
   }
   u32x4 af[2][MB], bf[2][NBW][NBL];
