@@ -1088,26 +1088,50 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
 // Sums the split-K partials in split order and applies the residual epilogue:
 // out = resid + sum_p partial[p]  (resid bf16 when EPI == EPI_RESID_BF16X,
 // float32 when EPI_RESID_F32), plus the f16 copy when out16 != nullptr.
+// A thread takes four consecutive columns of RR rows at a time (rows
+// RR y, RR y + 1, ... then RR (y + gridDim.y), ...) and issues every load of
+// those rows before its first store (the stores may alias the partials as far
+// as the compiler knows, so it would not move later rows' loads above them).
+constexpr int kReduceRows = 4;
 template <int EPI>
 __global__ void gemm_reduce_kernel(GemmArgs a) {
-  // block (x, y): four consecutive columns of rows y, y + gridDim.y, ... per
-  // thread (no division)
+  constexpr int RR = kReduceRows;
   const int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (n >= a.N) return;
   const int64_t plane = (int64_t)a.M * a.N;
-  for (int m = blockIdx.y; m < a.M; m += gridDim.y) {
-    const int64_t off = (int64_t)m * a.N + n;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(a.partial + off);
-    for (int p = 1; p < a.nsplit; ++p) {
-      const f32x4 t = *reinterpret_cast<const f32x4*>(a.partial + p * plane + off);
-      acc[0] += t[0];
-      acc[1] += t[1];
-      acc[2] += t[2];
-      acc[3] += t[3];
+  for (int m0 = blockIdx.y * RR; m0 < a.M; m0 += gridDim.y * RR) {
+    f32x4 acc[RR], in[RR];
+    int64_t off[RR];
+#pragma unroll
+    for (int i = 0; i < RR; ++i) {
+      const int m = m0 + i < a.M ? m0 + i : a.M - 1;  // rows past M: loaded, not stored
+      off[i] = (int64_t)m * a.N + n;
+      acc[i] = *reinterpret_cast<const f32x4*>(a.partial + off[i]);
+      in[i] = epilogue_input<EPI>(a, m0 + i, n);
     }
-    float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    epilogue4<EPI>(a, m, n, v, v, epilogue_input<EPI>(a, m, n));
+    for (int p = 1; p < a.nsplit; ++p) {
+      f32x4 t[RR];
+#pragma unroll
+      for (int i = 0; i < RR; ++i) t[i] = *reinterpret_cast<const f32x4*>(a.partial + p * plane + off[i]);
+#pragma unroll
+      for (int i = 0; i < RR; ++i) {
+        acc[i][0] += t[i][0];
+        acc[i][1] += t[i][1];
+        acc[i][2] += t[i][2];
+        acc[i][3] += t[i][3];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RR; ++i) {
+      float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+      epilogue4<EPI>(a, m0 + i, n, v, v, in[i]);
+    }
   }
+}
+
+static dim3 reduce_grid(const GemmArgs& a) {
+  const int rows = (a.M + kReduceRows - 1) / kReduceRows;
+  return dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
 }
 
 // --------------------------------------------------------------------------
@@ -1125,8 +1149,7 @@ static hipError_t launch_tile_seg(GemmArgs a, int nsplit, hipStream_t st) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((gemm_reduce_kernel<EPI>),
-                         dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535)), dim3(256),
-                         0, st, a);
+                         reduce_grid(a), dim3(256), 0, st, a);
       return hipGetLastError();
     }
   }
@@ -1165,8 +1188,7 @@ static hipError_t launch_staged_seg(GemmArgs a, int nsplit, hipStream_t st) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((gemm_reduce_kernel<EPI>),
-                         dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535)), dim3(256),
-                         0, st, a);
+                         reduce_grid(a), dim3(256), 0, st, a);
       return hipGetLastError();
     }
   }
