@@ -55,10 +55,17 @@ struct GemmArgs {
   // within K segment j, sits at B0 + j b_seg_step + kk ldbk + col(n) for
   // kk < b_half and at B1 + j b_seg_step + (kk - b_half) ldbk + col(n)
   // otherwise, col(n) = (n / b_w) b_shard + n % b_w (column blocks of b_w,
-  // one per weight shard).
+  // one per weight shard).  N-major B with b_w > 0: row n of B is row
+  // (n / b_w) b_shard + n % b_w of the stored matrix (blocks of b_w rows, one
+  // per shard, b_shard rows apart); b_w = 0: row n.
   int64_t ldbk, b_shard;
   int32_t b_w, b_half;
 };
+
+// Stored row of B's row n (N-major B; see GemmArgs::b_w).
+__host__ __device__ inline int64_t b_row(const GemmArgs& a, int n) {
+  return a.b_w > 0 ? (int64_t)(n / a.b_w) * a.b_shard + n % a.b_w : (int64_t)n;
+}
 
 __device__ __forceinline__ float silu_f32(float z) {
   return z / (1.0f + __expf(-z));
@@ -482,7 +489,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void gemm_kernel(GemmArgs a) {
       const int which = brow / BN;
       int n = n0 + brow - which * BN;
       n = n < a.N ? n : a.N - 1;
-      src[i] = ((NB == 2 && which == 1) ? a.B1 : a.B0) + (int64_t)n * a.ldb;
+      src[i] = ((NB == 2 && which == 1) ? a.B1 : a.B0) + b_row(a, n) * a.ldb;
     }
     if constexpr (SEGFAST) src[i] += chunk[i] * 8;
   }
@@ -824,7 +831,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_staged_kernel(GemmArgs a) {
       const int which = brow >= BN ? 1 : 0;
       int n = n0 + brow - which * BN;
       n = n < a.N ? n : a.N - 1;
-      goff[i] = (uint32_t)(((int64_t)n * a.ldb + slot_k) * 2);
+      goff[i] = (uint32_t)((b_row(a, n) * a.ldb + slot_k) * 2);
     }
   }
   const uint32_t lds_w = crow * ROWB + cslot * 16;
@@ -1172,7 +1179,7 @@ static hipError_t launch_tile(GemmArgs a, int nsplit, hipStream_t st) {
 static bool staged_fits(const GemmArgs& a) {
   const int64_t seg_extra = a.seg_len;
   const int64_t a_end = ((int64_t)(a.M - 1) * a.lda + (int64_t)(a.nseg - 1) * a.a_seg_step + seg_extra) * 2;
-  const int64_t b_end = ((int64_t)(a.N - 1) * a.ldb + (int64_t)(a.nseg - 1) * a.b_seg_step + seg_extra) * 2;
+  const int64_t b_end = (b_row(a, a.N - 1) * a.ldb + (int64_t)(a.nseg - 1) * a.b_seg_step + seg_extra) * 2;
   return a_end < ((int64_t)1 << 32) - 64 && b_end < ((int64_t)1 << 32) - 64 && a.K % 64 == 0;
 }
 
@@ -1507,14 +1514,18 @@ hipError_t launch_bwd_dwgu(const Shape& s, int m_pad, const uint16_t* dguT, cons
 // ---- backward of the attention (projections) --------------------------------
 // q = x Wq^T for the rank's tokens, Wq [Hq*dh][h] the Q rows of every shard:
 // the Q/K/V epilogue with every column a Q column (a shard of Hq/D dh).
-hipError_t launch_q_gemm(const Shape& s, const uint16_t* x, const uint16_t* w_q, uint16_t* q, hipStream_t st) {
+hipError_t launch_q_gemm(const Shape& s, const uint16_t* x, const uint16_t* w_qkv, uint16_t* q, hipStream_t st) {
   Shape sq = s;
   sq.nqkv_s = s.Hq_s * s.dh;
   GemmArgs a = base_args(sq);
   a.A = x;
   a.lda = s.h;
-  a.B0 = a.B1 = w_q;
+  // the Q rows of every shard of W_QKV: Hq/D dh rows at the start of each
+  // shard's nqkv_s rows
+  a.B0 = a.B1 = w_qkv;
   a.ldb = s.h;
+  a.b_w = s.Hq_s * s.dh;
+  a.b_shard = s.nqkv_s;
   a.M = s.M;
   a.N = s.Hq * s.dh;
   a.K = s.h;

@@ -106,11 +106,12 @@ hipError_t launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* 
                              float* partial, hipStream_t st, float* lse = nullptr);
 
 // ---- backward of the attention ----------------------------------------------
-// Projections (bf16 matrix cores): q = x Wq^T (Wq [Hq*dh][h], q f16 [B][Hq][T][dh]);
+// Projections (bf16 matrix cores): q = x Wq^T (Wq: the Q rows of every shard of
+// W_QKV [D][nqkv_s][h], read in place; q f16 [B][Hq][T][dh]);
 // dO = dh16 WoT^T (f16 [M][Hq*dh]); dW_O [D][h][Hq/D dh] = dhT oT^T;
 // dx = dx_resid + G WqkvT^T (G [M][D nqkv_s] bf16, ring order over the
 // shards); dW_QKV [D nqkv_s][h] = gT xT^T.
-hipError_t launch_q_gemm(const Shape& s, const uint16_t* x, const uint16_t* w_q, uint16_t* q, hipStream_t st);
+hipError_t launch_q_gemm(const Shape& s, const uint16_t* x, const uint16_t* w_qkv, uint16_t* q, hipStream_t st);
 hipError_t launch_attn_bwd_do(const Shape& s, const uint16_t* dh16, const uint16_t* woT, uint16_t* dout,
                               hipStream_t st);
 hipError_t launch_attn_bwd_dwo(const Shape& s, int m_pad, const uint16_t* dhT, const uint16_t* oT, float* dw_o,

@@ -173,9 +173,9 @@ size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullp
 }
 
 // Backward of the attention, part 1:
-// [q | Wq | o | lse | delta | dh16 | dh^T | (Wo^T) | dO | O^T | attention pieces]
+// [q | o | lse | delta | dh16 | dh^T | (Wo^T) | dO | O^T | attention pieces]
 struct AttnBwdWs {
-  uint16_t *q, *wq, *o, *dh16, *dhT, *woT, *dout, *oT;
+  uint16_t *q, *o, *dh16, *dhT, *woT, *dout, *oT;
   float *lse, *delta, *partial;
 };
 size_t ws_attn_bwd(const tsp::Shape& s, AttnBwdWs* w = nullptr, char* base = nullptr) {
@@ -184,7 +184,6 @@ size_t ws_attn_bwd(const tsp::Shape& s, AttnBwdWs* w = nullptr, char* base = nul
   const size_t M = s.M, h = s.h, qd = (size_t)s.Hq * s.dh, Mp = mpad(s), rows = (size_t)s.B * s.Hq * s.T;
   Carve c{base};
   x.q = c.take<uint16_t>(M * qd * 2);
-  x.wq = c.take<uint16_t>(qd * h * 2);
   x.o = c.take<uint16_t>(M * qd * 2);
   x.lse = c.take<float>(rows * 4);
   x.delta = c.take<float>(rows * 4);
@@ -632,12 +631,9 @@ int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t
   AttnBwdWs w;
   ws_attn_bwd(s, &w, static_cast<char*>(ws));
   const int Mp = mpad(s), h = s.h, qs = s.Hq_s * s.dh;
-  // recomputation: Q rows of every shard, then Q and the attention output
-  // with its row normalisers
-  TSP_LAUNCH(tsp::launch_copy_bf16(tsp::TR_BF16, w_qkv, h, (int64_t)s.nqkv_s * h, w.wq, h, (int64_t)qs * h, qs, h,
-                                   s.D, stream),
-             "attn bwd: W_Q rows");
-  TSP_LAUNCH(tsp::launch_q_gemm(s, x_local, w.wq, w.q, stream), "attn bwd: Q");
+  // recomputation: Q (from the Q rows of every shard of W_QKV, read in
+  // place), then the attention output with its row normalisers
+  TSP_LAUNCH(tsp::launch_q_gemm(s, x_local, static_cast<const uint16_t*>(w_qkv), w.q, stream), "attn bwd: Q");
   TSP_LAUNCH(tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, stream, w.lse), "attn bwd: attention");
   // dO = dh W_O: W_O read as stored, or through the copy WoT (W_O_j
   // [h][qs] -> WoT rows j qs ..: [qs][h]) where the workspace holds one
