@@ -338,6 +338,28 @@ def attn_backward_measure(d, wl, prob, steps: int):
     n_core, core_ms = B.tsp_profile_result()
     B.tsp_profile_kernel(None)
     t1, t2 = t1 / steps, t2 / steps
+    # the same part 1 from the forward's kept Q, O and row normalisers
+    # (tsp_attn_fwd_keep, untimed) instead of recomputing them
+    q_keep = torch.empty(d.batch * T * qd, dtype=torch.int16, device="cuda")
+    o_keep = torch.empty_like(q_keep)
+    lse = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_LSE) // 4, dtype=torch.float32, device="cuda")
+    hout = torch.empty_like(dh)
+    wsk = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_KEEP), dtype=torch.uint8, device="cuda")
+    B.tsp_attn_fwd_keep(d, prob.x_local, w["w_qkv"], w["w_o"], prob.kv_gathered, hout, q_keep, o_keep, lse, wsk)
+    wsb = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_BWD_KEPT), dtype=torch.uint8, device="cuda")
+    p1k = lambda: B.tsp_attn_bwd_kept(d, w["w_o"], prob.kv_gathered, q_keep, o_keep, lse, dh, dq, send, dwo, wsb)
+    for _ in range(3):
+        p1k()
+    torch.cuda.synchronize()
+    t1k = 0.0
+    for _ in range(steps):
+        ev[0].record(stream)
+        p1k()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t1k += ev[0].elapsed_time(ev[1])
+    t1k /= steps
+    del q_keep, o_keep, lse, hout, wsk, wsb
     f = layer_flops(d)
     alg = 2.0 * (f["qkv"] + f["o"] + f["attn"])
     core_alg = 2.0 * f["attn"]
@@ -347,6 +369,10 @@ def attn_backward_measure(d, wl, prob, steps: int):
     core = core_ms / max(n_core, 1)
     return {"ms_per_call": round(ms, 5), "ms_before_reduce_scatter": round(t1, 5),
             "ms_after_reduce_scatter": round(t2, 5), "calls": steps,
+            "kept_forward_activations": {
+                "ms_before_reduce_scatter": round(t1k, 5), "ms_per_call": round(t1k + t2, 5),
+                "what": "tsp_attn_bwd_kept from tsp_attn_fwd_keep's Q, O and row normalisers (no "
+                        "recomputation of Q and of the attention); the same outputs"},
             "gflop_algorithmic": round(alg / 1e9, 2), "gflop_executed": round(executed / 1e9, 2),
             "tflops": round(alg / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(alg / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),

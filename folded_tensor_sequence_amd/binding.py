@@ -52,6 +52,9 @@ TSP_FN_MLP_BWD = 6
 TSP_FN_ATTN_BWD = 7
 TSP_FN_ATTN_BWD_PROJ = 8
 TSP_FN_DKV = 9
+TSP_FN_ATTN_KEEP = 10
+TSP_FN_ATTN_BWD_KEPT = 11
+TSP_FN_LSE = 12
 
 KERNELS = {"qkv": 1, "reorder": 2, "attn": 3, "oproj": 4, "gateup": 5, "down": 6, "attn_bwd": 7}
 
@@ -61,7 +64,8 @@ TUNE = {"gemm_qkv": 0, "gemm_oproj": 1, "gemm_gateup": 2, "gemm_down": 3, "split
 EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd",
             "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",
             "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning", "tsp_layer_fwd_noalloc",
-            "tsp_mlp_ring_bwd", "tsp_attn_bwd", "tsp_attn_bwd_proj")
+            "tsp_mlp_ring_bwd", "tsp_attn_bwd", "tsp_attn_bwd_proj", "tsp_attn_fwd_keep",
+            "tsp_attn_bwd_kept")
 
 # Size of the library's fixed scratch array (TSP_SCRATCH_BYTES in include/tsp.h).
 TSP_SCRATCH_BYTES = 128 * 1024 * 1024
@@ -104,6 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tsp_mlp_ring_bwd": [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_attn_bwd": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_attn_bwd_proj": [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_attn_fwd_keep": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_attn_bwd_kept": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -323,6 +329,39 @@ def tsp_attn_bwd(dims, x_local, w_qkv, w_o, kv_gathered, dh, dq, dkv_send, dw_o,
         ctypes.byref(d), _tensor(x_local, "x_local", "bf16", z.x16), _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv),
         _tensor(w_o, "w_o", "bf16", z.w_o),
         _tensor(kv_gathered, "kv_gathered", "f16", tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+        _tensor(dh, "dh", "f32", z.f32), _tensor(dq, "dq", "f32", z.dq),
+        _tensor(dkv_send, "dkv_send", "f32", tsp_workspace_bytes(dims, TSP_FN_DKV)),
+        _tensor(dw_o, "dw_o", "f32", 2 * z.w_o), wsp, wsn, _s(stream)))
+
+
+def tsp_attn_fwd_keep(dims, x_local, w_qkv, w_o, kv_gathered, out, q_keep, o_keep, lse_keep, ws, residual=None,
+                      stream=None):
+    """tsp_attn_fwd that also hands Q (f16 [B][Hq][T][dh]), the attention output
+    O (f16 [B][T][Hq*dh]) and each row's log2 softmax normaliser (float32
+    [B][Hq][T]) to the caller, for tsp_attn_bwd_kept."""
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    wsp, wsn = _ws(dims, ws, TSP_FN_ATTN_KEEP)
+    _check(load().tsp_attn_fwd_keep(
+        ctypes.byref(d), _tensor(x_local, "x_local", "bf16", z.x16), _tensor(w_qkv, "w_qkv", "bf16", z.w_qkv),
+        _tensor(w_o, "w_o", "bf16", z.w_o),
+        _tensor(kv_gathered, "kv_gathered", "f16", tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+        _tensor(residual, "residual", "f32", z.f32, optional=True), _tensor(out, "out", "f32", z.f32),
+        _tensor(q_keep, "q_keep", "f16", z.q), _tensor(o_keep, "o_keep", "f16", z.q),
+        _tensor(lse_keep, "lse_keep", "f32", tsp_workspace_bytes(dims, TSP_FN_LSE)), wsp, wsn, _s(stream)))
+
+
+def tsp_attn_bwd_kept(dims, w_o, kv_gathered, q_keep, o_keep, lse_keep, dh, dq, dkv_send, dw_o, ws, stream=None):
+    """tsp_attn_bwd from the activations tsp_attn_fwd_keep kept (no
+    recomputation of Q and of the attention); the same outputs."""
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    wsp, wsn = _ws(dims, ws, TSP_FN_ATTN_BWD_KEPT)
+    _check(load().tsp_attn_bwd_kept(
+        ctypes.byref(d), _tensor(w_o, "w_o", "bf16", z.w_o),
+        _tensor(kv_gathered, "kv_gathered", "f16", tsp_workspace_bytes(dims, TSP_FN_KV_GATHERED)),
+        _tensor(q_keep, "q_keep", "f16", z.q), _tensor(o_keep, "o_keep", "f16", z.q),
+        _tensor(lse_keep, "lse_keep", "f32", tsp_workspace_bytes(dims, TSP_FN_LSE)),
         _tensor(dh, "dh", "f32", z.f32), _tensor(dq, "dq", "f32", z.dq),
         _tensor(dkv_send, "dkv_send", "f32", tsp_workspace_bytes(dims, TSP_FN_DKV)),
         _tensor(dw_o, "dw_o", "f32", 2 * z.w_o), wsp, wsn, _s(stream)))

@@ -174,18 +174,20 @@ size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullp
 
 // Backward of the attention, part 1:
 // [q | o | lse | delta | dh16 | dh^T | (Wo^T) | dO | O^T | attention pieces]
+// (kept: the caller holds q, o and lse from tsp_attn_fwd_keep; they are not
+// in the workspace)
 struct AttnBwdWs {
   uint16_t *q, *o, *dh16, *dhT, *woT, *dout, *oT;
   float *lse, *delta, *partial;
 };
-size_t ws_attn_bwd(const tsp::Shape& s, AttnBwdWs* w = nullptr, char* base = nullptr) {
+size_t ws_attn_bwd(const tsp::Shape& s, AttnBwdWs* w = nullptr, char* base = nullptr, bool kept = false) {
   AttnBwdWs tmp;
   AttnBwdWs& x = w != nullptr ? *w : tmp;
   const size_t M = s.M, h = s.h, qd = (size_t)s.Hq * s.dh, Mp = mpad(s), rows = (size_t)s.B * s.Hq * s.T;
   Carve c{base};
-  x.q = c.take<uint16_t>(M * qd * 2);
-  x.o = c.take<uint16_t>(M * qd * 2);
-  x.lse = c.take<float>(rows * 4);
+  x.q = kept ? nullptr : c.take<uint16_t>(M * qd * 2);
+  x.o = kept ? nullptr : c.take<uint16_t>(M * qd * 2);
+  x.lse = kept ? nullptr : c.take<float>(rows * 4);
   x.delta = c.take<float>(rows * 4);
   x.dh16 = c.take<uint16_t>(M * h * 2);
   x.dhT = c.take<uint16_t>(h * Mp * 2);
@@ -233,6 +235,9 @@ struct MlpWs {
 //   layer      [q | o | h32 | h16 | act | split-K partials]
 // (attention reads K/V straight from the all-gathered buffer)
 size_t ws_attn(const tsp::Shape& s) { return up(bytes_q(s)) + up(bytes_o(s)) + up(bytes_partial(s)); }
+// tsp_attn_fwd_keep: q and o go to the caller's buffers; at least one
+// aligned piece so that the size is never 0
+size_t ws_attn_keep(const tsp::Shape& s) { return bytes_partial(s) > 0 ? up(bytes_partial(s)) : kAlign; }
 size_t ws_mlp(const tsp::Shape& s) { return up(bytes_h16(s)) + up(bytes_act(s)) + up(bytes_partial(s)); }
 size_t ws_layer(const tsp::Shape& s) {
   return up(bytes_q(s)) + up(bytes_o(s)) + up(bytes_h32(s)) + up(bytes_h16(s)) + up(bytes_act(s)) +
@@ -346,12 +351,13 @@ int check_device(const char* where) {
 
 // out = resid + attention branch; resid is x_resid (bf16, the layer's own
 // input), else resid_f32, else nothing.
+// lse (optional): each row's log2 softmax normaliser, for the backward.
 int run_attention(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* w_qkv,
                   const uint16_t* w_o, uint16_t* kv_gathered, const uint16_t* x_resid, const float* resid_f32,
-                  float* out, uint16_t* out16, const AttnWs& w, hipStream_t st) {
+                  float* out, uint16_t* out16, const AttnWs& w, hipStream_t st, float* lse = nullptr) {
   TSP_KLAUNCH(TSP_K_QKV, st, tsp::launch_qkv_gemm(s, s.r, x_local, w_qkv, w.q, kv_gathered, st),
               "qkv projection");
-  TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, st),
+  TSP_KLAUNCH(TSP_K_ATTN, st, tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, st, lse),
               "flash attention");
   TSP_KLAUNCH(TSP_K_OPROJ, st,
               tsp::launch_oproj_gemm(s, w.o, w_o, x_resid, resid_f32, out, out16, w.partial, st),
@@ -440,6 +446,9 @@ size_t tsp_workspace_bytes(const tsp_dims_t* dims, int32_t fn) {
     case TSP_FN_ATTN_BWD: return ws_attn_bwd(s);
     case TSP_FN_ATTN_BWD_PROJ: return ws_attn_bwd_proj(s);
     case TSP_FN_DKV: return bytes_dkv(s);
+    case TSP_FN_ATTN_KEEP: return ws_attn_keep(s);
+    case TSP_FN_ATTN_BWD_KEPT: return ws_attn_bwd(s, nullptr, nullptr, true);
+    case TSP_FN_LSE: return (size_t)s.B * s.Hq * s.T * 4;
     default: fail(TSP_ERR_INVALID_ARG, "unknown workspace selector %d", fn); return 0;
   }
 }
@@ -611,30 +620,13 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
   return TSP_OK;
 }
 
-int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const uint16_t* w_o,
-                 const uint16_t* kv_gathered, const float* dh, float* dq, float* dkv_send, float* dw_o, void* ws,
-                 size_t ws_bytes, hipStream_t stream) {
-  tsp::Shape s;
-  TSP_TRY(make_shape(dims, &s));
-  TSP_TRY(need_ptr(x_local, "x_local"));
-  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
-  TSP_TRY(need_ptr(w_o, "w_o"));
-  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
-  TSP_TRY(need_ptr(dh, "dh"));
-  TSP_TRY(need_ptr(dq, "dq"));
-  TSP_TRY(need_ptr(dkv_send, "dkv_send"));
-  TSP_TRY(need_ptr(dw_o, "dw_o"));
-  TSP_TRY(need_ptr(ws, "ws"));
-  if (ws_bytes < ws_attn_bwd(s))
-    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_attn_bwd(s));
-  TSP_TRY(check_device("tsp_attn_bwd"));
-  AttnBwdWs w;
-  ws_attn_bwd(s, &w, static_cast<char*>(ws));
+// The attention backward from the forward's Q, O and row normalisers (w.q,
+// w.o, w.lse) on: dO = dh W_O, Delta, dQ, the K/V-gradient send buffer and
+// the dW_O share.
+static int attn_bwd_from_forward(const tsp::Shape& s, const uint16_t* w_o, const uint16_t* kv_gathered,
+                                 const float* dh, float* dq, float* dkv_send, float* dw_o, AttnBwdWs& w,
+                                 hipStream_t stream) {
   const int Mp = mpad(s), h = s.h, qs = s.Hq_s * s.dh;
-  // recomputation: Q (from the Q rows of every shard of W_QKV, read in
-  // place), then the attention output with its row normalisers
-  TSP_LAUNCH(tsp::launch_q_gemm(s, x_local, static_cast<const uint16_t*>(w_qkv), w.q, stream), "attn bwd: Q");
-  TSP_LAUNCH(tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, stream, w.lse), "attn bwd: attention");
   // dO = dh W_O: W_O read as stored, or through the copy WoT (W_O_j
   // [h][qs] -> WoT rows j qs ..: [qs][h]) where the workspace holds one
   TSP_LAUNCH(tsp::launch_f32_to_bf16(dh, w.dh16, (int64_t)s.M * h, stream), "attn bwd: dh to bf16");
@@ -661,6 +653,84 @@ int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t
              "attn bwd: O^T");
   TSP_LAUNCH(tsp::launch_attn_bwd_dwo(s, Mp, w.dhT, w.oT, dw_o, stream), "attn bwd: dW_O");
   return TSP_OK;
+}
+
+int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const uint16_t* w_o,
+                 const uint16_t* kv_gathered, const float* dh, float* dq, float* dkv_send, float* dw_o, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(x_local, "x_local"));
+  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
+  TSP_TRY(need_ptr(w_o, "w_o"));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(need_ptr(dh, "dh"));
+  TSP_TRY(need_ptr(dq, "dq"));
+  TSP_TRY(need_ptr(dkv_send, "dkv_send"));
+  TSP_TRY(need_ptr(dw_o, "dw_o"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  if (ws_bytes < ws_attn_bwd(s))
+    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_attn_bwd(s));
+  TSP_TRY(check_device("tsp_attn_bwd"));
+  AttnBwdWs w;
+  ws_attn_bwd(s, &w, static_cast<char*>(ws));
+  // recomputation: Q (from the Q rows of every shard of W_QKV, read in
+  // place), then the attention output with its row normalisers
+  TSP_LAUNCH(tsp::launch_q_gemm(s, x_local, static_cast<const uint16_t*>(w_qkv), w.q, stream), "attn bwd: Q");
+  TSP_LAUNCH(tsp::launch_flash_attn(s, w.q, kv_gathered, w.o, w.partial, stream, w.lse), "attn bwd: attention");
+  return attn_bwd_from_forward(s, w_o, kv_gathered, dh, dq, dkv_send, dw_o, w, stream);
+}
+
+int tsp_attn_bwd_kept(const tsp_dims_t* dims, const uint16_t* w_o, const uint16_t* kv_gathered,
+                      const uint16_t* q_keep, const uint16_t* o_keep, const float* lse_keep, const float* dh,
+                      float* dq, float* dkv_send, float* dw_o, void* ws, size_t ws_bytes, hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(w_o, "w_o"));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(need_ptr(q_keep, "q_keep"));
+  TSP_TRY(need_ptr(o_keep, "o_keep"));
+  TSP_TRY(need_ptr(lse_keep, "lse_keep"));
+  TSP_TRY(need_ptr(dh, "dh"));
+  TSP_TRY(need_ptr(dq, "dq"));
+  TSP_TRY(need_ptr(dkv_send, "dkv_send"));
+  TSP_TRY(need_ptr(dw_o, "dw_o"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  const size_t need = ws_attn_bwd(s, nullptr, nullptr, true);
+  if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  TSP_TRY(check_device("tsp_attn_bwd_kept"));
+  AttnBwdWs w;
+  ws_attn_bwd(s, &w, static_cast<char*>(ws), true);
+  w.q = const_cast<uint16_t*>(q_keep);
+  w.o = const_cast<uint16_t*>(o_keep);
+  w.lse = const_cast<float*>(lse_keep);
+  return attn_bwd_from_forward(s, w_o, kv_gathered, dh, dq, dkv_send, dw_o, w, stream);
+}
+
+int tsp_attn_fwd_keep(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                      const uint16_t* w_o, uint16_t* kv_gathered, const float* residual, float* out,
+                      uint16_t* q_keep, uint16_t* o_keep, float* lse_keep, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  tsp::Shape s;
+  TSP_TRY(make_shape(dims, &s));
+  TSP_TRY(need_ptr(x_local, "x_local"));
+  TSP_TRY(need_ptr(w_qkv, "w_qkv"));
+  TSP_TRY(need_ptr(w_o, "w_o"));
+  TSP_TRY(need_ptr(kv_gathered, "kv_gathered"));
+  TSP_TRY(opt_ptr(residual, "residual"));
+  TSP_TRY(need_ptr(out, "out"));
+  TSP_TRY(need_ptr(q_keep, "q_keep"));
+  TSP_TRY(need_ptr(o_keep, "o_keep"));
+  TSP_TRY(need_ptr(lse_keep, "lse_keep"));
+  TSP_TRY(need_ptr(ws, "ws"));
+  const size_t need = ws_attn_keep(s);
+  if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  TSP_TRY(check_device("tsp_attn_fwd_keep"));
+  AttnWs w;
+  w.q = q_keep;
+  w.o = o_keep;
+  w.partial = partial_or_null(s, static_cast<char*>(ws));
+  return run_attention(s, x_local, w_qkv, w_o, kv_gathered, nullptr, residual, out, nullptr, w, stream, lse_keep);
 }
 
 int tsp_attn_bwd_proj(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const float* dq,

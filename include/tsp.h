@@ -117,7 +117,10 @@ typedef enum {
   TSP_FN_MLP_BWD = 6,    /* tsp_mlp_ring_bwd workspace */
   TSP_FN_ATTN_BWD = 7,   /* tsp_attn_bwd workspace */
   TSP_FN_ATTN_BWD_PROJ = 8, /* tsp_attn_bwd_proj workspace */
-  TSP_FN_DKV = 9         /* size of tsp_attn_bwd's dkv_send output */
+  TSP_FN_DKV = 9,        /* size of tsp_attn_bwd's dkv_send output */
+  TSP_FN_ATTN_KEEP = 10, /* tsp_attn_fwd_keep workspace */
+  TSP_FN_ATTN_BWD_KEPT = 11, /* tsp_attn_bwd_kept workspace */
+  TSP_FN_LSE = 12        /* size of tsp_attn_fwd_keep's lse_keep output */
 } tsp_fn;
 
 /* Maps of the partition dims->partition selects, as described above (TSP
@@ -306,6 +309,34 @@ int tsp_attn_bwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t
 int tsp_attn_bwd_proj(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv, const float* dq,
                       const float* dkv_own, const float* dx_residual, float* dx, float* dw_qkv, void* ws,
                       size_t ws_bytes, hipStream_t stream);
+
+/* The attention backward with the forward's activations kept instead of
+ * recomputed (the other side of the recompute-or-keep choice the pages leave
+ * open; tsp_attn_bwd recomputes): tsp_attn_fwd_keep is tsp_attn_fwd that
+ * also hands its Q, its attention output O and each row's softmax
+ * normaliser to the caller, and tsp_attn_bwd_kept is part 1 of the backward
+ * (tsp_attn_bwd's outputs, bit for bit) from them, skipping the
+ * recomputation of Q and of the attention (about a fifth of part 1's time at
+ * the 8K layer).  The kept tensors cost 2 M Hq dh 2 + B Hq T 4 bytes per
+ * layer (about 16 MiB per layer at the 8K layer, 256 MiB at 128K).
+ * tsp_attn_fwd_keep arguments: those of tsp_attn_fwd, and
+ *   q_keep    f16 [B][Hq][T][dh] out: Q of the rank's tokens (all heads)
+ *   o_keep    f16 [B][T][Hq*dh] out: the attention output before W_O
+ *   lse_keep  float32 [B][Hq][T] out (tsp_workspace_bytes(dims, TSP_FN_LSE)
+ *             bytes): log2 of each row's softmax normaliser of the scaled
+ *             scores, so P = 2^(s log2(e) / sqrt(dh) - lse)
+ *   ws        >= tsp_workspace_bytes(dims, TSP_FN_ATTN_KEEP) bytes
+ * tsp_attn_bwd_kept arguments: those of tsp_attn_bwd without x_local and
+ * w_qkv, plus q_keep, o_keep and lse_keep from tsp_attn_fwd_keep on the same
+ * dims and K/V (read only), and
+ *   ws        >= tsp_workspace_bytes(dims, TSP_FN_ATTN_BWD_KEPT) bytes */
+int tsp_attn_fwd_keep(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t* w_qkv,
+                      const uint16_t* w_o, uint16_t* kv_gathered, const float* residual, float* out,
+                      uint16_t* q_keep, uint16_t* o_keep, float* lse_keep, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+int tsp_attn_bwd_kept(const tsp_dims_t* dims, const uint16_t* w_o, const uint16_t* kv_gathered,
+                      const uint16_t* q_keep, const uint16_t* o_keep, const float* lse_keep, const float* dh,
+                      float* dq, float* dkv_send, float* dw_o, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Whole layer on rank dims->rank: h = x + Attn(x), y = h + MLP(h), with the
  * argument layouts of tsp_attn_fwd and tsp_mlp_ring_fwd.  h stays float32;

@@ -424,3 +424,39 @@ def test_bwd_dx_copies_when_shard_width_is_not_a_multiple_of_32(lib):
     finally:
         lib.tsp_set_tuning(B.TUNE["bwd_weights"], -1)
     assert copies - base == _up256(704 * 192 * 2)
+
+
+def test_attn_keep_argument_checks_and_sizes(lib):
+    d = _dims()
+    s = B.dims_struct(synth.WORKLOADS["llama7b_s8k_d8"].dims)
+    big = 1 << 40
+    # kept tensors: lse is float32 [B][Hq][T]; the kept backward's workspace is
+    # the recomputing one without q, o and lse
+    wl = synth.WORKLOADS["llama7b_s8k_d8"].dims
+    T = wl.seq // wl.degree
+    rows = wl.batch * wl.n_q_heads * T
+    assert lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_LSE) == rows * 4
+    qo = wl.batch * T * wl.n_q_heads * wl.head_dim * 2
+    full = lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_ATTN_BWD)
+    kept = lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_ATTN_BWD_KEPT)
+    assert full - kept == 2 * _up256(qo) + _up256(rows * 4)
+    assert lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_ATTN_KEEP) > 0
+    f = lib.tsp_attn_fwd_keep
+    names = ("x", "wqkv", "wo", "kv", "res", "out", "q", "o", "lse", "ws")
+    args = lambda **kw: [kw.get(n, None if n == "res" else FAKE) for n in names]
+    for n, label in (("q", "q_keep"), ("o", "o_keep"), ("lse", "lse_keep"), ("out", "out")):
+        assert f(ctypes.byref(d), *args(**{n: None}), big, None) == B.TSP_ERR_NULL_POINTER
+        assert f"{label} is NULL" in lib.tsp_last_error().decode()
+    assert f(ctypes.byref(d), *args(lse=MISALIGNED), big, None) == B.TSP_ERR_MISALIGNED
+    need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_ATTN_KEEP)
+    assert f(ctypes.byref(d), *args(), need - 1, None) == B.TSP_ERR_WORKSPACE
+    g = lib.tsp_attn_bwd_kept
+    gnames = ("wo", "kv", "q", "o", "lse", "dh", "dq", "send", "dwo", "ws")
+    gargs = lambda **kw: [kw.get(n, FAKE) for n in gnames]
+    for n, label in zip(gnames, ("w_o", "kv_gathered", "q_keep", "o_keep", "lse_keep", "dh", "dq", "dkv_send",
+                                 "dw_o", "ws")):
+        assert g(ctypes.byref(d), *gargs(**{n: None}), big, None) == B.TSP_ERR_NULL_POINTER
+        assert f"{label} is NULL" in lib.tsp_last_error().decode()
+    need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_ATTN_BWD_KEPT)
+    assert g(ctypes.byref(d), *gargs(), need - 1, None) == B.TSP_ERR_WORKSPACE
+    assert g(ctypes.byref(_dims(rank=5)), *gargs(), big, None) == B.TSP_ERR_RANK

@@ -226,3 +226,43 @@ def test_attn_bwd_full_size_llama7b():
     pref = bwd.rank_attention_bwd_proj(inp, d, dq_in, own_in)
     _check("dx", dx.cpu().numpy(), pref["dx_attn"] + dh_rows)
     _check("dw_qkv", dwqkv.cpu().numpy(), pref["dw_qkv"])
+
+
+# tsp_attn_fwd_keep + tsp_attn_bwd_kept (the forward's Q, O and row
+# normalisers kept instead of recomputed) against tsp_attn_fwd +
+# tsp_attn_bwd: the same kernels produce the kept tensors, so the layer
+# output and every backward output agree bit for bit.  Shapes: GQA 4 with
+# head_dim 128 under both partitions, blocks cut into key pieces (the merge
+# writes those rows' normalisers), chunks of 24 positions.
+@pytest.mark.parametrize("name,partition", [("gqa4_dh128_d4_r2", 0), ("gqa4_dh128_d4_r2", 1),
+                                            ("split_keys_dh128", 0), ("c24_generic_reorder", 1)])
+def test_attn_bwd_kept_equals_recompute(name, partition):
+    shape = SWEEP[name][:9] + (partition,)
+    d = dims_of(shape)
+    _case(f"attn_bwd_kept {name} partition={partition} {d}")
+    inp = inputs_for(shape, 0.02, 101)
+    R = _Ranks(d, inp)
+    r = d.rank
+    T = d.seq // d.degree
+    f32 = dict(dtype=torch.float32, device="cuda")
+    x32 = R.x_loc[r].view(torch.bfloat16).float()
+    out_ref = torch.empty((d.batch, T, d.hidden), **f32)
+    wsa = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN), dtype=torch.uint8, device="cuda")
+    B.tsp_attn_fwd(d, R.x_loc[r], R.w["w_qkv"], R.w["w_o"], R.kv, out_ref, wsa, residual=x32)
+    qd = d.n_q_heads * d.head_dim
+    out = torch.empty_like(out_ref)
+    q_keep = torch.empty(d.batch * T * qd, dtype=torch.int16, device="cuda")
+    o_keep = torch.empty_like(q_keep)
+    lse = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_LSE) // 4, **f32)
+    wsk = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_KEEP), dtype=torch.uint8, device="cuda")
+    B.tsp_attn_fwd_keep(d, R.x_loc[r], R.w["w_qkv"], R.w["w_o"], R.kv, out, q_keep, o_keep, lse, wsk, residual=x32)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    dh_rows = torch.from_numpy(np.ascontiguousarray(synth.make_grad(d, 29)[:, R.l2g[r]])).cuda()
+    dq, send, dwo = R.bwd(r, dh_rows)
+    dq2, send2, dwo2 = torch.empty_like(dq), torch.empty_like(send), torch.empty_like(dwo)
+    wsb = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_ATTN_BWD_KEPT), dtype=torch.uint8, device="cuda")
+    B.tsp_attn_bwd_kept(d, R.w["w_o"], R.kv, q_keep, o_keep, lse, dh_rows, dq2, send2, dwo2, wsb)
+    torch.cuda.synchronize()
+    for nm, x, y in (("dq", dq, dq2), ("dkv_send", send, send2), ("dw_o", dwo, dwo2)):
+        assert torch.equal(x, y), nm
