@@ -275,12 +275,43 @@ def mlp_backward_measure(d, wl, prob, steps: int):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # the same backward from the forward's kept g and u (tsp_mlp_ring_fwd_keep)
+    # instead of recomputing them; and the forward's cost of keeping them
+    y = torch.empty_like(dy)
+    gu = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_GU) // 4, dtype=torch.float32, device="cuda")
+    wsf = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP), dtype=torch.uint8, device="cuda")
+    fwd_ms = timed(lambda: B.tsp_mlp_ring_fwd(d, prob.x_local, w["w_gate"], w["w_up"], w["w_down"], y, wsf,
+                                              x_dtype=B.TSP_BF16))
+    fwd_keep_ms = timed(lambda: B.tsp_mlp_ring_fwd_keep(d, prob.x_local, w["w_gate"], w["w_up"], w["w_down"], y,
+                                                        gu, wsf, x_dtype=B.TSP_BF16))
+    wsk = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP_BWD_KEPT), dtype=torch.uint8, device="cuda")
+    kept_ms = timed(lambda: B.tsp_mlp_ring_bwd_kept(d, prob.x_local, dy, w["w_gate"], w["w_up"], w["w_down"], gu,
+                                                    dx, dwg, dwu, dwd, wsk, dx_residual=dy, x_dtype=B.TSP_BF16))
     alg = 12.0 * M * d.ffn * d.hidden
     executed = alg + 4.0 * M * d.ffn * d.hidden
-    del ws, dwg, dwu, dwd, dx, dy
+    del ws, wsk, wsf, gu, y, dwg, dwu, dwd, dx, dy
     return {"ms_per_call": round(ms, 5), "calls": steps, "gflop_algorithmic": round(alg / 1e9, 2),
             "gflop_executed": round(executed / 1e9, 2), "tflops": round(alg / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(alg / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "kept_forward_activations": {
+                "ms_per_call": round(kept_ms, 5),
+                "tflops": round(alg / (kept_ms * 1e-3) / 1e12, 2),
+                "forward_ms": round(fwd_ms, 5), "forward_keep_ms": round(fwd_keep_ms, 5),
+                "what": "tsp_mlp_ring_bwd_kept from tsp_mlp_ring_fwd_keep's g and u (no recomputation of the "
+                        "gate/up product); the same outputs.  forward_ms / forward_keep_ms: tsp_mlp_ring_fwd "
+                        "without and with handing g and u over"},
             "input": "bf16 rank rows of x; dy float32 ~ N(0, 1); dx_residual = dy"}
 
 

@@ -55,6 +55,8 @@ TSP_FN_DKV = 9
 TSP_FN_ATTN_KEEP = 10
 TSP_FN_ATTN_BWD_KEPT = 11
 TSP_FN_LSE = 12
+TSP_FN_MLP_BWD_KEPT = 13
+TSP_FN_GU = 14
 
 KERNELS = {"qkv": 1, "reorder": 2, "attn": 3, "oproj": 4, "gateup": 5, "down": 6, "attn_bwd": 7}
 
@@ -65,7 +67,7 @@ EXPORTED = ("tsp_zigzag_index", "tsp_qkv_proj", "tsp_kv_reorder", "tsp_attn_fwd"
             "tsp_mlp_ring_fwd", "tsp_layer_fwd", "tsp_workspace_bytes", "tsp_last_error",
             "tsp_profile_kernel", "tsp_profile_result", "tsp_set_tuning", "tsp_layer_fwd_noalloc",
             "tsp_mlp_ring_bwd", "tsp_attn_bwd", "tsp_attn_bwd_proj", "tsp_attn_fwd_keep",
-            "tsp_attn_bwd_kept")
+            "tsp_attn_bwd_kept", "tsp_mlp_ring_fwd_keep", "tsp_mlp_ring_bwd_kept")
 
 # Size of the library's fixed scratch array (TSP_SCRATCH_BYTES in include/tsp.h).
 TSP_SCRATCH_BYTES = 128 * 1024 * 1024
@@ -110,6 +112,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tsp_attn_bwd_proj": [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_attn_fwd_keep": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "tsp_attn_bwd_kept": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_mlp_ring_fwd_keep": [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "tsp_mlp_ring_bwd_kept": [dp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -273,13 +277,10 @@ def tsp_attn_fwd(dims, x_local, w_qkv, w_o, kv_gathered, out, ws, residual=None,
 _XDTYPE = {torch.bfloat16: TSP_BF16, torch.float16: TSP_F16, torch.float32: TSP_F32}
 
 
-def tsp_mlp_ring_fwd(dims, x, w_gate, w_up, w_down, y, ws, residual=None, x_dtype=None, stream=None):
-    """y = residual + MLP ring over x (residual None: the MLP branch alone).
-
-    x_dtype: TSP_BF16 / TSP_F16 / TSP_F32; None takes it from x's torch dtype
-    (bfloat16, float16 or float32; 16-bit integer bit patterns need x_dtype)."""
-    z = _Sizes(dims)
-    d = dims_struct(dims)
+def _x_kind(x, x_dtype):
+    """(x_dtype, tensor kind) of an MLP input: x_dtype TSP_BF16 / TSP_F16 /
+    TSP_F32, or None to take it from x's torch dtype (bfloat16, float16 or
+    float32; 16-bit integer bit patterns need x_dtype)."""
     if x_dtype is None:
         if not isinstance(x, torch.Tensor) or x.dtype not in _XDTYPE:
             raise ValueError("x_dtype is required unless x is bfloat16, float16 or float32")
@@ -287,36 +288,70 @@ def tsp_mlp_ring_fwd(dims, x, w_gate, w_up, w_down, y, ws, residual=None, x_dtyp
     kind = {TSP_BF16: "bf16", TSP_F16: "f16", TSP_F32: "f32"}.get(int(x_dtype))
     if kind is None:
         raise ValueError(f"x_dtype {x_dtype} unknown")
+    return int(x_dtype), kind
+
+
+def _mlp_fwd(fn, dims, x, w_gate, w_up, w_down, y, ws, residual, x_dtype, stream, gu_keep=None):
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    x_dtype, kind = _x_kind(x, x_dtype)
     wsp, wsn = _ws(dims, ws, TSP_FN_MLP)
-    _check(load().tsp_mlp_ring_fwd(ctypes.byref(d), _tensor(x, "x", kind, z.f32 if kind == "f32" else z.x16),
-                                   int(x_dtype), _tensor(w_gate, "w_gate", "bf16", z.w_ffn),
-                                   _tensor(w_up, "w_up", "bf16", z.w_ffn), _tensor(w_down, "w_down", "bf16", z.w_ffn),
-                                   _tensor(residual, "residual", "f32", z.f32, optional=True),
-                                   _tensor(y, "y", "f32", z.f32), wsp, wsn, _s(stream)))
+    head = [ctypes.byref(d), _tensor(x, "x", kind, z.f32 if kind == "f32" else z.x16), x_dtype,
+            _tensor(w_gate, "w_gate", "bf16", z.w_ffn), _tensor(w_up, "w_up", "bf16", z.w_ffn),
+            _tensor(w_down, "w_down", "bf16", z.w_ffn), _tensor(residual, "residual", "f32", z.f32, optional=True),
+            _tensor(y, "y", "f32", z.f32)]
+    if fn == "tsp_mlp_ring_fwd_keep":
+        head.append(_tensor(gu_keep, "gu_keep", "f32", tsp_workspace_bytes(dims, TSP_FN_GU)))
+    _check(getattr(load(), fn)(*head, wsp, wsn, _s(stream)))
+
+
+def tsp_mlp_ring_fwd(dims, x, w_gate, w_up, w_down, y, ws, residual=None, x_dtype=None, stream=None):
+    """y = residual + MLP ring over x (residual None: the MLP branch alone).
+
+    x_dtype: TSP_BF16 / TSP_F16 / TSP_F32; None takes it from x's torch dtype
+    (bfloat16, float16 or float32; 16-bit integer bit patterns need x_dtype)."""
+    _mlp_fwd("tsp_mlp_ring_fwd", dims, x, w_gate, w_up, w_down, y, ws, residual, x_dtype, stream)
+
+
+def tsp_mlp_ring_fwd_keep(dims, x, w_gate, w_up, w_down, y, gu_keep, ws, residual=None, x_dtype=None, stream=None):
+    """tsp_mlp_ring_fwd that also hands g = x Wg^T and u = x Wu^T (float32
+    [2][B][T][F]: g, then u) to the caller, for tsp_mlp_ring_bwd_kept."""
+    _mlp_fwd("tsp_mlp_ring_fwd_keep", dims, x, w_gate, w_up, w_down, y, ws, residual, x_dtype, stream, gu_keep)
+
+
+def _mlp_bwd(fn, dims, x, dy, w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down, ws, dx_residual, x_dtype, stream,
+             gu_keep=None):
+    z = _Sizes(dims)
+    d = dims_struct(dims)
+    x_dtype, kind = _x_kind(x, x_dtype)
+    kept = fn == "tsp_mlp_ring_bwd_kept"
+    wsp, wsn = _ws(dims, ws, TSP_FN_MLP_BWD_KEPT if kept else TSP_FN_MLP_BWD)
+    fw = 2 * z.w_ffn      # float32 gradient of a [F][h] weight
+    args = [ctypes.byref(d), _tensor(x, "x", kind, z.f32 if kind == "f32" else z.x16), x_dtype,
+            _tensor(dy, "dy", "f32", z.f32), _tensor(w_gate, "w_gate", "bf16", z.w_ffn),
+            _tensor(w_up, "w_up", "bf16", z.w_ffn), _tensor(w_down, "w_down", "bf16", z.w_ffn)]
+    if kept:
+        args.append(_tensor(gu_keep, "gu_keep", "f32", tsp_workspace_bytes(dims, TSP_FN_GU)))
+    args += [_tensor(dx_residual, "dx_residual", "f32", z.f32, optional=True), _tensor(dx, "dx", "f32", z.f32),
+             _tensor(dw_gate, "dw_gate", "f32", fw), _tensor(dw_up, "dw_up", "f32", fw),
+             _tensor(dw_down, "dw_down", "f32", fw), wsp, wsn, _s(stream)]
+    _check(getattr(load(), fn)(*args))
 
 
 def tsp_mlp_ring_bwd(dims, x, dy, w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down, ws, dx_residual=None,
                      x_dtype=None, stream=None):
     """Backward of the MLP ring: dx = dx_residual + dMLP/dx^T dy and this rank's
     contributions to dW_gate, dW_up ([F][h]) and dW_down ([D][h][F/D])."""
-    z = _Sizes(dims)
-    d = dims_struct(dims)
-    if x_dtype is None:
-        if not isinstance(x, torch.Tensor) or x.dtype not in _XDTYPE:
-            raise ValueError("x_dtype is required unless x is bfloat16, float16 or float32")
-        x_dtype = _XDTYPE[x.dtype]
-    kind = {TSP_BF16: "bf16", TSP_F16: "f16", TSP_F32: "f32"}.get(int(x_dtype))
-    if kind is None:
-        raise ValueError(f"x_dtype {x_dtype} unknown")
-    wsp, wsn = _ws(dims, ws, TSP_FN_MLP_BWD)
-    fw = 2 * z.w_ffn      # float32 gradient of a [F][h] weight
-    _check(load().tsp_mlp_ring_bwd(
-        ctypes.byref(d), _tensor(x, "x", kind, z.f32 if kind == "f32" else z.x16), int(x_dtype),
-        _tensor(dy, "dy", "f32", z.f32), _tensor(w_gate, "w_gate", "bf16", z.w_ffn),
-        _tensor(w_up, "w_up", "bf16", z.w_ffn), _tensor(w_down, "w_down", "bf16", z.w_ffn),
-        _tensor(dx_residual, "dx_residual", "f32", z.f32, optional=True), _tensor(dx, "dx", "f32", z.f32),
-        _tensor(dw_gate, "dw_gate", "f32", fw), _tensor(dw_up, "dw_up", "f32", fw),
-        _tensor(dw_down, "dw_down", "f32", fw), wsp, wsn, _s(stream)))
+    _mlp_bwd("tsp_mlp_ring_bwd", dims, x, dy, w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down, ws, dx_residual,
+             x_dtype, stream)
+
+
+def tsp_mlp_ring_bwd_kept(dims, x, dy, w_gate, w_up, w_down, gu_keep, dx, dw_gate, dw_up, dw_down, ws,
+                          dx_residual=None, x_dtype=None, stream=None):
+    """tsp_mlp_ring_bwd from the g and u tsp_mlp_ring_fwd_keep kept (no
+    recomputation of the gate/up product); the same outputs."""
+    _mlp_bwd("tsp_mlp_ring_bwd_kept", dims, x, dy, w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down, ws,
+             dx_residual, x_dtype, stream, gu_keep)
 
 
 def tsp_attn_bwd(dims, x_local, w_qkv, w_o, kv_gathered, dh, dq, dkv_send, dw_o, ws, stream=None):

@@ -26,7 +26,9 @@ namespace tsp {
 
 enum { EPI_QKV = 0, EPI_RESID_BF16X = 1, EPI_RESID_F32 = 2, EPI_SWIGLU = 3, EPI_PARTIAL = 4,
        // backward of the gated MLP (see the launchers at the end)
-       EPI_SWIGLU_BWD = 5, EPI_DWD = 6, EPI_DWGU = 7 };
+       EPI_SWIGLU_BWD = 5, EPI_DWD = 6, EPI_DWGU = 7,
+       // ... with g and u kept from the forward: the dA product's epilogue
+       EPI_SWIGLU_KEPT = 8 };
 
 struct GemmArgs {
   const uint16_t* A;
@@ -60,6 +62,8 @@ struct GemmArgs {
   // per shard, b_shard rows apart); b_w = 0: row n.
   int64_t ldbk, b_shard;
   int32_t b_w, b_half;
+  // EPI_SWIGLU_KEPT: u kept from the forward (float32 [M][N]; g is resid)
+  const float* resid2;
 };
 
 // Stored row of B's row n (N-major B; see GemmArgs::b_w).
@@ -80,38 +84,77 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// The epilogue input of columns n..n+3 of row m, for the epilogues that read
-// one (the residual, or dA): loaded apart from the epilogue itself so that a
+// The epilogue inputs of columns n..n+3 of row m, for the epilogues that
+// read them (the residual; dA; g and u kept from the forward): loaded apart from the epilogue itself so that a
 // tile issues all its input loads before its first store (the stores may
 // alias the inputs as far as the compiler knows, so loads placed between
 // them would each wait for the previous group's round trip).
+// y is read by EPI_SWIGLU_KEPT only (the other epilogues leave it zero and
+// the compiler drops it).
+struct EpiIn {
+  f32x4 x, y;
+};
+
 template <int EPI>
-__device__ __forceinline__ f32x4 epilogue_input(const GemmArgs& a, int m, int n) {
-  f32x4 r{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ EpiIn epilogue_input(const GemmArgs& a, int m, int n) {
+  EpiIn r{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   if (m >= a.M || n >= a.N) return r;
   const int64_t off = (int64_t)m * a.N + n;
   if constexpr (EPI == EPI_RESID_BF16X) {
     const u32x2 xr = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.resid) + off);
-    r[0] = __uint_as_float(xr[0] << 16);
-    r[1] = __uint_as_float(xr[0] & 0xffff0000u);
-    r[2] = __uint_as_float(xr[1] << 16);
-    r[3] = __uint_as_float(xr[1] & 0xffff0000u);
+    r.x[0] = __uint_as_float(xr[0] << 16);
+    r.x[1] = __uint_as_float(xr[0] & 0xffff0000u);
+    r.x[2] = __uint_as_float(xr[1] << 16);
+    r.x[3] = __uint_as_float(xr[1] & 0xffff0000u);
   } else if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_SWIGLU_BWD) {
-    if (a.resid != nullptr) r = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
+    if (a.resid != nullptr) r.x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
+  } else if constexpr (EPI == EPI_SWIGLU_KEPT) {
+    r.x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.resid) + off);
+    r.y = *reinterpret_cast<const f32x4*>(a.resid2 + off);
   }
   return r;
 }
 
 template <int EPI>
 constexpr bool epilogue_reads() {
-  return EPI == EPI_RESID_BF16X || EPI == EPI_RESID_F32 || EPI == EPI_SWIGLU_BWD;
+  return EPI == EPI_RESID_BF16X || EPI == EPI_RESID_F32 || EPI == EPI_SWIGLU_BWD || EPI == EPI_SWIGLU_KEPT;
 }
 
-// in: the epilogue input (epilogue_input) for the epilogues that read one.
+// The SwiGLU backward of columns n..n+3 (F axis) of row m from g = x Wg^T,
+// u = x Wu^T and dA = dy Wd: with s = sigmoid(g), a = g s u, dU = dA g s,
+// dG = dA u s (1 + g (1 - s)).  a goes to out16 (bf16 [M][F]); dG and dU to
+// aux16 (bf16 [M][D][2][F/D]: shard j's dG block, then its dU block, per
+// row).  The four columns lie in one shard.
+__device__ __forceinline__ void swiglu_bwd4(const GemmArgs& a, int m, int n, const float* g4, const float* u4,
+                                            const float* da) {
+  const Shape& s = a.s;
+  const int64_t off = (int64_t)m * a.N + n;
+  float av[4], dg[4], du[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float g = g4[e], u = u4[e];
+    const float sg = 1.0f / (1.0f + __expf(-g));
+    const float gs = g * sg;
+    av[e] = gs * u;
+    du[e] = da[e] * gs;
+    dg[e] = da[e] * u * (sg + gs * (1.0f - sg));
+  }
+  u32x2 pa{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+  *reinterpret_cast<u32x2*>(a.out16 + off) = pa;
+  const int j = n / s.F_s, f = n - j * s.F_s;
+  uint16_t* gu = a.aux16 + (int64_t)m * 2 * s.F + (int64_t)j * 2 * s.F_s + f;
+  u32x2 pg{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+  u32x2 pu{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+  *reinterpret_cast<u32x2*>(gu) = pg;
+  *reinterpret_cast<u32x2*>(gu + s.F_s) = pu;
+}
+
+// ein: the epilogue inputs (epilogue_input) for the epilogues that read them.
 template <int EPI>
 __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const float* v,
-                                          const float* v2, const f32x4& in) {
+                                          const float* v2, const EpiIn& ein) {
   if (m >= a.M || n >= a.N) return;
+  const f32x4& in = ein.x;
   if constexpr (EPI == EPI_QKV) {
     const Shape& s = a.s;
     const int b = m / s.T, t = m - b * s.T;
@@ -164,32 +207,15 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
     // v2 carries the split index in its first element's bits (see caller)
     (void)v2;
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    // v = g = x Wg^T, v2 = u = x Wu^T for columns n..n+3 (F axis); resid =
-    // dA = dy Wd (float32 [M][F]).  With s = sigmoid(g): a = g s u,
-    // dU = dA g s, dG = dA u s (1 + g (1 - s)).  a goes to out16 (bf16
-    // [M][F]); dG and dU to aux16 (bf16 [M][D][2][F/D]: shard j's dG block,
-    // then its dU block, per row).  The four columns lie in one shard.
-    const Shape& s = a.s;
-    const int64_t off = (int64_t)m * a.N + n;
-    const f32x4& da = in;
-    float av[4], dg[4], du[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float g = v[e], u = v2[e];
-      const float sg = 1.0f / (1.0f + __expf(-g));
-      const float gs = g * sg;
-      av[e] = gs * u;
-      du[e] = da[e] * gs;
-      dg[e] = da[e] * u * (sg + gs * (1.0f - sg));
-    }
-    u32x2 pa{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
-    *reinterpret_cast<u32x2*>(a.out16 + off) = pa;
-    const int j = n / s.F_s, f = n - j * s.F_s;
-    uint16_t* gu = a.aux16 + (int64_t)m * 2 * s.F + (int64_t)j * 2 * s.F_s + f;
-    u32x2 pg{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-    u32x2 pu{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-    *reinterpret_cast<u32x2*>(gu) = pg;
-    *reinterpret_cast<u32x2*>(gu + s.F_s) = pu;
+    // v = g = x Wg^T, v2 = u = x Wu^T recomputed; in = dA = dy Wd (resid,
+    // float32 [M][F])
+    const float da[4] = {in[0], in[1], in[2], in[3]};
+    swiglu_bwd4(a, m, n, v, v2, da);
+  } else if constexpr (EPI == EPI_SWIGLU_KEPT) {
+    // v = dA = dy Wd; g and u as the forward wrote them (ein.x, ein.y)
+    const float g4[4] = {ein.x[0], ein.x[1], ein.x[2], ein.x[3]};
+    const float u4[4] = {ein.y[0], ein.y[1], ein.y[2], ein.y[3]};
+    swiglu_bwd4(a, m, n, g4, u4, v);
   } else if constexpr (EPI == EPI_DWD) {
     // C [M][N] (row m = hidden index, column n) -> out [N / w][M][w], w =
     // shard_w: dW_down [D][h][F/D], dW_O [D][h][Hq/D dh]
@@ -207,8 +233,12 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int m, int n, const
     const int f = j * s.F_s + (up ? w - s.F_s : w);
     f32x4 o{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>((up ? a.out2 : a.out) + (int64_t)f * a.N + n) = o;
-  } else {  // EPI_SWIGLU: v = gate, v2 = up
+  } else {  // EPI_SWIGLU: v = gate, v2 = up; kept for the backward when out != nullptr
     const int64_t off = (int64_t)m * a.N + n;
+    if (a.out != nullptr) {
+      *reinterpret_cast<f32x4*>(a.out + off) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(a.out2 + off) = f32x4{v2[0], v2[1], v2[2], v2[3]};
+    }
     u32x2 pk{pack_f16x2(silu_f32(v[0]) * v2[0], silu_f32(v[1]) * v2[1]),
              pack_f16x2(silu_f32(v[2]) * v2[2], silu_f32(v[3]) * v2[3])};
     *reinterpret_cast<u32x2*>(a.out16 + off) = pk;
@@ -313,7 +343,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
   for (int y = 0; y < NBL; ++y) {
     // the inputs of this column block's groups first (see epilogue_input),
     // then its stores: MB x 4 loads in flight at a time
-    f32x4 in[MB][4];
+    EpiIn in[MB][4];
     if constexpr (epilogue_reads<EPI>()) {
 #pragma unroll
       for (int z = 0; z < MB; ++z)
@@ -345,7 +375,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
           } else if constexpr (epilogue_reads<EPI>()) {
             epilogue4<EPI>(a, m, n, v, v2, in[z][q4]);
           } else {
-            epilogue4<EPI>(a, m, n, v, v2, f32x4{0.f, 0.f, 0.f, 0.f});
+            epilogue4<EPI>(a, m, n, v, v2, EpiIn{});
           }
         }
       }
@@ -385,13 +415,13 @@ __device__ __forceinline__ void store_tile_rows(const GemmArgs& a, const f32x16 
                         acc[x][y][z][4 * q4 + 3]};
           *reinterpret_cast<f32x4*>(lds + (x * 32 + lrow) * P + 8 * q4 + 4 * lgrp) = v;
         }
-      f32x4 in[4];
+      EpiIn in[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (epilogue_reads<EPI>())
           in[i] = epilogue_input<EPI>(a, m_base + z * 32 + rr + 8 * i, n_base + y * 32 + cc);
         else
-          in[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          in[i] = EpiIn{};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1107,7 +1137,8 @@ __global__ void gemm_reduce_kernel(GemmArgs a) {
   if (n >= a.N) return;
   const int64_t plane = (int64_t)a.M * a.N;
   for (int m0 = blockIdx.y * RR; m0 < a.M; m0 += gridDim.y * RR) {
-    f32x4 acc[RR], in[RR];
+    f32x4 acc[RR];
+    EpiIn in[RR];
     int64_t off[RR];
 #pragma unroll
     for (int i = 0; i < RR; ++i) {
@@ -1348,8 +1379,12 @@ hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* 
 }
 
 hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g,
-                              const uint16_t* w_u, uint16_t* act, hipStream_t st) {
+                              const uint16_t* w_u, uint16_t* act, hipStream_t st, float* gu_keep) {
   GemmArgs a = base_args(s);
+  if (gu_keep != nullptr) {
+    a.out = gu_keep;
+    a.out2 = gu_keep + (int64_t)s.M * s.F;
+  }
   a.A = x;
   a.lda = s.h;
   a.B0 = w_g;
@@ -1429,6 +1464,24 @@ hipError_t launch_bwd_da(const Shape& s, const uint16_t* dy16, const uint16_t* w
   a.out = da;
   a.resid = nullptr;
   return launch_cfg<false, false, EPI_RESID_F32>(a, 0, 1, st);
+}
+
+hipError_t launch_bwd_da_kept(const Shape& s, const uint16_t* dy16, const uint16_t* wdT, const float* gu_keep,
+                              uint16_t* act16, uint16_t* dgu, hipStream_t st) {
+  GemmArgs a = base_args(s);
+  a.A = dy16;
+  a.lda = s.h;
+  a.B0 = a.B1 = wdT;
+  a.ldb = s.h;
+  a.M = s.M;
+  a.N = s.F;
+  a.K = s.h;
+  a.seg_len = s.h;
+  a.resid = gu_keep;
+  a.resid2 = gu_keep + (int64_t)s.M * s.F;
+  a.out16 = act16;
+  a.aux16 = dgu;
+  return launch_cfg<false, false, EPI_SWIGLU_KEPT>(a, 0, 1, st);
 }
 
 hipError_t launch_bwd_gu(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g, const uint16_t* w_u,
@@ -1683,6 +1736,18 @@ hipError_t launch_bwd_da_kmajor(const Shape& s, const uint16_t* dy16, const uint
   a.resid = nullptr;
   // 256x192 tiles: one round of work groups at the 8K layer (4 x 58 tiles)
   return launch_staged_bkm<256, 192, 4, 8, EPI_RESID_F32>(a, 1, st);
+}
+
+hipError_t launch_bwd_da_kept_kmajor(const Shape& s, const uint16_t* dy16, const uint16_t* w_down,
+                                     const float* gu_keep, uint16_t* act16, uint16_t* dgu, hipStream_t st) {
+  GemmArgs a = kmajor_args(s, KMAJ_DA);
+  a.A = dy16;
+  a.B0 = a.B1 = w_down;
+  a.resid = gu_keep;
+  a.resid2 = gu_keep + (int64_t)s.M * s.F;
+  a.out16 = act16;
+  a.aux16 = dgu;
+  return launch_staged_bkm<256, 192, 4, 8, EPI_SWIGLU_KEPT>(a, 1, st);
 }
 
 hipError_t launch_bwd_dx_kmajor(const Shape& s, const uint16_t* dgu, const uint16_t* w_g, const uint16_t* w_u,

@@ -44,9 +44,11 @@ hipError_t launch_oproj_gemm(const Shape& s, const uint16_t* o, const uint16_t* 
                              float* partial, hipStream_t st);
 
 // act = silu(x Wg^T) * (x Wu^T): x f16 with f16 matrix cores (weights
-// bf16 -> f16), or x bf16 (x_bf16) with bf16 matrix cores on the weights as given.
+// bf16 -> f16), or x bf16 (x_bf16) with bf16 matrix cores on the weights as
+// given.  gu_keep (optional, float [2][M][F]): g = x Wg^T, then u = x Wu^T,
+// as the epilogue receives them (for the backward).
 hipError_t launch_gateup_gemm(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g,
-                              const uint16_t* w_u, uint16_t* act, hipStream_t st);
+                              const uint16_t* w_u, uint16_t* act, hipStream_t st, float* gu_keep = nullptr);
 
 // y = resid + sum over ring steps of act_j W_d,j^T (resid may be nullptr).
 hipError_t launch_down_gemm(const Shape& s, const uint16_t* act, const uint16_t* w_d,
@@ -68,6 +70,11 @@ hipError_t launch_f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_
 
 // dA = dy16 WdT^T (float32 [M][F]); WdT [F][h] bf16.
 hipError_t launch_bwd_da(const Shape& s, const uint16_t* dy16, const uint16_t* wdT, float* da, hipStream_t st);
+// dA = dy16 WdT^T in registers, with g and u kept from the forward (gu_keep,
+// float [2][M][F]): the epilogue of launch_bwd_gu without dA's round trip
+// through memory (act16 and dgu as there).
+hipError_t launch_bwd_da_kept(const Shape& s, const uint16_t* dy16, const uint16_t* wdT, const float* gu_keep,
+                              uint16_t* act16, uint16_t* dgu, hipStream_t st);
 // g, u recomputed from x (f16, or bf16 when x_bf16); epilogue: act16 = a
 // (bf16 [M][F]), dgu = dG | dU per shard (bf16 [M][D][2][F/D]).
 hipError_t launch_bwd_gu(const Shape& s, const uint16_t* x, bool x_bf16, const uint16_t* w_g, const uint16_t* w_u,
@@ -121,7 +128,8 @@ hipError_t launch_attn_bwd_dx(const Shape& s, const uint16_t* g16, const uint16_
 hipError_t launch_attn_bwd_dwqkv(const Shape& s, int m_pad, const uint16_t* gT, const uint16_t* xT, float* dw_qkv,
                                  hipStream_t st);
 // The same backward products with the weight read as stored (K-major, no
-// transposed copy): dA = dy16 W_down, dx = dx_resid + ring sum of dG_j
+// transposed copy): dA = dy16 W_down (also with launch_bwd_da_kept's
+// epilogue), dx = dx_resid + ring sum of dG_j
 // W_gate,j + dU_j W_up,j, dO = dh16 W_O, dx = dx_resid + G W_QKV (ring
 // order).  kmajor_ok(s, use) tells whether the variant applies to the shape
 // (K segments whole multiples of 64, operands within 32-bit offsets); the
@@ -130,6 +138,8 @@ enum { KMAJ_DA = 0, KMAJ_DX_MLP = 1, KMAJ_DO = 2, KMAJ_DX_ATTN = 3 };
 bool kmajor_ok(const Shape& s, int use);
 hipError_t launch_bwd_da_kmajor(const Shape& s, const uint16_t* dy16, const uint16_t* w_down, float* da,
                                 hipStream_t st);
+hipError_t launch_bwd_da_kept_kmajor(const Shape& s, const uint16_t* dy16, const uint16_t* w_down,
+                                     const float* gu_keep, uint16_t* act16, uint16_t* dgu, hipStream_t st);
 hipError_t launch_bwd_dx_kmajor(const Shape& s, const uint16_t* dgu, const uint16_t* w_g, const uint16_t* w_u,
                                 const float* dx_resid, float* dx, float* partial, hipStream_t st);
 hipError_t launch_attn_bwd_do_kmajor(const Shape& s, const uint16_t* dh16, const uint16_t* w_o, uint16_t* dout,

@@ -150,19 +150,21 @@ struct MlpBwdWs {
   float *da, *partial;
 };
 
-// [x16 | xT | dy16 | dyT | (wdT) | (wguT) | da | act | dgu | actT | dguT | split-K partials]
-size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullptr) {
+// [(x16) | xT | dy16 | dyT | (wdT) | (wguT) | (da) | act | dgu | actT | dguT | split-K partials]
+// (kept: g and u come from tsp_mlp_ring_fwd_keep, so neither the f16 copy of
+// a float32 x for their recomputation nor dA is stored)
+size_t ws_mlp_bwd(const tsp::Shape& s, MlpBwdWs* w = nullptr, char* base = nullptr, bool kept = false) {
   MlpBwdWs tmp;
   MlpBwdWs& x = w != nullptr ? *w : tmp;
   const size_t M = s.M, h = s.h, F = s.F, Mp = mpad(s);
   Carve c{base};
-  x.x16 = c.take<uint16_t>(M * h * 2);
+  x.x16 = kept ? nullptr : c.take<uint16_t>(M * h * 2);
   x.xT = c.take<uint16_t>(h * Mp * 2);
   x.dy16 = c.take<uint16_t>(M * h * 2);
   x.dyT = c.take<uint16_t>(h * Mp * 2);
   x.wdT = kmajor(s, tsp::KMAJ_DA) ? nullptr : c.take<uint16_t>(F * h * 2);
   x.wguT = kmajor(s, tsp::KMAJ_DX_MLP) ? nullptr : c.take<uint16_t>(h * 2 * F * 2);
-  x.da = c.take<float>(M * F * 4);
+  x.da = kept ? nullptr : c.take<float>(M * F * 4);
   x.act = c.take<uint16_t>(M * F * 2);
   x.dgu = c.take<uint16_t>(M * 2 * F * 2);
   x.actT = c.take<uint16_t>(F * Mp * 2);
@@ -365,9 +367,11 @@ int run_attention(const tsp::Shape& s, const uint16_t* x_local, const uint16_t* 
   return TSP_OK;
 }
 
+// gu_keep (optional): g and u kept for the backward.
 int run_mlp(const tsp::Shape& s, const uint16_t* x16, bool x_bf16, const float* resid, const uint16_t* w_gate,
-            const uint16_t* w_up, const uint16_t* w_down, float* y, const MlpWs& w, hipStream_t st) {
-  TSP_KLAUNCH(TSP_K_GATEUP, st, tsp::launch_gateup_gemm(s, x16, x_bf16, w_gate, w_up, w.act, st),
+            const uint16_t* w_up, const uint16_t* w_down, float* y, const MlpWs& w, hipStream_t st,
+            float* gu_keep = nullptr) {
+  TSP_KLAUNCH(TSP_K_GATEUP, st, tsp::launch_gateup_gemm(s, x16, x_bf16, w_gate, w_up, w.act, st, gu_keep),
               "mlp gate/up");
   TSP_KLAUNCH(TSP_K_DOWN, st, tsp::launch_down_gemm(s, w.act, w_down, resid, y, w.partial, st),
               "mlp down ring");
@@ -449,6 +453,8 @@ size_t tsp_workspace_bytes(const tsp_dims_t* dims, int32_t fn) {
     case TSP_FN_ATTN_KEEP: return ws_attn_keep(s);
     case TSP_FN_ATTN_BWD_KEPT: return ws_attn_bwd(s, nullptr, nullptr, true);
     case TSP_FN_LSE: return (size_t)s.B * s.Hq * s.T * 4;
+    case TSP_FN_MLP_BWD_KEPT: return ws_mlp_bwd(s, nullptr, nullptr, true);
+    case TSP_FN_GU: return (size_t)2 * s.M * s.F * 4;
     default: fail(TSP_ERR_INVALID_ARG, "unknown workspace selector %d", fn); return 0;
   }
 }
@@ -518,9 +524,10 @@ int tsp_attn_fwd(const tsp_dims_t* dims, const uint16_t* x_local, const uint16_t
   return run_attention(s, x_local, w_qkv, w_o, kv_gathered, nullptr, residual, out, nullptr, w, stream);
 }
 
-int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const uint16_t* w_gate,
-                     const uint16_t* w_up, const uint16_t* w_down, const float* residual, float* y, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+// tsp_mlp_ring_fwd, and tsp_mlp_ring_fwd_keep when gu_keep != nullptr.
+static int mlp_ring_fwd(const char* fn, const tsp_dims_t* dims, const void* x, int32_t x_dtype,
+                        const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, const float* residual,
+                        float* y, float* gu_keep, void* ws, size_t ws_bytes, hipStream_t stream) {
   tsp::Shape s;
   TSP_TRY(make_shape(dims, &s));
   if (x_dtype != TSP_BF16 && x_dtype != TSP_F16 && x_dtype != TSP_F32)
@@ -534,7 +541,7 @@ int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
   TSP_TRY(need_ptr(ws, "ws"));
   if (ws_bytes < ws_mlp(s))
     return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_mlp(s));
-  TSP_TRY(check_device("tsp_mlp_ring_fwd"));
+  TSP_TRY(check_device(fn));
   MlpWs w;
   w.partial = partial_or_null(s, carve_mlp(s, static_cast<char*>(ws), &w));
   const uint16_t* x16 = static_cast<const uint16_t*>(x);
@@ -543,13 +550,29 @@ int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
                "mlp input rounding");
     x16 = w.h16;
   }
-  return run_mlp(s, x16, x_dtype == TSP_BF16, residual, w_gate, w_up, w_down, y, w, stream);
+  return run_mlp(s, x16, x_dtype == TSP_BF16, residual, w_gate, w_up, w_down, y, w, stream, gu_keep);
 }
 
-int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const float* dy,
-                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                     const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down, void* ws,
+int tsp_mlp_ring_fwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const uint16_t* w_gate,
+                     const uint16_t* w_up, const uint16_t* w_down, const float* residual, float* y, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
+  return mlp_ring_fwd("tsp_mlp_ring_fwd", dims, x, x_dtype, w_gate, w_up, w_down, residual, y, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+int tsp_mlp_ring_fwd_keep(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const uint16_t* w_gate,
+                          const uint16_t* w_up, const uint16_t* w_down, const float* residual, float* y,
+                          float* gu_keep, void* ws, size_t ws_bytes, hipStream_t stream) {
+  TSP_TRY(need_ptr(gu_keep, "gu_keep"));
+  return mlp_ring_fwd("tsp_mlp_ring_fwd_keep", dims, x, x_dtype, w_gate, w_up, w_down, residual, y, gu_keep, ws,
+                      ws_bytes, stream);
+}
+
+// tsp_mlp_ring_bwd, and tsp_mlp_ring_bwd_kept when gu_keep != nullptr.
+static int mlp_ring_bwd(const char* fn, const tsp_dims_t* dims, const void* x, int32_t x_dtype, const float* dy,
+                        const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, const float* gu_keep,
+                        const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   tsp::Shape s;
   TSP_TRY(make_shape(dims, &s));
   if (x_dtype != TSP_BF16 && x_dtype != TSP_F16 && x_dtype != TSP_F32)
@@ -565,16 +588,17 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
   TSP_TRY(need_ptr(dw_up, "dw_up"));
   TSP_TRY(need_ptr(dw_down, "dw_down"));
   TSP_TRY(need_ptr(ws, "ws"));
-  if (ws_bytes < ws_mlp_bwd(s))
-    return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, ws_mlp_bwd(s));
-  TSP_TRY(check_device("tsp_mlp_ring_bwd"));
+  const bool kept = gu_keep != nullptr;
+  const size_t need = ws_mlp_bwd(s, nullptr, nullptr, kept);
+  if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  TSP_TRY(check_device(fn));
   MlpBwdWs w;
-  ws_mlp_bwd(s, &w, static_cast<char*>(ws));
+  ws_mlp_bwd(s, &w, static_cast<char*>(ws), kept);
   const int Mp = mpad(s), h = s.h, F = s.F, Fs = s.F_s;
   const int tin = x_dtype == TSP_BF16 ? tsp::TR_BF16 : x_dtype == TSP_F16 ? tsp::TR_F16 : tsp::TR_F32;
   // recomputation input: x itself (bf16 or f16), or x rounded to f16
   const uint16_t* xg = static_cast<const uint16_t*>(x);
-  if (x_dtype == TSP_F32) {
+  if (!kept && x_dtype == TSP_F32) {
     TSP_LAUNCH(tsp::launch_f32_to_f16(static_cast<const float*>(x), w.x16, (int64_t)s.M * h, stream),
                "mlp bwd: x to f16");
     xg = w.x16;
@@ -586,18 +610,27 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
              "mlp bwd: dy^T");
   // dA = dy W_down and dx = sum dG_j W_gate,j + dU_j W_up,j read the weights
   // as stored; the workspace holds transposed copies (wdT, wguT) only where
-  // the K-major products do not apply
+  // the K-major products do not apply.  Kept g and u: dA stays in registers
+  // and its epilogue forms a, dG and dU (no recomputation of g and u).
   if (w.wdT == nullptr) {
-    TSP_LAUNCH(tsp::launch_bwd_da_kmajor(s, w.dy16, w_down, w.da, stream), "mlp bwd: dA");
+    if (kept)
+      TSP_LAUNCH(tsp::launch_bwd_da_kept_kmajor(s, w.dy16, w_down, gu_keep, w.act, w.dgu, stream),
+                 "mlp bwd: dA, dG, dU");
+    else
+      TSP_LAUNCH(tsp::launch_bwd_da_kmajor(s, w.dy16, w_down, w.da, stream), "mlp bwd: dA");
   } else {
     // Wd_j [h][Fs] -> WdT rows j Fs .. : [Fs][h]
     TSP_LAUNCH(tsp::launch_transpose_bf16(tsp::TR_BF16, w_down, Fs, (int64_t)h * Fs, w.wdT, h, (int64_t)Fs * h, h,
                                           Fs, h, s.D, stream),
                "mlp bwd: Wd^T");
-    TSP_LAUNCH(tsp::launch_bwd_da(s, w.dy16, w.wdT, w.da, stream), "mlp bwd: dA");
+    if (kept)
+      TSP_LAUNCH(tsp::launch_bwd_da_kept(s, w.dy16, w.wdT, gu_keep, w.act, w.dgu, stream), "mlp bwd: dA, dG, dU");
+    else
+      TSP_LAUNCH(tsp::launch_bwd_da(s, w.dy16, w.wdT, w.da, stream), "mlp bwd: dA");
   }
-  TSP_LAUNCH(tsp::launch_bwd_gu(s, xg, x_dtype == TSP_BF16, w_gate, w_up, w.da, w.act, w.dgu, stream),
-             "mlp bwd: gate/up recompute");
+  if (!kept)
+    TSP_LAUNCH(tsp::launch_bwd_gu(s, xg, x_dtype == TSP_BF16, w_gate, w_up, w.da, w.act, w.dgu, stream),
+               "mlp bwd: gate/up recompute");
   if (w.wguT == nullptr) {
     TSP_LAUNCH(tsp::launch_bwd_dx_kmajor(s, w.dgu, w_gate, w_up, dx_residual, dx, w.partial, stream), "mlp bwd: dx");
   } else {
@@ -618,6 +651,23 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
   TSP_LAUNCH(tsp::launch_bwd_dwd(s, Mp, w.dyT, w.actT, dw_down, stream), "mlp bwd: dW_down");
   TSP_LAUNCH(tsp::launch_bwd_dwgu(s, Mp, w.dguT, w.xT, dw_gate, dw_up, stream), "mlp bwd: dW_gate, dW_up");
   return TSP_OK;
+}
+
+int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const float* dy,
+                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                     const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  return mlp_ring_bwd("tsp_mlp_ring_bwd", dims, x, x_dtype, dy, w_gate, w_up, w_down, nullptr, dx_residual, dx,
+                      dw_gate, dw_up, dw_down, ws, ws_bytes, stream);
+}
+
+int tsp_mlp_ring_bwd_kept(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const float* dy,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, const float* gu_keep,
+                          const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  TSP_TRY(need_ptr(gu_keep, "gu_keep"));
+  return mlp_ring_bwd("tsp_mlp_ring_bwd_kept", dims, x, x_dtype, dy, w_gate, w_up, w_down, gu_keep, dx_residual,
+                      dx, dw_gate, dw_up, dw_down, ws, ws_bytes, stream);
 }
 
 // The attention backward from the forward's Q, O and row normalisers (w.q,

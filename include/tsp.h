@@ -120,7 +120,9 @@ typedef enum {
   TSP_FN_DKV = 9,        /* size of tsp_attn_bwd's dkv_send output */
   TSP_FN_ATTN_KEEP = 10, /* tsp_attn_fwd_keep workspace */
   TSP_FN_ATTN_BWD_KEPT = 11, /* tsp_attn_bwd_kept workspace */
-  TSP_FN_LSE = 12        /* size of tsp_attn_fwd_keep's lse_keep output */
+  TSP_FN_LSE = 12,       /* size of tsp_attn_fwd_keep's lse_keep output */
+  TSP_FN_MLP_BWD_KEPT = 13, /* tsp_mlp_ring_bwd_kept workspace */
+  TSP_FN_GU = 14         /* size of tsp_mlp_ring_fwd_keep's gu_keep output */
 } tsp_fn;
 
 /* Maps of the partition dims->partition selects, as described above (TSP
@@ -250,6 +252,33 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
                      const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                      const float* dx_residual, float* dx, float* dw_gate, float* dw_up, float* dw_down,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The MLP backward with the forward's gate and up values kept instead of
+ * recomputed (the other side of the recompute-or-keep choice the pages leave
+ * open; tsp_mlp_ring_bwd recomputes): tsp_mlp_ring_fwd_keep is
+ * tsp_mlp_ring_fwd that also hands g_j = x Wg_j^T and u_j = x Wu_j^T of every
+ * shard (float32, as its matrix cores accumulated them) to the caller, and
+ * tsp_mlp_ring_bwd_kept is tsp_mlp_ring_bwd (its outputs bit for bit) from
+ * them: the product dA = dy Wd forms a, dG and dU as it finishes, so neither
+ * the recomputing gate/up product nor dA's trip through memory runs.  The
+ * kept tensor costs 8 M F bytes per layer (86 MiB at the 8K layer).
+ * tsp_mlp_ring_fwd_keep arguments: those of tsp_mlp_ring_fwd, and
+ *   gu_keep  float32 [2][B][T][F] out (tsp_workspace_bytes(dims, TSP_FN_GU)
+ *            bytes): g of all F columns, then u (shard j's columns are
+ *            j F/D .. (j + 1) F/D - 1, the rows of w_gate and w_up)
+ *   ws       >= tsp_workspace_bytes(dims, TSP_FN_MLP) bytes
+ * tsp_mlp_ring_bwd_kept arguments: those of tsp_mlp_ring_bwd, plus gu_keep
+ * from tsp_mlp_ring_fwd_keep on the same dims, x, x_dtype and weights (read
+ * only; x still feeds dW_gate and dW_up), and
+ *   ws       >= tsp_workspace_bytes(dims, TSP_FN_MLP_BWD_KEPT) bytes */
+int tsp_mlp_ring_fwd_keep(const tsp_dims_t* dims, const void* x, int32_t x_dtype,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          const float* residual, float* y, float* gu_keep, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+int tsp_mlp_ring_bwd_kept(const tsp_dims_t* dims, const void* x, int32_t x_dtype, const float* dy,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          const float* gu_keep, const float* dx_residual, float* dx, float* dw_gate,
+                          float* dw_up, float* dw_down, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the attention on rank dims->rank, in the two parts that the
  * K/V-gradient reduce-scatter separates.  The TSP article gives the forward

@@ -43,12 +43,13 @@ int main() {
             for (int32_t dh : dhs)
               for (int32_t part = -1; part <= 2; ++part) {
                 tsp_dims_t d{b, S, D, D > 1 ? D - 1 : 0, h, 4 * (D > 0 ? D : 1), 2 * (D > 0 ? D : 1), dh, F, part};
-                size_t ws[10];
-                for (int fn = 0; fn <= 9; ++fn) ws[fn] = tsp_workspace_bytes(&d, fn);
+                size_t ws[15];
+                for (int fn = 0; fn <= 14; ++fn) ws[fn] = tsp_workspace_bytes(&d, fn);
                 if (ws[3] > 0) {
                   ++valid;
                   if (ws[0] != 0 || ws[1] == 0 || ws[2] == 0 || ws[6] == 0 || ws[3] < ws[1] || ws[7] == 0 ||
-                      ws[8] == 0 || ws[9] == 0) {
+                      ws[8] == 0 || ws[9] == 0 || ws[10] == 0 || ws[11] == 0 || ws[11] > ws[7] || ws[12] == 0 ||
+                      ws[13] == 0 || ws[13] > ws[6] || ws[14] == 0) {
                     std::fprintf(stderr, "inconsistent workspace sizes\n");
                     ++failures;
                   }
@@ -58,6 +59,18 @@ int main() {
                          TSP_ERR_HIP);
                   EXPECT(tsp_mlp_ring_bwd(&d, P, TSP_F32, f32(P), u16(P), u16(P), u16(P), nullptr, f32(P), f32(P),
                                           f32(P), f32(P), P, ws[6], nullptr),
+                         TSP_ERR_HIP);
+                  EXPECT(tsp_mlp_ring_fwd_keep(&d, P, TSP_F32, u16(P), u16(P), u16(P), nullptr, f32(P), f32(P), P,
+                                               ws[2], nullptr),
+                         TSP_ERR_HIP);
+                  EXPECT(tsp_mlp_ring_bwd_kept(&d, P, TSP_F32, f32(P), u16(P), u16(P), u16(P), f32(P), nullptr,
+                                               f32(P), f32(P), f32(P), f32(P), P, ws[13], nullptr),
+                         TSP_ERR_HIP);
+                  EXPECT(tsp_attn_fwd_keep(&d, u16(P), u16(P), u16(P), u16(P), nullptr, f32(P), u16(P), u16(P),
+                                           f32(P), P, ws[10], nullptr),
+                         TSP_ERR_HIP);
+                  EXPECT(tsp_attn_bwd_kept(&d, u16(P), u16(P), u16(P), u16(P), f32(P), f32(P), f32(P), f32(P),
+                                           f32(P), P, ws[11], nullptr),
                          TSP_ERR_HIP);
                   EXPECT(tsp_kv_reorder(&d, u16(P), u16(P), S, nullptr), TSP_ERR_HIP);
                   EXPECT(tsp_attn_bwd(&d, u16(P), u16(P), u16(P), u16(P), f32(P), f32(P), f32(P), f32(P), P, ws[7],
@@ -97,6 +110,17 @@ int main() {
          TSP_ERR_NULL_POINTER);
   EXPECT(tsp_mlp_ring_bwd(&d, P, TSP_BF16, f32(P), u16(P), u16(P), u16(P), nullptr, f32(P), f32(P), f32(P), f32(P),
                           P, wb - 1, nullptr),
+         TSP_ERR_WORKSPACE);
+  const size_t w13 = tsp_workspace_bytes(&d, TSP_FN_MLP_BWD_KEPT);
+  EXPECT(tsp_mlp_ring_fwd_keep(&d, P, TSP_BF16, u16(P), u16(P), u16(P), nullptr, f32(P), nullptr, P, wm, nullptr),
+         TSP_ERR_NULL_POINTER);
+  EXPECT(tsp_mlp_ring_fwd_keep(&d, P, TSP_BF16, u16(P), u16(P), u16(P), nullptr, f32(P), f32(Q), P, wm, nullptr),
+         TSP_ERR_MISALIGNED);
+  EXPECT(tsp_mlp_ring_bwd_kept(&d, P, TSP_BF16, f32(P), u16(P), u16(P), u16(P), nullptr, nullptr, f32(P), f32(P),
+                               f32(P), f32(P), P, w13, nullptr),
+         TSP_ERR_NULL_POINTER);
+  EXPECT(tsp_mlp_ring_bwd_kept(&d, P, TSP_BF16, f32(P), u16(P), u16(P), u16(P), f32(P), nullptr, f32(P), f32(P),
+                               f32(P), f32(P), P, w13 - 1, nullptr),
          TSP_ERR_WORKSPACE);
   EXPECT(tsp_layer_fwd_noalloc(&d, u16(P), u16(P), u16(P), u16(P), u16(P), u16(P), u16(P), nullptr, nullptr),
          TSP_ERR_NULL_POINTER);

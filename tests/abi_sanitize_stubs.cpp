@@ -19,7 +19,7 @@ hipError_t launch_oproj_gemm(const Shape&, const uint16_t*, const uint16_t*, con
   return hipSuccess;
 }
 hipError_t launch_gateup_gemm(const Shape&, const uint16_t*, bool, const uint16_t*, const uint16_t*, uint16_t*,
-                              hipStream_t) {
+                              hipStream_t, float*) {
   return hipSuccess;
 }
 hipError_t launch_down_gemm(const Shape&, const uint16_t*, const uint16_t*, const float*, float*, float*,
@@ -33,6 +33,10 @@ hipError_t launch_transpose_bf16(int, const void*, int64_t, int64_t, uint16_t*, 
 }
 hipError_t launch_f32_to_bf16(const float*, uint16_t*, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_da(const Shape&, const uint16_t*, const uint16_t*, float*, hipStream_t) { return hipSuccess; }
+hipError_t launch_bwd_da_kept(const Shape&, const uint16_t*, const uint16_t*, const float*, uint16_t*, uint16_t*,
+                              hipStream_t) {
+  return hipSuccess;
+}
 hipError_t launch_bwd_gu(const Shape&, const uint16_t*, bool, const uint16_t*, const uint16_t*, const float*,
                          uint16_t*, uint16_t*, hipStream_t) {
   return hipSuccess;
@@ -48,6 +52,10 @@ hipError_t launch_bwd_dwgu(const Shape&, int, const uint16_t*, const uint16_t*, 
 }
 bool kmajor_ok(const Shape& s, int use) { return use != KMAJ_DX_MLP || s.F_s % 32 == 0; }
 hipError_t launch_bwd_da_kmajor(const Shape&, const uint16_t*, const uint16_t*, float*, hipStream_t) {
+  return hipSuccess;
+}
+hipError_t launch_bwd_da_kept_kmajor(const Shape&, const uint16_t*, const uint16_t*, const float*, uint16_t*,
+                                     uint16_t*, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_bwd_dx_kmajor(const Shape&, const uint16_t*, const uint16_t*, const uint16_t*, const float*, float*,

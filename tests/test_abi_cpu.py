@@ -460,3 +460,43 @@ def test_attn_keep_argument_checks_and_sizes(lib):
     need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_ATTN_BWD_KEPT)
     assert g(ctypes.byref(d), *gargs(), need - 1, None) == B.TSP_ERR_WORKSPACE
     assert g(ctypes.byref(_dims(rank=5)), *gargs(), big, None) == B.TSP_ERR_RANK
+
+
+def test_mlp_keep_argument_checks_and_sizes(lib):
+    d = _dims()
+    big = 1 << 40
+    # kept tensor: g then u, float32 [2][B][T][F]; the kept backward's
+    # workspace is the recomputing one without dA and the f16 copy of x
+    wl = synth.WORKLOADS["llama7b_s8k_d8"].dims
+    s = B.dims_struct(wl)
+    M = wl.batch * (wl.seq // wl.degree)
+    assert lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_GU) == 2 * M * wl.ffn * 4
+    full = lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_MLP_BWD)
+    kept = lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_MLP_BWD_KEPT)
+    assert full - kept == _up256(M * wl.hidden * 2) + _up256(M * wl.ffn * 4)
+    f = lib.tsp_mlp_ring_fwd_keep
+    names = ("x", "wg", "wu", "wd", "res", "y", "gu", "ws")
+    args = lambda **kw: [kw.get(n, None if n == "res" else FAKE) for n in names]
+    call = lambda xdt=B.TSP_BF16, nbytes=big, **kw: f(ctypes.byref(d), *args(**kw)[:1], xdt, *args(**kw)[1:],
+                                                      nbytes, None)
+    for n, label in (("gu", "gu_keep"), ("y", "y"), ("x", "x"), ("ws", "ws")):
+        assert call(**{n: None}) == B.TSP_ERR_NULL_POINTER
+        assert f"{label} is NULL" in lib.tsp_last_error().decode()
+    assert call(gu=MISALIGNED) == B.TSP_ERR_MISALIGNED
+    assert call(xdt=7) == B.TSP_ERR_DTYPE
+    need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_MLP)
+    assert call(nbytes=need - 1) == B.TSP_ERR_WORKSPACE
+    g = lib.tsp_mlp_ring_bwd_kept
+    gnames = ("x", "dy", "wg", "wu", "wd", "gu", "dxr", "dx", "dwg", "dwu", "dwd", "ws")
+    gargs = lambda **kw: [kw.get(n, None if n == "dxr" else FAKE) for n in gnames]
+    gcall = lambda nbytes=big, rank_dims=d, **kw: g(ctypes.byref(rank_dims), *gargs(**kw)[:1], B.TSP_BF16,
+                                                    *gargs(**kw)[1:], nbytes, None)
+    for n, label in zip(gnames, ("x", "dy", "w_gate", "w_up", "w_down", "gu_keep", None, "dx", "dw_gate", "dw_up",
+                                 "dw_down", "ws")):
+        if label is None:
+            continue
+        assert gcall(**{n: None}) == B.TSP_ERR_NULL_POINTER
+        assert f"{label} is NULL" in lib.tsp_last_error().decode()
+    need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_MLP_BWD_KEPT)
+    assert gcall(nbytes=need - 1) == B.TSP_ERR_WORKSPACE
+    assert gcall(rank_dims=_dims(rank=5)) == B.TSP_ERR_RANK

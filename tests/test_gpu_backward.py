@@ -165,3 +165,77 @@ def test_mlp_ring_bwd_full_size_llama7b():
     gpu, ref, _ = _run(d, inp, "bf16")
     for k in ("dx", "dw_g", "dw_u", "dw_d"):
         _check(k, gpu[k], ref[k])
+
+
+def _keep_vs_recompute(d, inp, xdt, sample_rows=None):
+    """tsp_mlp_ring_fwd_keep then tsp_mlp_ring_bwd_kept on rank d.rank's rows,
+    beside tsp_mlp_ring_fwd then tsp_mlp_ring_bwd on the same inputs: y and
+    every backward output must agree bit for bit; the kept g and u are held
+    to the oracle's (all rows, or sample_rows of them)."""
+    gpu, _, (xt, dyt, w, _, kw, _, _, _, _) = _run(d, inp, xdt)
+    T, F, h = d.seq // d.degree, d.ffn, d.hidden
+    M = d.batch * T
+    f32 = dict(dtype=torch.float32, device="cuda")
+    resid = torch.from_numpy(synth.make_grad(d, 3)[:, :T].copy()).cuda()
+    y_ref, y = torch.empty_like(resid), torch.empty_like(resid)
+    ws = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP), dtype=torch.uint8, device="cuda")
+    B.tsp_mlp_ring_fwd(d, xt, w["w_gate"], w["w_up"], w["w_down"], y_ref, ws, residual=resid, **kw)
+    gu = torch.full((B.tsp_workspace_bytes(d, B.TSP_FN_GU) // 4,), float("nan"), **f32)
+    B.tsp_mlp_ring_fwd_keep(d, xt, w["w_gate"], w["w_up"], w["w_down"], y, gu, ws, residual=resid, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    dx = torch.empty_like(dyt)
+    dwg, dwu = torch.empty((F, h), **f32), torch.empty((F, h), **f32)
+    dwd = torch.empty((d.degree, h, F // d.degree), **f32)
+    wsk = torch.empty(B.tsp_workspace_bytes(d, B.TSP_FN_MLP_BWD_KEPT), dtype=torch.uint8, device="cuda")
+    B.tsp_mlp_ring_bwd_kept(d, xt, dyt, w["w_gate"], w["w_up"], w["w_down"], gu, dx, dwg, dwu, dwd, wsk,
+                            dx_residual=dyt, **kw)
+    torch.cuda.synchronize()
+    for k, v in (("dx", dx), ("dw_g", dwg), ("dw_u", dwu), ("dw_d", dwd)):
+        assert np.array_equal(v.cpu().numpy(), gpu[k]), k
+    # the kept g = x Wg^T and u = x Wu^T against the oracle's, from x as the
+    # matrix cores saw it (f32 input: rounded to f16)
+    x64 = xt.view(torch.bfloat16).double().cpu().numpy() if xdt == "bf16" else \
+        xt.to(torch.float16).double().cpu().numpy()
+    x64 = x64.reshape(M, h)
+    rows = np.arange(M) if sample_rows is None else \
+        np.sort(np.random.default_rng(5).choice(M, sample_rows, replace=False))
+    wts = {n: orc.bf16_bits_to_f64(inp[n]) for n in ("w_g", "w_u", "w_d")}
+    ref = bwd.mlp_backward(x64[rows], wts["w_g"], wts["w_u"], wts["w_d"], np.zeros((len(rows), h)))
+    g_u = gu.view(2, M, F).cpu().numpy()
+    _check("g", g_u[0][rows], ref["g"])
+    _check("u", g_u[1][rows], ref["u"])
+
+
+# tsp_mlp_ring_fwd_keep + tsp_mlp_ring_bwd_kept (g and u kept instead of
+# recomputed): the forward's gate/up product and the backward's
+# recomputation run the same kernel, and the kept epilogue of dA = dy W_down
+# applies the recomputing epilogue's arithmetic to the same values, so y and
+# every gradient agree bit for bit with tsp_mlp_ring_fwd + tsp_mlp_ring_bwd
+# (held to the oracle above).  Shapes: the tiny layer, shards of 176 columns
+# (ragged K segments), B = 2 with 96-position chunks, D = 1, a wider hidden
+# size; every input type.
+@pytest.mark.parametrize("name", ["tiny_d2", "ffn_tail_d4_r3", "gqa8_b2_c96", "d1", "wide_tiles_dh128"])
+@pytest.mark.parametrize("xdt", ["bf16", "f16", "f32"])
+def test_mlp_kept_equals_recompute(name, xdt):
+    d, sigma, seed = _shape(name)
+    _case(f"mlp kept vs recompute {name} x={xdt}")
+    _keep_vs_recompute(d, inputs_for(d.astuple(), sigma, seed), xdt)
+
+
+# The same with the transposed copy of W_down (TSP_TUNE_BWD_WEIGHTS = 1):
+# the kept epilogue on the other dA kernel.
+@pytest.mark.parametrize("name", ["tiny_d2", "ffn_tail_d4_r3"])
+def test_mlp_kept_equals_recompute_weight_copies(name):
+    d, sigma, seed = _shape(name)
+    _case(f"mlp kept vs recompute {name} transposed weight copies")
+    with tuning(bwd_weights=1):
+        _keep_vs_recompute(d, inputs_for(d.astuple(), sigma, seed), "f32")
+
+
+# The 8K layer's MLP at full size (1024 rows, 8 shards of 1376): bit equality
+# of every output; g and u on 64 sampled rows against the oracle.
+def test_mlp_kept_equals_recompute_full_size_llama7b():
+    wl = synth.WORKLOADS["llama7b_s8k_d8"]
+    _case("mlp kept vs recompute llama7b_s8k_d8 full size")
+    _keep_vs_recompute(wl.dims, synth.make_inputs(wl.dims, wl.sigma, wl.seed), "f16", sample_rows=64)
