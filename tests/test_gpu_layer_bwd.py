@@ -6,7 +6,10 @@ tsp_mlp_ring_bwd (dh = dy + the MLP branch's input gradient, the rank's
 weight-gradient contributions), tsp_attn_bwd (dQ, the K/V-gradient send
 buffer, dW_O share); then the reduce-scatter (test plumbing: the blocks for
 rank r summed over ranks) and tsp_attn_bwd_proj (dx = dh + the attention
-branch's input gradient, dW_QKV share).  Reference: the oracle's
+branch's input gradient, dW_QKV share).  With kept activations the forward
+calls also hand over what the backward would recompute (tsp_attn_fwd_keep:
+Q, O, the row normalisers; tsp_mlp_ring_fwd_keep: g and u) and the backward
+calls take them (tsp_attn_bwd_kept, tsp_mlp_ring_bwd_kept).  Reference: the oracle's
 layer_backward (float64 autograd-free gradients of the unsharded layer over
 whole sequences, pinned on the CPU against torch autograd and finite
 differences): every rank's dh and dx rows, and the weight gradients summed
@@ -45,9 +48,10 @@ def _check(name, got, ref):
     assert ma_rel <= MAX_ABS and rf <= REL_FROB, (name, ma_rel, rf)
 
 
-def _layer_backward_on_gpu(d, inp, dy):
+def _layer_backward_on_gpu(d, inp, dy, kept=False):
     """Every rank's pieces; returns per-rank dh, dx rows and the summed weight
-    gradients (ABI layouts), as numpy."""
+    gradients (ABI layouts), as numpy.  kept: the forward's activations kept
+    instead of recomputed."""
     prob = RankProblem.build(d, inp)
     w = prob.w
     D, T, h = d.degree, d.seq // d.degree, d.hidden
@@ -62,20 +66,39 @@ def _layer_backward_on_gpu(d, inp, dy):
     # every rank's K/V slot of the all-gather (the build skipped dims.rank's:
     # the layer call writes it), so that each rank's attention sees all keys
     B.tsp_qkv_proj(d, d.rank, xloc[d.rank], w["w_qkv"], None, prob.kv_gathered)
-    dhs, dqs, sends = [], [], []
+    dhs, dqs, sends, keeps = [], [], [], []
     for r, dr in enumerate(ranks):
         # forward to the MLP input h
         x32 = xloc[r].view(torch.bfloat16).float()
         hr = torch.empty((d.batch, T, h), **f32)
-        wsa = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_ATTN), dtype=torch.uint8, device="cuda")
-        B.tsp_attn_fwd(dr, xloc[r], w["w_qkv"], w["w_o"], prob.kv_gathered, hr, wsa, residual=x32)
+        if kept:
+            q_keep = torch.empty(d.batch * T * qd, dtype=torch.int16, device="cuda")
+            o_keep = torch.empty_like(q_keep)
+            lse = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_LSE) // 4, **f32)
+            wsa = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_ATTN_KEEP), dtype=torch.uint8, device="cuda")
+            B.tsp_attn_fwd_keep(dr, xloc[r], w["w_qkv"], w["w_o"], prob.kv_gathered, hr, q_keep, o_keep, lse, wsa,
+                                residual=x32)
+            keeps.append((q_keep, o_keep, lse))
+        else:
+            wsa = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_ATTN), dtype=torch.uint8, device="cuda")
+            B.tsp_attn_fwd(dr, xloc[r], w["w_qkv"], w["w_o"], prob.kv_gathered, hr, wsa, residual=x32)
         l2g = prob.l2g[r].cpu().numpy()
         dyr = torch.from_numpy(np.ascontiguousarray(dy[:, l2g])).cuda()
         dhr = torch.empty_like(dyr)
         g, u, dd = torch.empty_like(dwg), torch.empty_like(dwu), torch.empty_like(dwd)
-        wsm = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_MLP_BWD), dtype=torch.uint8, device="cuda")
-        B.tsp_mlp_ring_bwd(dr, hr, dyr, w["w_gate"], w["w_up"], w["w_down"], dhr, g, u, dd, wsm,
-                           dx_residual=dyr, x_dtype=B.TSP_F32)
+        if kept:
+            # the MLP forward (its output is not needed here) keeps g and u
+            gu = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_GU) // 4, **f32)
+            wsf = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_MLP), dtype=torch.uint8, device="cuda")
+            B.tsp_mlp_ring_fwd_keep(dr, hr, w["w_gate"], w["w_up"], w["w_down"], torch.empty_like(hr), gu, wsf,
+                                    x_dtype=B.TSP_F32)
+            wsm = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_MLP_BWD_KEPT), dtype=torch.uint8, device="cuda")
+            B.tsp_mlp_ring_bwd_kept(dr, hr, dyr, w["w_gate"], w["w_up"], w["w_down"], gu, dhr, g, u, dd, wsm,
+                                    dx_residual=dyr, x_dtype=B.TSP_F32)
+        else:
+            wsm = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_MLP_BWD), dtype=torch.uint8, device="cuda")
+            B.tsp_mlp_ring_bwd(dr, hr, dyr, w["w_gate"], w["w_up"], w["w_down"], dhr, g, u, dd, wsm,
+                               dx_residual=dyr, x_dtype=B.TSP_F32)
         dwg += g
         dwu += u
         dwd += dd
@@ -85,8 +108,12 @@ def _layer_backward_on_gpu(d, inp, dy):
         dq = torch.empty((d.batch, T, qd), **f32)
         send = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_DKV) // 4, **f32)
         o = torch.empty((D, h, qs), **f32)
-        ws1 = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_ATTN_BWD), dtype=torch.uint8, device="cuda")
-        B.tsp_attn_bwd(dr, xloc[r], w["w_qkv"], w["w_o"], prob.kv_gathered, dhs[r], dq, send, o, ws1)
+        if kept:
+            ws1 = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_ATTN_BWD_KEPT), dtype=torch.uint8, device="cuda")
+            B.tsp_attn_bwd_kept(dr, w["w_o"], prob.kv_gathered, *keeps[r], dhs[r], dq, send, o, ws1)
+        else:
+            ws1 = torch.empty(B.tsp_workspace_bytes(dr, B.TSP_FN_ATTN_BWD), dtype=torch.uint8, device="cuda")
+            B.tsp_attn_bwd(dr, xloc[r], w["w_qkv"], w["w_o"], prob.kv_gathered, dhs[r], dq, send, o, ws1)
         dwo += o
         dqs.append(dq)
         sends.append(send)
@@ -115,8 +142,7 @@ CASES = [("tiny_d2", 0), ("gqa4_dh128_d4_r2", 0), ("gqa4_dh128_d4_r2", 1), ("c24
          ("mha_d2_r1", 0)]
 
 
-@pytest.mark.parametrize("name,partition", CASES)
-def test_layer_backward_composed_equals_unsharded(name, partition):
+def _case(name, partition):
     if name in synth.WORKLOADS:
         wl = synth.WORKLOADS[name]
         d = dataclasses.replace(wl.dims, partition=partition)
@@ -125,9 +151,36 @@ def test_layer_backward_composed_equals_unsharded(name, partition):
         shape = SWEEP[name][:9] + (partition,)
         d = dims_of(shape)
         inp = inputs_for(shape, 0.02, 101)
+    return d, inp
+
+
+@pytest.mark.parametrize("name,partition", CASES)
+def test_layer_backward_composed_equals_unsharded(name, partition):
+    d, inp = _case(name, partition)
     print(f"[case] composed layer backward {name} partition={partition} {d}", flush=True)
     dy = synth.make_grad(d, 23)
-    got = _layer_backward_on_gpu(d, inp, dy)
+    _check_against_oracle(d, inp, dy, _layer_backward_on_gpu(d, inp, dy))
+
+
+# The same composition with the forward's activations kept (attention: Q, O,
+# row normalisers; MLP: g and u): the oracle's bars, and every output equal
+# bit for bit to the recomputing composition's.
+@pytest.mark.parametrize("name,partition", [("tiny_d2", 0), ("gqa4_dh128_d4_r2", 1), ("c24_generic_reorder", 1)])
+def test_layer_backward_composed_kept(name, partition):
+    d, inp = _case(name, partition)
+    print(f"[case] composed layer backward, kept activations, {name} partition={partition} {d}", flush=True)
+    dy = synth.make_grad(d, 23)
+    got = _layer_backward_on_gpu(d, inp, dy, kept=True)
+    _check_against_oracle(d, inp, dy, got)
+    rec = _layer_backward_on_gpu(d, inp, dy)
+    for k in ("dh", "dx"):
+        for r in range(d.degree):
+            assert np.array_equal(got[k][r], rec[k][r]), (k, r)
+    for k in ("dw_g", "dw_u", "dw_d", "dw_o", "dw_qkv"):
+        assert np.array_equal(got[k], rec[k]), k
+
+
+def _check_against_oracle(d, inp, dy, got):
     ref = bwd.layer_backward(inp, d, dy)
     D = d.degree
     qs = d.n_q_heads // D * d.head_dim
