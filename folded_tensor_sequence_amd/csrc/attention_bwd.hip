@@ -393,9 +393,10 @@ __global__ void attn_bwd_dq_merge_kernel(AttnBwdArgs a) {
 // dV^T += dO^T P and dK^T += Q^T dS over its rows.  The block's K and V rows
 // sit in LDS (read once), so a wave holds only its accumulators and two
 // waves share a SIMD: one's exp work runs beside the other's products.  At
-// the end the two waves of a key group add their sums through LDS and the
-// keys' K/V gradient contributions go to the send buffer of the keys' owner
-// ranks (zeros for keys no query of the rank sees).
+// the end the two waves of a key group add their sums through LDS (one
+// finishes dV, the other dK) and the keys' K/V gradient contributions go to
+// the send buffer of the keys' owner ranks (zeros for keys no query of the
+// rank sees).
 template <int DH>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   constexpr int NWV = 8, BQ = 64, KROW = DH * 2, TILE = BQ * KROW;
@@ -589,10 +590,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   }
   if (it < items) step(it, IC<0>{});
 
-  // the pair's sums: the second-half wave of each key group leaves its dV
-  // partial in the K/V rows' array and its dK partial in a stage (every
-  // wave is past its last LDS read: the loop ends on a barrier, and with no
-  // item the K/V rows were never read), the first-half wave adds them
+  // the pair's sums, half the work each: the second-half wave of each key
+  // group leaves its dV partial in the K/V rows' array, the first-half wave
+  // its dK partial in a stage (every wave is past its last LDS read: the
+  // loop ends on a barrier, and with no item the K/V rows were never read);
+  // then the first-half wave adds and stores dV, the second-half wave dK
   if (items == 0) {
     wait_loads();  // the K/V rows' loads land before that memory is reused
     barrier_nofence();
@@ -603,21 +605,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pv[(db * 16 + e) * 64] = dvacc[db][e];
-        pk[(db * 16 + e) * 64] = dkacc[db][e];
-      }
+      for (int e = 0; e < 16; ++e) pv[(db * 16 + e) * 64] = dvacc[db][e];
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pk[(db * 16 + e) * 64] = dkacc[db][e];
   }
   wait_loads();
   barrier_nofence();
-  if (hf == 1 || kpos >= s.S) return;
+  if (kpos >= s.S) return;
+  if (hf == 0) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dvacc[db][e] += pv[(db * 16 + e) * 64];
-      dkacc[db][e] += pk[(db * 16 + e) * 64];
-    }
+      for (int e = 0; e < 16; ++e) dvacc[db][e] += pv[(db * 16 + e) * 64];
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dkacc[db][e] += pk[(db * 16 + e) * 64];
+  }
   // owner rank and local row of the key
   int g, t;
   if (s.part == 1) {
@@ -633,17 +641,26 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
   float* dk = a.dkv + kslot * kvd + (int64_t)hk * DH;
   float* dv = a.dkv + vslot * kvd + (int64_t)hk * DH;
   const float scl = a.scale;
+  if (hf == 0) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + 8 * j + 4 * lgrp;
-      f32x4 kv4{dkacc[db][4 * j] * scl, dkacc[db][4 * j + 1] * scl, dkacc[db][4 * j + 2] * scl,
-                dkacc[db][4 * j + 3] * scl};
-      f32x4 vv4{dvacc[db][4 * j], dvacc[db][4 * j + 1], dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]};
-      *reinterpret_cast<f32x4*>(dk + d) = kv4;
-      *reinterpret_cast<f32x4*>(dv + d) = vv4;
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * lgrp;
+        f32x4 vv4{dvacc[db][4 * j], dvacc[db][4 * j + 1], dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(dv + d) = vv4;
+      }
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * lgrp;
+        f32x4 kv4{dkacc[db][4 * j] * scl, dkacc[db][4 * j + 1] * scl, dkacc[db][4 * j + 2] * scl,
+                  dkacc[db][4 * j + 3] * scl};
+        *reinterpret_cast<f32x4*>(dk + d) = kv4;
+      }
+  }
 }
 
 // ---- host -------------------------------------------------------------------

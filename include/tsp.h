@@ -265,7 +265,8 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
  * tsp_mlp_ring_fwd_keep arguments: those of tsp_mlp_ring_fwd, and
  *   gu_keep  float32 [2][B][T][F] out (tsp_workspace_bytes(dims, TSP_FN_GU)
  *            bytes): g of all F columns, then u (shard j's columns are
- *            j F/D .. (j + 1) F/D - 1, the rows of w_gate and w_up)
+ *            j F/D .. (j + 1) F/D - 1, the rows of w_gate and w_up); must
+ *            not overlap any other argument
  *   ws       >= tsp_workspace_bytes(dims, TSP_FN_MLP) bytes
  * tsp_mlp_ring_bwd_kept arguments: those of tsp_mlp_ring_bwd, plus gu_keep
  * from tsp_mlp_ring_fwd_keep on the same dims, x, x_dtype and weights (read
