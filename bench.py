@@ -6,10 +6,12 @@ Q/K/V projection for all D weight shards, causal flash attention over the
 all-gathered K/V (read in zigzag order through the position -> slot map), the
 output projection with residual, and the gated-MLP weight ring (gate/up +
 SwiGLU, down + residual).  The standalone zigzag K/V reorder kernel
-(``tsp_kv_reorder``) is timed separately and reported as ``reorder_standalone``.  The other ranks' K/V slots of the
-all-gather buffer are filled once before timing (they are communication, not
-this rank's compute).  Inputs are resident in device memory when the timed
-region starts.
+(``tsp_kv_reorder``) is timed separately and reported as
+``reorder_standalone``, and the layer backward's calls (with and without kept
+forward activations) as ``mlp_ring_bwd`` and ``attn_bwd``.  The other ranks'
+K/V slots of the all-gather buffer are filled once before timing (they are
+communication, not this rank's compute).  Inputs are resident in device
+memory when the timed region starts.
 
 Prints one JSON line.  ``value`` is algorithmic TFLOP/s (2MNK per GEMM,
 4*dh per causal query/key pair per head; masked pairs and elementwise work
