@@ -258,8 +258,10 @@ int tsp_mlp_ring_bwd(const tsp_dims_t* dims, const void* x, int32_t x_dtype, con
  * open; tsp_mlp_ring_bwd recomputes): tsp_mlp_ring_fwd_keep is
  * tsp_mlp_ring_fwd that also hands g_j = x Wg_j^T and u_j = x Wu_j^T of every
  * shard (float32, as its matrix cores accumulated them) to the caller, and
- * tsp_mlp_ring_bwd_kept is tsp_mlp_ring_bwd (its outputs bit for bit) from
- * them: the product dA = dy Wd forms a, dG and dU as it finishes, so neither
+ * tsp_mlp_ring_bwd_kept is tsp_mlp_ring_bwd from them (its outputs bit for
+ * bit under the default kernel choice, where the forward's gate/up product
+ * and the backward's recomputation are the same kernel): the product
+ * dA = dy Wd forms a, dG and dU as it finishes, so neither
  * the recomputing gate/up product nor dA's trip through memory runs.  The
  * kept tensor costs 8 M F bytes per layer (86 MiB at the 8K layer).
  * tsp_mlp_ring_fwd_keep arguments: those of tsp_mlp_ring_fwd, and
