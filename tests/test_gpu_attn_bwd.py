@@ -233,14 +233,20 @@ def test_attn_bwd_full_size_llama7b():
 # tsp_attn_bwd: the same kernels produce the kept tensors, so the layer
 # output and every backward output agree bit for bit.  Shapes: GQA 4 with
 # head_dim 128 under both partitions, blocks cut into key pieces (the merge
-# writes those rows' normalisers), chunks of 24 positions.
+# writes those rows' normalisers), chunks of 24 positions, the 8K layer.
 @pytest.mark.parametrize("name,partition", [("gqa4_dh128_d4_r2", 0), ("gqa4_dh128_d4_r2", 1),
-                                            ("split_keys_dh128", 0), ("c24_generic_reorder", 1)])
+                                            ("split_keys_dh128", 0), ("c24_generic_reorder", 1),
+                                            ("llama7b_s8k_d8", 0)])
 def test_attn_bwd_kept_equals_recompute(name, partition):
-    shape = SWEEP[name][:9] + (partition,)
-    d = dims_of(shape)
+    if name in synth.WORKLOADS:
+        wl = synth.WORKLOADS[name]
+        d = dataclasses.replace(wl.dims, partition=partition)
+        inp = synth.make_inputs(d, wl.sigma, wl.seed)
+    else:
+        shape = SWEEP[name][:9] + (partition,)
+        d = dims_of(shape)
+        inp = inputs_for(shape, 0.02, 101)
     _case(f"attn_bwd_kept {name} partition={partition} {d}")
-    inp = inputs_for(shape, 0.02, 101)
     R = _Ranks(d, inp)
     r = d.rank
     T = d.seq // d.degree
