@@ -44,14 +44,16 @@ The pages give no split of their totals, so the two coefficients are
 GPUs); the calculator is then checked against what was not fitted: the
 TP+SP range 85.0-140.0 GB and TSP ~ TP at short context.  A first-principles
 count of the tensors the layer of this library saves for its backward pass
-(bf16, no recomputation) is given beside the fit for comparison.
+(bf16, no recomputation) is given beside the fit for comparison, and
+kept_activation_bytes gives what the library's kept-activation calls hold
+per rank and layer on top of the layer inputs.
 """
 from __future__ import annotations
 
 import dataclasses
 
 __all__ = ["Model", "Layout", "MODEL_7B", "PAGES_128K", "model_state_bytes", "per_gpu_bytes",
-           "fit_activation_coeffs", "first_principles_coeffs", "report"]
+           "kept_activation_bytes", "fit_activation_coeffs", "first_principles_coeffs", "report"]
 
 GB = 1e9                      # the pages' figures are decimal gigabytes (7e9 x 16 B = 112 GB)
 ADAM_MIXED_BYTES_PER_PARAM = 16
@@ -139,6 +141,19 @@ def first_principles_coeffs(model: Model = MODEL_7B, elem_bytes: int = 2):
     qkvo = (2 * model.n_q_heads + 2 * model.n_kv_heads) * dh * elem_bytes
     mlp = (3 if model.gated else 2) * model.ffn * elem_bytes
     return float(rep), float(qkvo + mlp)
+
+
+def kept_activation_bytes(model: Model, seq: int, batch: int, degree: int) -> dict:
+    """Bytes one TSP rank keeps per layer when the backward takes the
+    forward's activations instead of recomputing them (the library's
+    kept-activation calls): Q and the attention output O of the rank's
+    S/D tokens (16-bit, all heads), each row's softmax normaliser (float32,
+    per q-head), and the MLP's g and u (float32, all F columns)."""
+    tokens = batch * (seq // degree)
+    qo = 2 * tokens * model.n_q_heads * model.head_dim * 2
+    lse = batch * model.n_q_heads * (seq // degree) * 4
+    gu = 2 * tokens * model.ffn * 4
+    return {"attention": float(qo + lse), "mlp": float(gu), "total": float(qo + lse + gu)}
 
 
 def tpsp_layouts(devices: int):

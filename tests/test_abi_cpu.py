@@ -500,3 +500,18 @@ def test_mlp_keep_argument_checks_and_sizes(lib):
     need = lib.tsp_workspace_bytes(ctypes.byref(d), B.TSP_FN_MLP_BWD_KEPT)
     assert gcall(nbytes=need - 1) == B.TSP_ERR_WORKSPACE
     assert gcall(rank_dims=_dims(rank=5)) == B.TSP_ERR_RANK
+
+
+@pytest.mark.parametrize("name", ["llama7b_s8k_d8", "llama3_8b_gqa_s16k_d8", "tiny_d2"])
+def test_kept_bytes_match_the_memory_calculator(lib, name):
+    # the calculator's count of what the kept-activation calls hold per rank
+    # and layer (written from the shapes) against the library's buffer sizes
+    from folded_tensor_sequence_amd import memory_model as mm
+    d = synth.WORKLOADS[name].dims
+    s = B.dims_struct(d)
+    model = mm.Model(params=0.0, hidden=d.hidden, layers=1, n_q_heads=d.n_q_heads, n_kv_heads=d.n_kv_heads,
+                     head_dim=d.head_dim, ffn=d.ffn)
+    kept = mm.kept_activation_bytes(model, d.seq, d.batch, d.degree)
+    qo = 2 * B._Sizes(d).q
+    assert kept["attention"] == qo + lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_LSE)
+    assert kept["mlp"] == lib.tsp_workspace_bytes(ctypes.byref(s), B.TSP_FN_GU)
